@@ -1,0 +1,297 @@
+/*
+ * oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously-correct CPU reference for GGUF Q8_0 / Q4_0
+ * block-quantised weight x activation products, in fp64. Only the tests,
+ * the smoke check and the benchmark's CPU-baseline leg may call it; the
+ * library's compute path never does. It shares no code, header, table or
+ * constant generator with the HIP library: it reads the canonical GGUF
+ * block bytes (never the library's packed arrays) and decodes them itself.
+ *
+ * Build: gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off -fno-fast-math
+ * (float arithmetic on x86-64 is SSE binary32 with FLT_EVAL_METHOD == 0, so
+ * every `float` operation below is one IEEE-754 binary32 operation with
+ * round-to-nearest-even).
+ *
+ * Sources ("page" = one of the web pages the method is taken from):
+ *  - Gem native architecture page, "M4 Max operating assumptions": Q4_0 is a
+ *    32-element, 18-byte block; Q8_0 is kept for embeddings.
+ *  - jouleclaw-loader-gguf BENCHMARKS page, "Matmul throughput -- Q8_0 scalar
+ *    vs NEON": Q8_0 weights against int8 activations with an int32 widening
+ *    accumulate, the caller picking fp32 activations (quantised first) or
+ *    pre-quantised ones.
+ *  - SafeC Gemma 4 DESIGN_NOTES page, "Gated FFN" (down(gelu_tanh(gate x) *
+ *    up x) and the tanh form of GELU) and "Math primitives" (y = x W^T with
+ *    W stored [out][in] row-major).
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *  - block byte layout: fp16 scale d first, then the quants (GGUF order);
+ *  - Q4_0 nibble order: byte j of a block holds element j in its low nibble
+ *    and element j+16 in its high nibble; value (q - 8) * d;
+ *  - activation quantiser: per 32-element block, d = fp16(amax / 127) in
+ *    fp32 then round-to-nearest-even to binary16; q = clamp(round-half-away(
+ *    x / d), -127, 127) with the division in fp32 by the fp16-rounded scale;
+ *    q = 0 when that scale is zero.  Inputs are assumed finite.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <string.h>
+#include <float.h>
+
+#if FLT_EVAL_METHOD != 0
+#error "the oracle needs binary32 float evaluation (FLT_EVAL_METHOD == 0)"
+#endif
+
+#define OR_QK 32
+#define OR_TYPE_Q4_0 2
+#define OR_TYPE_Q8_0 8
+
+/* ------------------------------------------------------------------------ */
+/* IEEE-754 binary16 <-> wider types, written out bit by bit.                */
+/* ------------------------------------------------------------------------ */
+
+/* binary16 bits -> the exact fp64 value (subnormals, +-0, inf, NaN). */
+double or_fp16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 31;
+    int m = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);                 /* subnormal or zero */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25);     /* (1 + m/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* fp32 -> binary16 bits, round to nearest, ties to even. The fp32 value is
+ * exact in fp64, so scaling by powers of two and nearbyint() (default
+ * rounding mode: nearest-even) give the correctly rounded half. */
+uint16_t or_f32_to_fp16_rne(float f)
+{
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    uint16_t sign = (uint16_t)((bits >> 16) & 0x8000u);
+    if (isnan(f))
+        return (uint16_t)(sign | 0x7E00u);
+    double a = fabs((double)f);
+    if (a >= 65520.0)              /* at or past the midpoint above 65504 */
+        return (uint16_t)(sign | 0x7C00u);
+    if (a < 0x1p-14) {             /* subnormal range: multiples of 2^-24 */
+        double q = nearbyint(a * 0x1p24);          /* 0..1024; 1024 = min normal */
+        return (uint16_t)(sign | (uint16_t)q);
+    }
+    int E;
+    (void)frexp(a, &E);            /* a in [2^(E-1), 2^E) */
+    int e = E - 1;
+    double s = nearbyint(ldexp(a, 10 - e));        /* in [1024, 2048] */
+    if (s == 2048.0) {
+        s = 1024.0;
+        e += 1;
+    }
+    if (e + 15 >= 31)
+        return (uint16_t)(sign | 0x7C00u);
+    return (uint16_t)(sign | (uint16_t)(((e + 15) << 10) | ((int)s - 1024)));
+}
+
+/* ------------------------------------------------------------------------ */
+/* Block decode.                                                             */
+/* ------------------------------------------------------------------------ */
+
+size_t or_block_bytes(int type)
+{
+    if (type == OR_TYPE_Q8_0) return 34;
+    if (type == OR_TYPE_Q4_0) return 18;
+    return 0;
+}
+
+/* Integer quant values of one block: Q8_0 q_i, Q4_0 (nibble_i - 8). */
+static void block_ints(int type, const uint8_t *blk, int q[OR_QK])
+{
+    if (type == OR_TYPE_Q8_0) {
+        for (int i = 0; i < OR_QK; ++i)
+            q[i] = (int)(int8_t)blk[2 + i];
+    } else {
+        for (int j = 0; j < 16; ++j) {
+            q[j] = (int)(blk[2 + j] & 0x0F) - 8;
+            q[j + 16] = (int)(blk[2 + j] >> 4) - 8;
+        }
+    }
+}
+
+static double block_scale(const uint8_t *blk)
+{
+    return or_fp16_to_f64((uint16_t)(blk[0] | (blk[1] << 8)));
+}
+
+/* Dequantise rows [0, n) of a [n][k/32] block matrix into w[n][k] (fp64,
+ * exact: an 11-bit scale times an integer of at most 8 bits). */
+int or_dequantize(int type, const uint8_t *blocks, int64_t n, int64_t k, double *w)
+{
+    size_t bb = or_block_bytes(type);
+    if (!bb || k <= 0 || k % OR_QK || n < 0) return 1;
+    int64_t nb = k / OR_QK;
+    int q[OR_QK];
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *blk = blocks + (size_t)(r * nb + b) * bb;
+            double d = block_scale(blk);
+            block_ints(type, blk, q);
+            for (int i = 0; i < OR_QK; ++i)
+                w[r * k + b * OR_QK + i] = d * (double)q[i];
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* y = W x with fp64 activations (fp32 inputs widen exactly).                */
+/* y[r] = sum_k w[r][k] x[k], k ascending; a[r] = sum_k |w[r][k] x[k]|.      */
+/* ------------------------------------------------------------------------ */
+int or_matvec(int type, const uint8_t *blocks, int64_t n, int64_t k,
+              const double *x, double *y, double *a)
+{
+    size_t bb = or_block_bytes(type);
+    if (!bb || k <= 0 || k % OR_QK || n < 0) return 1;
+    int64_t nb = k / OR_QK;
+    int q[OR_QK];
+    for (int64_t r = 0; r < n; ++r) {
+        double sum = 0.0, asum = 0.0;
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *blk = blocks + (size_t)(r * nb + b) * bb;
+            double d = block_scale(blk);
+            block_ints(type, blk, q);
+            for (int i = 0; i < OR_QK; ++i) {
+                double p = (d * (double)q[i]) * x[b * OR_QK + i];
+                sum += p;
+                asum += fabs(p);
+            }
+        }
+        y[r] = sum;
+        if (a) a[r] = asum;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Q8_0 activation quantiser (an encoding, spelled out step by step).        */
+/* x [m][k] fp32 -> xq [m][k] int8, xd [m][k/32] binary16 bits.               */
+/* ------------------------------------------------------------------------ */
+int or_quantize_q8_0(const float *x, int64_t m, int64_t k, int8_t *xq, uint16_t *xd)
+{
+    if (k <= 0 || k % OR_QK || m < 0) return 1;
+    int64_t nb = k / OR_QK;
+    for (int64_t r = 0; r < m; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const float *xb = x + r * k + b * OR_QK;
+            int8_t *qb = xq + r * k + b * OR_QK;
+            float amax = 0.0f;                       /* 1: block absolute max */
+            for (int i = 0; i < OR_QK; ++i) {
+                float v = fabsf(xb[i]);
+                if (v > amax) amax = v;
+            }
+            float d32 = amax / 127.0f;               /* 2: fp32 divide */
+            uint16_t h = or_f32_to_fp16_rne(d32);    /* 3: round to binary16 */
+            float d16 = (float)or_fp16_to_f64(h);    /*    (exact in fp32) */
+            xd[r * nb + b] = h;
+            for (int i = 0; i < OR_QK; ++i) {        /* 4: codes */
+                int qi = 0;
+                if (d16 != 0.0f) {
+                    float v = xb[i] / d16;           /* fp32 divide */
+                    float rv = roundf(v);            /* half away from zero */
+                    if (rv > 127.0f) rv = 127.0f;
+                    if (rv < -127.0f) rv = -127.0f;
+                    qi = (int)rv;
+                }
+                qb[i] = (int8_t)qi;
+            }
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Integer path: weights x Q8_0 activation rows.                              */
+/* S[mi][r][b] = sum_i qw[r][b][i] * qx[mi][b][i] exactly (int64, checked to  */
+/* fit int32); y[mi][r] = sum_b dw[r][b] dx[mi][b] S (fp64);                  */
+/* a[mi][r] = sum_b |dw dx| sum_i |qw qx|.  S, y, a may each be NULL.         */
+/* Returns 2 if some S does not fit int32.                                    */
+/* ------------------------------------------------------------------------ */
+int or_blockdots(int type, const uint8_t *blocks, int64_t n, int64_t k,
+                 const int8_t *xq, const uint16_t *xd, int64_t m,
+                 int32_t *S, double *y, double *a)
+{
+    size_t bb = or_block_bytes(type);
+    if (!bb || k <= 0 || k % OR_QK || n < 0 || m < 0) return 1;
+    int64_t nb = k / OR_QK;
+    int q[OR_QK];
+    int rc = 0;
+    for (int64_t mi = 0; mi < m; ++mi)
+        for (int64_t r = 0; r < n; ++r) {
+            double sum = 0.0, asum = 0.0;
+            for (int64_t b = 0; b < nb; ++b) {
+                const uint8_t *blk = blocks + (size_t)(r * nb + b) * bb;
+                const int8_t *qx = xq + mi * k + b * OR_QK;
+                block_ints(type, blk, q);
+                int64_t s = 0, sa = 0;
+                for (int i = 0; i < OR_QK; ++i) {
+                    int64_t p = (int64_t)q[i] * (int64_t)qx[i];
+                    s += p;
+                    sa += p < 0 ? -p : p;
+                }
+                if (s > INT32_MAX || s < INT32_MIN) rc = 2;
+                double scale = block_scale(blk) * or_fp16_to_f64(xd[mi * nb + b]);
+                sum += scale * (double)s;
+                asum += fabs(scale) * (double)sa;
+                if (S) S[(mi * n + r) * nb + b] = (int32_t)s;
+            }
+            if (y) y[mi * n + r] = sum;
+            if (a) a[mi * n + r] = asum;
+        }
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* GELU, tanh form (SafeC DESIGN_NOTES page, "Gated FFN"):                    */
+/* G(t) = 0.5 t (1 + tanh(sqrt(2/pi) (t + 0.044715 t^3))); libm tanh          */
+/* saturates to +-1, so finite t gives a finite result.                       */
+/* ------------------------------------------------------------------------ */
+double or_gelu_tanh(double t)
+{
+    const double c = sqrt(2.0 / 3.14159265358979323846);
+    return 0.5 * t * (1.0 + tanh(c * (t + 0.044715 * t * t * t)));
+}
+
+/* Gate/up half of the gated FFN: g = Wg x, u = Wu x (both [n_ff][k]),
+ * h = G(g) * u. ag/au are the sum |w x| of each row (may be NULL). */
+int or_ffn_gate_up(int type, const uint8_t *gblocks, const uint8_t *ublocks,
+                   int64_t n_ff, int64_t k, const double *x,
+                   double *g, double *u, double *h, double *ag, double *au)
+{
+    int rc = or_matvec(type, gblocks, n_ff, k, x, g, ag);
+    if (rc) return rc;
+    rc = or_matvec(type, ublocks, n_ff, k, x, u, au);
+    if (rc) return rc;
+    for (int64_t r = 0; r < n_ff; ++r)
+        h[r] = or_gelu_tanh(g[r]) * u[r];
+    return 0;
+}
+
+/* Sampled rows: y[i] = row rows[i] of W times x, for spot checks at sizes
+ * where the full product would take too long. */
+int or_matvec_rows(int type, const uint8_t *blocks, int64_t n, int64_t k,
+                   const int64_t *rows, int64_t nrows, const double *x,
+                   double *y, double *a)
+{
+    size_t bb = or_block_bytes(type);
+    if (!bb || k <= 0 || k % OR_QK) return 1;
+    int64_t nb = k / OR_QK;
+    for (int64_t i = 0; i < nrows; ++i) {
+        if (rows[i] < 0 || rows[i] >= n) return 1;
+        const uint8_t *row = blocks + (size_t)(rows[i] * nb) * bb;
+        int rc = or_matvec(type, row, 1, k, x, y + i, a ? a + i : NULL);
+        if (rc) return rc;
+    }
+    return 0;
+}
