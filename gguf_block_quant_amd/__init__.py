@@ -1,0 +1,206 @@
+"""gguf_block_quant_amd -- Python binding of libgq (include/gq.h).
+
+Argument marshalling only: every function here checks that its tensors are
+device-resident and contiguous, passes their data pointers and the current
+(or given) HIP stream to the C ABI entry point of the same name (``gq_``
+prefix dropped), and raises ``GQError`` on a non-zero status. All compute
+runs in libgq's HIP kernels; there is no fallback. Importing this module
+fails loudly when libgq.so has not been built.
+
+Tensors are torch tensors (PyTorch supplies device memory and streams).
+Binary16 scale arrays are carried as int16/uint16 tensors of raw bits.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgq.so")
+
+TYPE_Q4_0 = 2
+TYPE_Q8_0 = 8
+
+GQ_OK = 0
+STATUS_NAMES = {0: "GQ_OK", 1: "GQ_ERR_NULL", 2: "GQ_ERR_SHAPE", 3: "GQ_ERR_ALIGN",
+                4: "GQ_ERR_ALIAS", 5: "GQ_ERR_UNSUPPORTED", 6: "GQ_ERR_LAUNCH"}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        "libgq.so is not built (expected at %s); run `python -m gguf_block_quant_amd.build` "
+        "or __graft_entry__.build()" % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+
+_SIGS = {
+    "gq_abi_version": ([], _I),
+    "gq_status_str": ([_I], ctypes.c_char_p),
+    "gq_block_bytes": ([_I], ctypes.c_size_t),
+    "gq_packed_qs_bytes": ([_I, _I64, _I64], ctypes.c_size_t),
+    "gq_packed_d_bytes": ([_I64, _I64], ctypes.c_size_t),
+    "gq_pack": ([_I, _P, _I64, _I64, _P, _P, _P], _I),
+    "gq_quantize_q8_0": ([_P, _I64, _I64, _P, _P, _P], _I),
+    "gq_qmv_q8_0": ([_P, _P, _I64, _I64, _P, _P, _P], _I),
+    "gq_qmv_q4_0": ([_P, _P, _I64, _I64, _P, _P, _P], _I),
+    "gq_qmv_q8_0_q8": ([_P, _P, _I64, _I64, _P, _P, _P, _P, _P], _I),
+    "gq_qmv_q4_0_q8": ([_P, _P, _I64, _I64, _P, _P, _P, _P, _P], _I),
+    "gq_qffn_gate_up_gelu": ([_P, _P, _P, _P, _I64, _I64, _P, _P, _P], _I),
+    "gq_qmm_tile_m": ([_P, _P, _I64, _I64, _I, _P, _P, _P, _P, _P], _I),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+
+def raw():
+    """The ctypes handle of libgq (for tests that call the C ABI directly)."""
+    return _lib
+
+
+class GQError(RuntimeError):
+    def __init__(self, status, fn):
+        self.status = status
+        super().__init__("%s failed: %s (%s)" % (fn, STATUS_NAMES.get(status, status),
+                                                 status_str(status)))
+
+
+def abi_version() -> int:
+    return _lib.gq_abi_version()
+
+
+def status_str(status: int) -> str:
+    return _lib.gq_status_str(status).decode()
+
+
+def block_bytes(qtype: int) -> int:
+    return _lib.gq_block_bytes(qtype)
+
+
+def packed_qs_bytes(qtype: int, n: int, k: int) -> int:
+    return _lib.gq_packed_qs_bytes(qtype, n, k)
+
+
+def packed_d_bytes(n: int, k: int) -> int:
+    return _lib.gq_packed_d_bytes(n, k)
+
+
+# ----------------------------------------------------------------------------
+# marshalling helpers
+# ----------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _call(fn, *args):
+    st = getattr(_lib, fn)(*args)
+    if st != GQ_OK:
+        raise GQError(st, fn)
+
+
+def _like(ref, shape, dtype):
+    torch = _torch()
+    return torch.empty(shape, dtype=dtype, device=ref.device)
+
+
+# ----------------------------------------------------------------------------
+# entry points
+# ----------------------------------------------------------------------------
+
+def pack(qtype, blocks, n, k, qs=None, d=None, stream=None):
+    """GGUF blocks (device uint8, n*k/32 blocks) -> packed (qs, d)."""
+    torch = _torch()
+    if qs is None:
+        qs = _like(blocks, (n, k if qtype == TYPE_Q8_0 else k // 2),
+                   torch.int8 if qtype == TYPE_Q8_0 else torch.uint8)
+    if d is None:
+        d = _like(blocks, (n, k // 32), torch.int16)
+    _call("gq_pack", qtype, _ptr(blocks, "blocks"), n, k, _ptr(qs, "qs"), _ptr(d, "d"), _stream(stream))
+    return qs, d
+
+
+def quantize_q8_0(x, xq=None, xd=None, stream=None):
+    """fp32 x [m][k] (or [k]) -> (xq int8 [m][k], xd binary16 bits [m][k/32])."""
+    torch = _torch()
+    m, k = (1, x.shape[0]) if x.dim() == 1 else tuple(x.shape)
+    if xq is None:
+        xq = _like(x, tuple(x.shape), torch.int8)
+    if xd is None:
+        xd = _like(x, tuple(x.shape[:-1]) + (k // 32,), torch.int16)
+    _call("gq_quantize_q8_0", _ptr(x, "x"), m, k, _ptr(xq, "xq"), _ptr(xd, "xd"), _stream(stream))
+    return xq, xd
+
+
+def _qmv_f32(fn, qs, d, n, k, x, y, stream):
+    torch = _torch()
+    if y is None:
+        y = _like(x, (n,), torch.float32)
+    _call(fn, _ptr(qs, "qs"), _ptr(d, "d"), n, k, _ptr(x, "x"), _ptr(y, "y"), _stream(stream))
+    return y
+
+
+def qmv_q8_0(qs, d, n, k, x, y=None, stream=None):
+    return _qmv_f32("gq_qmv_q8_0", qs, d, n, k, x, y, stream)
+
+
+def qmv_q4_0(qs, d, n, k, x, y=None, stream=None):
+    return _qmv_f32("gq_qmv_q4_0", qs, d, n, k, x, y, stream)
+
+
+def _qmv_q8(fn, qs, d, n, k, xq, xd, y, blockdots, stream):
+    torch = _torch()
+    if y is None:
+        y = _like(xq, (n,), torch.float32)
+    _call(fn, _ptr(qs, "qs"), _ptr(d, "d"), n, k, _ptr(xq, "xq"), _ptr(xd, "xd"), _ptr(y, "y"),
+          _ptr(blockdots, "blockdots"), _stream(stream))
+    return y
+
+
+def qmv_q8_0_q8(qs, d, n, k, xq, xd, y=None, blockdots=None, stream=None):
+    return _qmv_q8("gq_qmv_q8_0_q8", qs, d, n, k, xq, xd, y, blockdots, stream)
+
+
+def qmv_q4_0_q8(qs, d, n, k, xq, xd, y=None, blockdots=None, stream=None):
+    return _qmv_q8("gq_qmv_q4_0_q8", qs, d, n, k, xq, xd, y, blockdots, stream)
+
+
+def qffn_gate_up_gelu(g_qs, g_d, u_qs, u_d, n_ff, k, x, h=None, stream=None):
+    torch = _torch()
+    if h is None:
+        h = _like(x, (n_ff,), torch.float32)
+    _call("gq_qffn_gate_up_gelu", _ptr(g_qs, "g_qs"), _ptr(g_d, "g_d"), _ptr(u_qs, "u_qs"),
+          _ptr(u_d, "u_d"), n_ff, k, _ptr(x, "x"), _ptr(h, "h"), _stream(stream))
+    return h
+
+
+def qmm_tile_m(qs, d, n, k, m, xq, xd, y=None, blockdots=None, stream=None):
+    torch = _torch()
+    if y is None:
+        y = _like(xq, (m, n), torch.float32)
+    _call("gq_qmm_tile_m", _ptr(qs, "qs"), _ptr(d, "d"), n, k, m, _ptr(xq, "xq"), _ptr(xd, "xd"),
+          _ptr(y, "y"), _ptr(blockdots, "blockdots"), _stream(stream))
+    return y

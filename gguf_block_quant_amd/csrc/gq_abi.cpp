@@ -1,0 +1,212 @@
+// gq_abi.cpp -- the extern "C" boundary of libgq (declared in include/gq.h).
+// Every entry point validates all of its arguments on the host, before any
+// HIP call, then enqueues its kernel(s) on the caller's stream. No
+// allocation, no synchronisation, no global state.
+#include "../../include/gq.h"
+
+#include <hip/hip_runtime.h>
+
+#include "gq_launch.hpp"
+
+namespace {
+
+using gq::kMaxK;
+using gq::kMaxRows;
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+    const void* p;
+    size_t bytes;
+};
+
+inline bool overlap(Range a, Range b) {
+    if (a.p == nullptr || b.p == nullptr || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Any output overlapping any input, or two outputs overlapping each other.
+template <size_t NO, size_t NI>
+bool any_alias(const Range (&outs)[NO], const Range (&ins)[NI]) {
+    for (size_t i = 0; i < NO; ++i) {
+        for (size_t j = 0; j < NI; ++j)
+            if (overlap(outs[i], ins[j])) return true;
+        for (size_t j = i + 1; j < NO; ++j)
+            if (overlap(outs[i], outs[j])) return true;
+    }
+    return false;
+}
+
+inline bool type_ok(int type) { return type == GQ_TYPE_Q4_0 || type == GQ_TYPE_Q8_0; }
+
+// n x k shape check shared by every entry point.
+inline int check_shape(int64_t n, int64_t k) {
+    if (n < 1 || k < 32 || k % 32 != 0) return GQ_ERR_SHAPE;
+    if (n > kMaxRows) return GQ_ERR_UNSUPPORTED;
+    return GQ_OK;
+}
+
+inline size_t qs_bytes(int type, int64_t n, int64_t k) {
+    return type == GQ_TYPE_Q8_0 ? static_cast<size_t>(n) * static_cast<size_t>(k)
+                                : static_cast<size_t>(n) * static_cast<size_t>(k / 2);
+}
+inline size_t d_bytes(int64_t n, int64_t k) { return static_cast<size_t>(n) * static_cast<size_t>(k / 32) * 2; }
+
+inline int status_of(hipError_t e) { return e == hipSuccess ? GQ_OK : GQ_ERR_LAUNCH; }
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// Checks shared by the two matvec families: packed weights, n, k.
+int check_weights(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k) {
+    if (qs == nullptr || d == nullptr) return GQ_ERR_NULL;
+    int st = check_shape(n, k);
+    if (st != GQ_OK) return st;
+    if (k > kMaxK || !type_ok(type)) return GQ_ERR_UNSUPPORTED;
+    if (!aligned(qs, 16) || !aligned(d, 2)) return GQ_ERR_ALIGN;
+    return GQ_OK;
+}
+
+int qmv_f32(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k, const float* x,
+            float* y, void* stream) {
+    if (x == nullptr || y == nullptr) return GQ_ERR_NULL;
+    int st = check_weights(type, qs, d, n, k);
+    if (st != GQ_OK) return st;
+    if (!aligned(x, 16) || !aligned(y, 4)) return GQ_ERR_ALIGN;
+    const Range outs[] = {{y, static_cast<size_t>(n) * 4}};
+    const Range ins[] = {{qs, qs_bytes(type, n, k)}, {d, d_bytes(n, k)}, {x, static_cast<size_t>(k) * 4}};
+    if (any_alias(outs, ins)) return GQ_ERR_ALIAS;
+    return status_of(gq::launch_qmv_f32(type, qs, d, n, k, x, y, as_stream(stream)));
+}
+
+int qmv_q8(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k, const int8_t* xq,
+           const uint16_t* xd, float* y, int32_t* blockdots, void* stream) {
+    if (xq == nullptr || xd == nullptr || y == nullptr) return GQ_ERR_NULL;
+    int st = check_weights(type, qs, d, n, k);
+    if (st != GQ_OK) return st;
+    if (!aligned(xq, 16) || !aligned(xd, 2) || !aligned(y, 4) || !aligned(blockdots, 4)) return GQ_ERR_ALIGN;
+    const Range outs[] = {{y, static_cast<size_t>(n) * 4},
+                          {blockdots, blockdots ? static_cast<size_t>(n) * static_cast<size_t>(k / 32) * 4 : 0}};
+    const Range ins[] = {{qs, qs_bytes(type, n, k)}, {d, d_bytes(n, k)}, {xq, static_cast<size_t>(k)},
+                         {xd, static_cast<size_t>(k / 32) * 2}};
+    if (any_alias(outs, ins)) return GQ_ERR_ALIAS;
+    return status_of(gq::launch_qmv_q8(type, qs, d, n, k, xq, xd, y, blockdots, as_stream(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int gq_abi_version(void) { return GQ_ABI_VERSION; }
+
+const char* gq_status_str(int status) {
+    switch (status) {
+        case GQ_OK: return "ok";
+        case GQ_ERR_NULL: return "a required pointer is NULL";
+        case GQ_ERR_SHAPE: return "invalid shape (need n >= 1, k >= 32, k % 32 == 0, supported m)";
+        case GQ_ERR_ALIGN: return "a pointer is not aligned as required";
+        case GQ_ERR_ALIAS: return "an output overlaps an input";
+        case GQ_ERR_UNSUPPORTED: return "unsupported type, k, n or m";
+        case GQ_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+size_t gq_block_bytes(int type) {
+    if (type == GQ_TYPE_Q8_0) return 34;
+    if (type == GQ_TYPE_Q4_0) return 18;
+    return 0;
+}
+
+size_t gq_packed_qs_bytes(int type, int64_t n, int64_t k) {
+    if (!type_ok(type) || check_shape(n, k) != GQ_OK) return 0;
+    return qs_bytes(type, n, k);
+}
+
+size_t gq_packed_d_bytes(int64_t n, int64_t k) {
+    if (check_shape(n, k) != GQ_OK) return 0;
+    return d_bytes(n, k);
+}
+
+int gq_pack(int type, const void* blocks, int64_t n, int64_t k, void* qs, uint16_t* d, void* stream) {
+    if (blocks == nullptr || qs == nullptr || d == nullptr) return GQ_ERR_NULL;
+    int st = check_shape(n, k);
+    if (st != GQ_OK) return st;
+    if (!type_ok(type)) return GQ_ERR_UNSUPPORTED;
+    if (!aligned(qs, 16) || !aligned(d, 2)) return GQ_ERR_ALIGN;
+    const size_t blk_bytes = static_cast<size_t>(n) * static_cast<size_t>(k / 32) * gq_block_bytes(type);
+    const Range outs[] = {{qs, qs_bytes(type, n, k)}, {d, d_bytes(n, k)}};
+    const Range ins[] = {{blocks, blk_bytes}};
+    if (any_alias(outs, ins)) return GQ_ERR_ALIAS;
+    return status_of(gq::launch_pack(type, static_cast<const uint8_t*>(blocks), n, k,
+                                     static_cast<uint8_t*>(qs), d, as_stream(stream)));
+}
+
+int gq_quantize_q8_0(const float* x, int64_t m, int64_t k, int8_t* xq, uint16_t* xd, void* stream) {
+    if (x == nullptr || xq == nullptr || xd == nullptr) return GQ_ERR_NULL;
+    int st = check_shape(m, k);
+    if (st != GQ_OK) return st;
+    if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(xd, 2)) return GQ_ERR_ALIGN;
+    const Range outs[] = {{xq, static_cast<size_t>(m) * static_cast<size_t>(k)}, {xd, d_bytes(m, k)}};
+    const Range ins[] = {{x, static_cast<size_t>(m) * static_cast<size_t>(k) * 4}};
+    if (any_alias(outs, ins)) return GQ_ERR_ALIAS;
+    return status_of(gq::launch_quantize_q8_0(x, m, k, xq, xd, as_stream(stream)));
+}
+
+int gq_qmv_q8_0(const int8_t* qs, const uint16_t* d, int64_t n, int64_t k, const float* x, float* y,
+                void* stream) {
+    return qmv_f32(GQ_TYPE_Q8_0, qs, d, n, k, x, y, stream);
+}
+
+int gq_qmv_q4_0(const uint8_t* qs, const uint16_t* d, int64_t n, int64_t k, const float* x, float* y,
+                void* stream) {
+    return qmv_f32(GQ_TYPE_Q4_0, qs, d, n, k, x, y, stream);
+}
+
+int gq_qmv_q8_0_q8(const int8_t* qs, const uint16_t* d, int64_t n, int64_t k, const int8_t* xq,
+                   const uint16_t* xd, float* y, int32_t* blockdots, void* stream) {
+    return qmv_q8(GQ_TYPE_Q8_0, qs, d, n, k, xq, xd, y, blockdots, stream);
+}
+
+int gq_qmv_q4_0_q8(const uint8_t* qs, const uint16_t* d, int64_t n, int64_t k, const int8_t* xq,
+                   const uint16_t* xd, float* y, int32_t* blockdots, void* stream) {
+    return qmv_q8(GQ_TYPE_Q4_0, qs, d, n, k, xq, xd, y, blockdots, stream);
+}
+
+int gq_qffn_gate_up_gelu(const uint8_t* g_qs, const uint16_t* g_d, const uint8_t* u_qs,
+                         const uint16_t* u_d, int64_t n_ff, int64_t k, const float* x, float* h,
+                         void* stream) {
+    if (g_qs == nullptr || g_d == nullptr || u_qs == nullptr || u_d == nullptr || x == nullptr ||
+        h == nullptr)
+        return GQ_ERR_NULL;
+    int st = check_shape(n_ff, k);
+    if (st != GQ_OK) return st;
+    if (k > kMaxK) return GQ_ERR_UNSUPPORTED;
+    if (!aligned(g_qs, 16) || !aligned(u_qs, 16) || !aligned(g_d, 2) || !aligned(u_d, 2) ||
+        !aligned(x, 16) || !aligned(h, 4))
+        return GQ_ERR_ALIGN;
+    const size_t qb = qs_bytes(GQ_TYPE_Q4_0, n_ff, k), db = d_bytes(n_ff, k);
+    const Range outs[] = {{h, static_cast<size_t>(n_ff) * 4}};
+    const Range ins[] = {{g_qs, qb}, {g_d, db}, {u_qs, qb}, {u_d, db}, {x, static_cast<size_t>(k) * 4}};
+    if (any_alias(outs, ins)) return GQ_ERR_ALIAS;
+    return status_of(gq::launch_ffn_gate_up(g_qs, g_d, u_qs, u_d, n_ff, k, x, h, as_stream(stream)));
+}
+
+int gq_qmm_tile_m(const uint8_t* qs, const uint16_t* d, int64_t n, int64_t k, int m, const int8_t* xq,
+                  const uint16_t* xd, float* y, int32_t* blockdots, void* stream) {
+    if (qs == nullptr || d == nullptr || xq == nullptr || xd == nullptr || y == nullptr) return GQ_ERR_NULL;
+    int st = check_shape(n, k);
+    if (st != GQ_OK) return st;
+    if (m != 8 && m != 16 && m != 32) return GQ_ERR_UNSUPPORTED;
+    if (k > kMaxK) return GQ_ERR_UNSUPPORTED;
+    if (!aligned(qs, 16) || !aligned(d, 2) || !aligned(xq, 16) || !aligned(xd, 2) || !aligned(y, 4) ||
+        !aligned(blockdots, 4))
+        return GQ_ERR_ALIGN;
+    const size_t mn = static_cast<size_t>(m) * static_cast<size_t>(n);
+    const Range outs[] = {{y, mn * 4}, {blockdots, blockdots ? mn * static_cast<size_t>(k / 32) * 4 : 0}};
+    const Range ins[] = {{qs, qs_bytes(GQ_TYPE_Q4_0, n, k)}, {d, d_bytes(n, k)},
+                         {xq, static_cast<size_t>(m) * static_cast<size_t>(k)}, {xd, d_bytes(m, k)}};
+    if (any_alias(outs, ins)) return GQ_ERR_ALIAS;
+    return status_of(gq::launch_tile_q4_0(qs, d, n, k, m, xq, xd, y, blockdots, as_stream(stream)));
+}
+
+}  // extern "C"

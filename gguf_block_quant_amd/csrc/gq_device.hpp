@@ -1,0 +1,75 @@
+// gq_device.hpp -- device-side helpers shared by the libgq kernels (gfx950,
+// wave64). Nothing here is visible through the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gq {
+
+constexpr int kWave = 64;
+constexpr int kBlockThreads = 256;   // 4 waves per workgroup
+constexpr int kWavesPerBlock = kBlockThreads / kWave;
+
+constexpr int kTypeQ4_0 = 2;
+constexpr int kTypeQ8_0 = 8;
+
+// binary16 bits -> fp32 (exact; v_cvt_f32_f16 keeps fp16 subnormals).
+__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// fp32 -> binary16 bits, round to nearest even (v_cvt_f16_f32).
+__device__ __forceinline__ uint16_t float_to_half_bits(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+// DPP move of a 32-bit value within a row of 16 lanes (all lanes valid for
+// the quad_perm and mirror patterns used here).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+constexpr int kDppQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppRowHalfMirror = 0x141; // lane i <-> 7 - i within 8
+constexpr int kDppRowMirror = 0x140;     // lane i <-> 15 - i within 16
+
+// Sum of v over the 64 lanes of the wave, returned in every lane. The order
+// is fixed (butterfly inside each 16-lane row, then rows 0+1 and 2+3), so the
+// result is bitwise reproducible and identical in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_f32<kDppQuadSwap1>(v);
+    v += dpp_f32<kDppQuadSwap2>(v);
+    v += dpp_f32<kDppRowHalfMirror>(v);
+    v += dpp_f32<kDppRowMirror>(v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// Exact int8x4 dot product with int32 accumulate (v_dot4_i32_i8).
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot4(static_cast<int>(a), static_cast<int>(b), c, false);
+}
+
+// Tanh-form GELU, G(t) = 0.5 t (1 + tanh(z)), z = sqrt(2/pi) (t + 0.044715 t^3),
+// evaluated as t / (1 + exp(-2 z)) (the same function: 0.5 (1 + tanh z) is
+// the logistic function of 2z). For large positive z the exponential
+// underflows to 0 and G -> t; for large negative z it overflows to +inf and
+// G -> -0, so finite t never produces NaN.
+__device__ __forceinline__ float gelu_tanh(float t) {
+    const float c = 0.7978845608028654f;   // sqrt(2/pi)
+    const float z = c * fmaf(0.044715f * t, t * t, t);
+    return t / (1.0f + expf(-2.0f * z));
+}
+
+}  // namespace gq

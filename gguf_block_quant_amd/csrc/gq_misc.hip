@@ -1,0 +1,110 @@
+// gq_misc.hip -- load-time weight pack and the Q8_0 activation quantiser.
+#include "gq_device.hpp"
+#include "gq_launch.hpp"
+
+namespace gq {
+
+// ---------------------------------------------------------------------------
+// Pack: GGUF blocks (34 B Q8_0 / 18 B Q4_0, any byte alignment) -> quants
+// qs (16-B aligned rows) and scales d. One thread per block; byte loads
+// because a block's start is only 2-byte aligned at best. Pure byte moves.
+// The idea of a kernel-layout weight pack derived from the canonical file
+// comes from the Gemma-4-E2B raw-Metal port page ("Architecture", pack
+// bullet) and the Gem native architecture page ("M4 Max operating
+// assumptions", packed sidecar).
+// ---------------------------------------------------------------------------
+template <int TYPE>
+__global__ __launch_bounds__(kBlockThreads)
+void pack_kernel(const uint8_t* __restrict__ blocks, int64_t nblocks, uint8_t* __restrict__ qs,
+                 uint16_t* __restrict__ d) {
+    constexpr int BB = (TYPE == kTypeQ8_0) ? 34 : 18;
+    constexpr int QB = BB - 2;                       // quant bytes per block
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= nblocks) return;
+    const uint8_t* src = blocks + i * BB;
+    d[i] = static_cast<uint16_t>(src[0] | (src[1] << 8));
+    uint32_t w[QB / 4];
+#pragma unroll
+    for (int j = 0; j < QB / 4; ++j)
+        w[j] = static_cast<uint32_t>(src[2 + 4 * j]) | (static_cast<uint32_t>(src[3 + 4 * j]) << 8) |
+               (static_cast<uint32_t>(src[4 + 4 * j]) << 16) | (static_cast<uint32_t>(src[5 + 4 * j]) << 24);
+    uint4* dst = reinterpret_cast<uint4*>(qs + i * QB);  // row bytes are multiples of 16
+#pragma unroll
+    for (int j = 0; j < QB / 16; ++j) dst[j] = make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
+}
+
+hipError_t launch_pack(int type, const uint8_t* blocks, int64_t n, int64_t k, uint8_t* qs,
+                       uint16_t* d, hipStream_t stream) {
+    const int64_t nblocks = n * (k / 32);
+    const int64_t grid = (nblocks + kBlockThreads - 1) / kBlockThreads;
+    if (type == kTypeQ8_0)
+        hipLaunchKernelGGL(pack_kernel<kTypeQ8_0>, dim3(static_cast<unsigned>(grid)), dim3(kBlockThreads),
+                           0, stream, blocks, nblocks, qs, d);
+    else
+        hipLaunchKernelGGL(pack_kernel<kTypeQ4_0>, dim3(static_cast<unsigned>(grid)), dim3(kBlockThreads),
+                           0, stream, blocks, nblocks, qs, d);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Q8_0 activation quantiser, one thread per 32-element block:
+// amax (fp32) -> d = binary16(amax / 127) (fp32 divide, then round to
+// nearest even) -> q = clamp(round-half-away(x / d), -127, 127) with the
+// divide in fp32 by the rounded d; q = 0 when d == 0. The fp32 divides are
+// IEEE correctly rounded (no fast-math) so both the codes and the scale are
+// reproducible bit for bit. fp32 activation -> int8 codes + scale is the
+// activation quantiser of the jouleclaw-loader-gguf BENCHMARKS page
+// ("Matmul throughput -- Q8_0 scalar vs NEON"), taken per 32-element block.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlockThreads)
+void quantize_q8_0_kernel(const float* __restrict__ x, int64_t nblocks, int8_t* __restrict__ xq,
+                          uint16_t* __restrict__ xd) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= nblocks) return;
+    const float4* src = reinterpret_cast<const float4*>(x + i * 32);
+    float v[32];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float4 t = src[j];
+        v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        const float a = fabsf(v[j]);
+        amax = a > amax ? a : amax;
+    }
+    const uint16_t hb = float_to_half_bits(amax / 127.0f);
+    const float dh = half_bits_to_float(hb);
+    xd[i] = hb;
+    uint32_t packed[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            int q = 0;
+            if (dh != 0.0f) {
+                float r = roundf(v[4 * j + b] / dh);
+                r = fminf(fmaxf(r, -127.0f), 127.0f);
+                q = static_cast<int>(r);
+            }
+            w |= (static_cast<uint32_t>(q) & 0xFFu) << (8 * b);
+        }
+        packed[j] = w;
+    }
+    uint4* dst = reinterpret_cast<uint4*>(xq + i * 32);
+    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+}
+
+hipError_t launch_quantize_q8_0(const float* x, int64_t m, int64_t k, int8_t* xq, uint16_t* xd,
+                                hipStream_t stream) {
+    const int64_t nblocks = m * (k / 32);
+    const int64_t grid = (nblocks + kBlockThreads - 1) / kBlockThreads;
+    hipLaunchKernelGGL(quantize_q8_0_kernel, dim3(static_cast<unsigned>(grid)), dim3(kBlockThreads), 0,
+                       stream, x, nblocks, xq, xd);
+    return hipGetLastError();
+}
+
+}  // namespace gq

@@ -1,0 +1,352 @@
+// gq_qmv.hip -- M = 1 decode kernels: Q8_0 / Q4_0 matvec with fp32 or
+// Q8_0-quantised activations, and the fused gate+up GELU FFN pass.
+//
+// Decomposition (gfx950, wave64):
+//  * A "unit" is 16 bytes of packed quants: one global_load_dwordx4 per lane.
+//    For Q8_0 that is half a block (16 elements), for Q4_0 one whole block
+//    (32 elements). Lane l of a wave owns units l, l+64, ... of its K-slice,
+//    so each load instruction reads 1 KiB of one row contiguously.
+//  * The activation values a lane needs for its units are loaded once into
+//    VGPRs and reused for every row the wave streams (x is read from HBM
+//    once per wave, not once per row).
+//  * A wave streams R rows per step (R x NI independent 16-byte loads in
+//    flight per lane), dequantises and dot-reduces in registers, and sums
+//    the lanes with DPP (wave_sum), fixed order, no atomics.
+//  * Long rows (large k) are split over WS waves of the workgroup; their
+//    partial sums meet in LDS and are added in slice order.
+//  * The grid is persistent-ish: workgroups stride over row groups so each
+//    wave amortises its activation load over many rows.
+// The decode projection being a weight-streaming matvec, and the lesson that
+// an M == 1 product wants its own kernel rather than a tiled GEMM, follow the
+// SafeC Gemma 4 DESIGN_NOTES page ("A dedicated GEMV kernel for the M==1
+// decode step") and the Gemma-4-E2B raw-Metal port page ("Why this exists").
+#include "gq_device.hpp"
+#include "gq_launch.hpp"
+
+namespace gq {
+
+enum Mode { kF32 = 0, kQ8X = 1, kFFN = 2 };
+
+template <int TYPE> struct Fmt;
+template <> struct Fmt<kTypeQ8_0> {
+    static constexpr int kElemsPerUnit = 16;
+    static constexpr int kUnitToBlockShift = 1;
+};
+template <> struct Fmt<kTypeQ4_0> {
+    static constexpr int kElemsPerUnit = 32;
+    static constexpr int kUnitToBlockShift = 0;
+};
+
+struct QmvParams {
+    const uint8_t* qs;      // packed quants [n][row_bytes]
+    const uint16_t* d;      // scales [n][nb]
+    const uint8_t* qs2;     // FFN: up-matrix quants
+    const uint16_t* d2;     // FFN: up-matrix scales
+    const float* x;         // fp32 activations [k]
+    const int8_t* xq;       // Q8_0 activation codes [k]
+    const uint16_t* xd;     // Q8_0 activation scales [k/32]
+    float* y;               // output [n]
+    int32_t* blockdots;     // optional S [n][nb]
+    int n;
+    int units;              // 16-byte units per row
+    int nb;                 // blocks per row
+    int row_groups;         // ceil(n / R)
+};
+
+// fp32-activation dot of one unit against the lane's activation registers.
+template <int TYPE>
+__device__ __forceinline__ float unit_dot_f32(const uint4 q, const float* xr) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    float p = 0.0f;
+    if constexpr (TYPE == kTypeQ8_0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                p = fmaf(static_cast<float>(static_cast<int8_t>(w[j] >> (8 * b))), xr[4 * j + b], p);
+    } else {
+        // nibble ^ 8 read as a 4-bit two's-complement number is nibble - 8.
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t v = w[j] ^ 0x88888888u;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const float lo = static_cast<float>(static_cast<int32_t>(v << (28 - 8 * b)) >> 28);
+                const float hi = static_cast<float>(static_cast<int32_t>(v << (24 - 8 * b)) >> 28);
+                p = fmaf(lo, xr[4 * j + b], p);        // element 4j+b
+                p = fmaf(hi, xr[16 + 4 * j + b], p);   // element 16+4j+b
+            }
+        }
+    }
+    return p;
+}
+
+// Exact int32 dot of one unit against the lane's Q8_0 activation codes.
+// Q4_0: the unsigned nibbles (0..15, valid positive int8) are dotted and the
+// -8 offset is taken out with the exact integer sum of the codes, sx.
+template <int TYPE>
+__device__ __forceinline__ int unit_dot_q8(const uint4 q, const uint32_t* xr, int sx) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    int s = 0;
+    if constexpr (TYPE == kTypeQ8_0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s = dot4(w[j], xr[j], s);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            s = dot4(w[j] & 0x0F0F0F0Fu, xr[j], s);               // elements 4j..4j+3
+            s = dot4((w[j] >> 4) & 0x0F0F0F0Fu, xr[4 + j], s);    // elements 16+4j..
+        }
+        s -= 8 * sx;
+    }
+    return s;
+}
+
+// Waves per workgroup for a K split over WS waves: at least 4.
+template <int WS> struct Waves { static constexpr int value = WS < 4 ? 4 : WS; };
+
+template <int TYPE, int MODE, int NI, int WS, int R>
+__global__ __launch_bounds__(Waves<WS>::value * kWave)
+void qmv_kernel(const QmvParams p) {
+    constexpr int EPU = Fmt<TYPE>::kElemsPerUnit;
+    constexpr int SH = Fmt<TYPE>::kUnitToBlockShift;
+    constexpr int WAVES = Waves<WS>::value;
+    constexpr int SUBS = WAVES / WS;                // independent row groups per workgroup
+    constexpr int NMAT = (MODE == kFFN) ? 2 : 1;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int slice = wave % WS;
+    const int sub = wave / WS;
+    const int row_bytes = p.units * 16;
+
+    // ---- activation registers for this lane's units ----------------------
+    int unit[NI];
+    bool uvalid[NI];
+    float xr[(MODE == kQ8X) ? 1 : NI][(MODE == kQ8X) ? 1 : EPU];
+    uint32_t xqr[(MODE == kQ8X) ? NI : 1][(MODE == kQ8X) ? EPU / 4 : 1];
+    float dxr[NI];
+    int sxr[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        unit[i] = (slice * NI + i) * kWave + lane;
+        uvalid[i] = unit[i] < p.units;
+        const int e0 = unit[i] * EPU;
+        if constexpr (MODE != kQ8X) {
+            const float4* xs = reinterpret_cast<const float4*>(p.x + e0);
+#pragma unroll
+            for (int v = 0; v < EPU / 4; ++v) {
+                const float4 t = uvalid[i] ? xs[v] : make_float4(0.f, 0.f, 0.f, 0.f);
+                xr[i][4 * v + 0] = t.x; xr[i][4 * v + 1] = t.y;
+                xr[i][4 * v + 2] = t.z; xr[i][4 * v + 3] = t.w;
+            }
+            dxr[i] = 0.f; sxr[i] = 0;
+        } else {
+            const uint4* xs = reinterpret_cast<const uint4*>(p.xq + e0);
+#pragma unroll
+            for (int v = 0; v < EPU / 16; ++v) {
+                const uint4 t = uvalid[i] ? xs[v] : make_uint4(0u, 0u, 0u, 0u);
+                xqr[i][4 * v + 0] = t.x; xqr[i][4 * v + 1] = t.y;
+                xqr[i][4 * v + 2] = t.z; xqr[i][4 * v + 3] = t.w;
+            }
+            dxr[i] = uvalid[i] ? half_bits_to_float(p.xd[unit[i] >> SH]) : 0.f;
+            int sx = 0;
+            if constexpr (TYPE == kTypeQ4_0) {
+#pragma unroll
+                for (int v = 0; v < EPU / 4; ++v) sx = dot4(xqr[i][v], 0x01010101u, sx);
+            }
+            sxr[i] = sx;
+        }
+    }
+
+    __shared__ float part[WAVES][NMAT][R];
+
+    for (int it = blockIdx.x; it * SUBS < p.row_groups; it += gridDim.x) {
+        const int g = it * SUBS + sub;
+        const int r0 = g * R;
+        float acc[NMAT][R];
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[m][r] = 0.f;
+
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            uint4 q[NMAT][R];
+            uint16_t db[NMAT][R];
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) {
+                const uint8_t* qsm = (m == 0) ? p.qs : p.qs2;
+                const uint16_t* dm = (m == 0) ? p.d : p.d2;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int row = min(r0 + r, p.n - 1);   // rows past n: in-bounds, discarded
+                    if (uvalid[i]) {
+                        q[m][r] = *reinterpret_cast<const uint4*>(
+                            qsm + static_cast<int64_t>(row) * row_bytes + unit[i] * 16);
+                        db[m][r] = dm[static_cast<int64_t>(row) * p.nb + (unit[i] >> SH)];
+                    } else {
+                        q[m][r] = make_uint4(0u, 0u, 0u, 0u);
+                        db[m][r] = 0;
+                    }
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float dw = half_bits_to_float(db[m][r]);
+                    if constexpr (MODE != kQ8X) {
+                        acc[m][r] = fmaf(dw, unit_dot_f32<TYPE>(q[m][r], xr[i]), acc[m][r]);
+                    } else {
+                        int s = unit_dot_q8<TYPE>(q[m][r], xqr[i], sxr[i]);
+                        if constexpr (TYPE == kTypeQ8_0) {
+                            // a block is two adjacent lanes' units: S_b = s(2t) + s(2t+1)
+                            s += dpp_i32<kDppQuadSwap1>(s);
+                        }
+                        const bool owner = (TYPE == kTypeQ4_0) || ((lane & 1) == 0);
+                        const int row = r0 + r;
+                        if (p.blockdots != nullptr && owner && uvalid[i] && row < p.n)
+                            p.blockdots[static_cast<int64_t>(row) * p.nb + (unit[i] >> SH)] = s;
+                        const float sc = dw * dxr[i];          // exact: 11-bit x 11-bit
+                        acc[m][r] = owner ? fmaf(sc, static_cast<float>(s), acc[m][r]) : acc[m][r];
+                    }
+                }
+        }
+
+        // ---- cross-lane and cross-wave reduction ---------------------------
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[m][r] = wave_sum(acc[m][r]);
+
+        if constexpr (WS == 1) {
+            if (lane == 0) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int row = r0 + r;
+                    if (row < p.n) {
+                        if constexpr (MODE == kFFN)
+                            p.y[row] = gelu_tanh(acc[0][r]) * acc[1][r];
+                        else
+                            p.y[row] = acc[0][r];
+                    }
+                }
+            }
+        } else {
+            if (lane == 0) {
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                    for (int r = 0; r < R; ++r) part[wave][m][r] = acc[m][r];
+            }
+            __syncthreads();
+            if (slice == 0 && lane < R) {
+                const int row = r0 + lane;
+                float tot[NMAT];
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m) {
+                    float t = part[wave][m][lane];
+#pragma unroll
+                    for (int s = 1; s < WS; ++s) t += part[wave + s][m][lane];
+                    tot[m] = t;
+                }
+                if (row < p.n) {
+                    if constexpr (MODE == kFFN)
+                        p.y[row] = gelu_tanh(tot[0]) * tot[1];
+                    else
+                        p.y[row] = tot[0];
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launch: pick the K split (WS) and units per lane (NI) from k.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr int kRows = 4;            // rows per wave step
+constexpr int kMaxGrid = 1024;      // workgroups (4 per CU on 256 CUs)
+
+template <int TYPE, int MODE, int NI, int WS>
+hipError_t launch_cfg(QmvParams p, hipStream_t stream) {
+    constexpr int WAVES = Waves<WS>::value;
+    constexpr int SUBS = WAVES / WS;
+    p.row_groups = (p.n + kRows - 1) / kRows;
+    const int64_t iters = (static_cast<int64_t>(p.row_groups) + SUBS - 1) / SUBS;
+    const int64_t max_grid = kMaxGrid * 4 / WAVES;
+    const int grid = static_cast<int>(iters < max_grid ? iters : max_grid);
+    hipLaunchKernelGGL((qmv_kernel<TYPE, MODE, NI, WS, kRows>), dim3(grid), dim3(WAVES * kWave),
+                       0, stream, p);
+    return hipGetLastError();
+}
+
+// units per lane needed when the row is split over ws waves
+inline int units_per_lane(int units, int ws) {
+    const int per_wave = (units + ws - 1) / ws;
+    return (per_wave + kWave - 1) / kWave;
+}
+
+template <int TYPE, int MODE>
+hipError_t dispatch(QmvParams p, hipStream_t stream) {
+    // The lane's activation slice stays at <= 32 values in VGPRs (Q8_0: two
+    // units, Q4_0: one unit); longer rows are split over more waves.
+    constexpr int kNiMax = (TYPE == kTypeQ8_0) ? 2 : 1;
+    if (units_per_lane(p.units, 1) == 1) return launch_cfg<TYPE, MODE, 1, 1>(p, stream);
+    if (units_per_lane(p.units, 1) <= kNiMax) return launch_cfg<TYPE, MODE, kNiMax, 1>(p, stream);
+    if (units_per_lane(p.units, 2) <= kNiMax) return launch_cfg<TYPE, MODE, kNiMax, 2>(p, stream);
+    if (units_per_lane(p.units, 4) <= kNiMax) return launch_cfg<TYPE, MODE, kNiMax, 4>(p, stream);
+    if (units_per_lane(p.units, 8) <= kNiMax) return launch_cfg<TYPE, MODE, kNiMax, 8>(p, stream);
+    if (units_per_lane(p.units, 16) <= kNiMax) return launch_cfg<TYPE, MODE, kNiMax, 16>(p, stream);
+    return hipErrorInvalidValue;    // beyond the documented maximum k (32768)
+}
+
+QmvParams base_params(const void* qs, const uint16_t* d, int64_t n, int64_t k, int bytes_per_32) {
+    QmvParams p{};
+    p.qs = static_cast<const uint8_t*>(qs);
+    p.d = d;
+    p.n = static_cast<int>(n);
+    p.units = static_cast<int>(k / 32 * bytes_per_32 / 16);
+    p.nb = static_cast<int>(k / 32);
+    return p;
+}
+
+}  // namespace
+
+hipError_t launch_qmv_f32(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k,
+                          const float* x, float* y, hipStream_t stream) {
+    if (type == kTypeQ8_0) {
+        QmvParams p = base_params(qs, d, n, k, 32);
+        p.x = x; p.y = y;
+        return dispatch<kTypeQ8_0, kF32>(p, stream);
+    }
+    QmvParams p = base_params(qs, d, n, k, 16);
+    p.x = x; p.y = y;
+    return dispatch<kTypeQ4_0, kF32>(p, stream);
+}
+
+hipError_t launch_qmv_q8(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k,
+                         const int8_t* xq, const uint16_t* xd, float* y, int32_t* blockdots,
+                         hipStream_t stream) {
+    if (type == kTypeQ8_0) {
+        QmvParams p = base_params(qs, d, n, k, 32);
+        p.xq = xq; p.xd = xd; p.y = y; p.blockdots = blockdots;
+        return dispatch<kTypeQ8_0, kQ8X>(p, stream);
+    }
+    QmvParams p = base_params(qs, d, n, k, 16);
+    p.xq = xq; p.xd = xd; p.y = y; p.blockdots = blockdots;
+    return dispatch<kTypeQ4_0, kQ8X>(p, stream);
+}
+
+hipError_t launch_ffn_gate_up(const uint8_t* g_qs, const uint16_t* g_d, const uint8_t* u_qs,
+                              const uint16_t* u_d, int64_t n_ff, int64_t k, const float* x,
+                              float* h, hipStream_t stream) {
+    QmvParams p = base_params(g_qs, g_d, n_ff, k, 16);
+    p.qs2 = u_qs; p.d2 = u_d; p.x = x; p.y = h;
+    return dispatch<kTypeQ4_0, kFFN>(p, stream);
+}
+
+}  // namespace gq

@@ -1,0 +1,182 @@
+/*
+ * gq.h -- C ABI of libgq: GGUF Q8_0 / Q4_0 block-quantised weight x
+ * activation products on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (the pages this follows):
+ *  - every decode-step projection is a matrix-vector product against
+ *    block-quantised weights, and decode is bound by the weight stream
+ *    (Gemma-4-E2B raw-Metal port page, "Why this exists (the byte floor ...)";
+ *    TensorSharp Gemma 4 page, batched decode section);
+ *  - the projection contract is y = W x with W stored [out][in] row-major,
+ *    without materialising W^T (SafeC Gemma 4 DESIGN_NOTES page,
+ *    "Math primitives implementation status");
+ *  - Q4_0 is a 32-element, 18-byte block, Q8_0 is kept as the 8-bit
+ *    option (Gem native architecture page, "M4 Max operating assumptions");
+ *  - the caller picks an fp32-activation entry or a pre-quantised int8 one
+ *    (jouleclaw-loader-gguf BENCHMARKS page, "Matmul throughput -- Q8_0
+ *    scalar vs NEON" and "Q8_0 matmul -- NEON direct vs AMX-tiled");
+ *  - the gated FFN is down(gelu_tanh(gate x) * up x) (SafeC DESIGN_NOTES,
+ *    "Gated FFN"); gate+up fused in one pass (raw-Metal port page,
+ *    "Architecture", kernels bullet);
+ *  - prompt evaluation runs small-M tiles of up to 32 rows through each
+ *    projection (Gem native architecture page, "Ownership boundaries",
+ *    Metal/profiling bullets; raw-Metal port page, "Batched prefill").
+ *
+ * Formats (GGUF, little-endian):
+ *  - Q8_0 block, 34 B: binary16 scale d, then int8 q[32]; w_i = d * q_i.
+ *  - Q4_0 block, 18 B: binary16 scale d, then 16 bytes; byte j holds
+ *    element j in its low nibble and element j+16 in its high nibble;
+ *    w_i = d * (nibble_i - 8).
+ *  A weight matrix of n rows and k columns is n * k/32 blocks, row-major,
+ *  blocks along k.
+ *
+ * Packed layout (what every compute entry point reads; produced by gq_pack):
+ *  - qs: Q8_0 int8 [n][k] (row-major quants); Q4_0 uint8 [n][k/2] (the 16
+ *        quant bytes of each block, in GGUF in-block order, blocks along k);
+ *  - d : binary16 bits uint16 [n][k/32] (the block scales, row-major).
+ *  The pack only moves bytes: the same count as the GGUF blocks, split so
+ *  that every 16-byte quant chunk is 16-byte aligned.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named qs, d, x, y, h, xq, xd, blockdots and blocks are DEVICE
+ *    pointers on the current HIP device. The caller allocates and frees all
+ *    of them; libgq never allocates, frees or synchronises.
+ *  - Inputs are read-only. Outputs are fully overwritten.
+ *  - stream is a hipStream_t passed as void*; NULL is the default stream.
+ *    Work is enqueued asynchronously on that stream.
+ *  - Shapes: n >= 1, k >= 32, k % 32 == 0, else GQ_ERR_SHAPE. Each entry
+ *    point documents its maximum k (GQ_ERR_UNSUPPORTED beyond it); n is
+ *    limited to 2^31 - 1 rows.
+ *  - Alignment: qs, x, h and xq 16 bytes; d and xd 2 bytes; y and blockdots
+ *    4 bytes; else GQ_ERR_ALIGN.
+ *  - An output range overlapping any input range gives GQ_ERR_ALIAS.
+ *  - All validation is synchronous and happens before any HIP call: a call
+ *    that returns an error has launched nothing and written nothing.
+ *  - GQ_ERR_LAUNCH reports a failed kernel launch (hipGetLastError right
+ *    after the launch). Faults inside a kernel are asynchronous and surface
+ *    at the caller's next synchronisation.
+ *  - No global state: calls are reentrant and thread-safe. Identical inputs
+ *    give bitwise-identical outputs (fixed reduction order, no atomics).
+ */
+#ifndef GQ_H
+#define GQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GQ_ABI_VERSION 1
+
+enum {
+    GQ_OK = 0,
+    GQ_ERR_NULL = 1,         /* a required pointer is NULL */
+    GQ_ERR_SHAPE = 2,        /* n < 1, k < 32, k % 32 != 0, bad m */
+    GQ_ERR_ALIGN = 3,        /* a pointer violates its alignment */
+    GQ_ERR_ALIAS = 4,        /* an output overlaps an input */
+    GQ_ERR_UNSUPPORTED = 5,  /* unknown type, k or m beyond what is built */
+    GQ_ERR_LAUNCH = 6        /* the kernel launch failed */
+};
+
+enum {
+    GQ_TYPE_Q4_0 = 2,        /* GGUF type id of Q4_0 */
+    GQ_TYPE_Q8_0 = 8         /* GGUF type id of Q8_0 */
+};
+
+/* Version of this header's signatures; bumped on any change. */
+int gq_abi_version(void);
+
+/* Static, never-NULL description of a status code. */
+const char *gq_status_str(int status);
+
+/* Bytes of one GGUF block of `type` (34 or 18), 0 for an unknown type. */
+size_t gq_block_bytes(int type);
+
+/* Sizes of the packed arrays for an n x k matrix: qs is n*k (Q8_0) or
+ * n*k/2 (Q4_0) bytes, d is n*(k/32)*2 bytes. 0 for invalid arguments. */
+size_t gq_packed_qs_bytes(int type, int64_t n, int64_t k);
+size_t gq_packed_d_bytes(int64_t n, int64_t k);
+
+/*
+ * gq_pack -- split n x k/32 GGUF blocks (device memory, 34 or 18 bytes each,
+ * contiguous, any byte alignment) into the packed qs and d arrays above.
+ * No value changes. blocks must not overlap qs or d. Any k that is a
+ * multiple of 32 is accepted.
+ */
+int gq_pack(int type, const void *blocks, int64_t n, int64_t k,
+            void *qs, uint16_t *d, void *stream);
+
+/*
+ * gq_quantize_q8_0 -- quantise m rows of fp32 activations x [m][k] to Q8_0:
+ * per 32-element block, amax = max |x_i| (fp32); d = binary16(amax / 127)
+ * (fp32 divide, then round to nearest even); q_i = clamp(round half away
+ * from zero (x_i / d), -127, 127) with the divide in fp32 by the rounded
+ * d, and q_i = 0 when d == 0. Outputs xq int8 [m][k] and xd binary16 bits
+ * [m][k/32]. Inputs must be finite. Source: the activation quantiser of the
+ * jouleclaw-loader-gguf BENCHMARKS page ("Matmul throughput -- Q8_0 scalar
+ * vs NEON"), taken per 32-element block as in the GGUF Q8_0 format.
+ * m >= 1; any k that is a multiple of 32.
+ */
+int gq_quantize_q8_0(const float *x, int64_t m, int64_t k,
+                     int8_t *xq, uint16_t *xd, void *stream);
+
+/*
+ * gq_qmv_q8_0 / gq_qmv_q4_0 -- decode matvec with fp32 activations:
+ * y[r] = sum_c w[r][c] * x[c] for r < n, accumulated in fp32.
+ * Accuracy: |y - y_exact| <= 1e-4 * sum_c |w[r][c] x[c]| + 1e-6.
+ * qs/d packed as above; x fp32 [k]; y fp32 [n].
+ * Maximum k: 32768 (Q8_0), 65536 (Q4_0).
+ */
+int gq_qmv_q8_0(const int8_t *qs, const uint16_t *d, int64_t n, int64_t k,
+                const float *x, float *y, void *stream);
+int gq_qmv_q4_0(const uint8_t *qs, const uint16_t *d, int64_t n, int64_t k,
+                const float *x, float *y, void *stream);
+
+/*
+ * gq_qmv_q8_0_q8 / gq_qmv_q4_0_q8 -- decode matvec against one Q8_0
+ * activation row (xq int8 [k], xd binary16 bits [k/32]):
+ * S[r][b] = sum_i qw[r][b][i] * xq[b][i] computed exactly in int32
+ * (qw = q for Q8_0, nibble - 8 for Q4_0), y[r] = sum_b dw[r][b] * dx[b] * S
+ * in fp32. If blockdots is not NULL, S is also written to blockdots
+ * int32 [n][k/32]. Maximum k as for the fp32 entries.
+ */
+int gq_qmv_q8_0_q8(const int8_t *qs, const uint16_t *d, int64_t n, int64_t k,
+                   const int8_t *xq, const uint16_t *xd, float *y,
+                   int32_t *blockdots, void *stream);
+int gq_qmv_q4_0_q8(const uint8_t *qs, const uint16_t *d, int64_t n, int64_t k,
+                   const int8_t *xq, const uint16_t *xd, float *y,
+                   int32_t *blockdots, void *stream);
+
+/*
+ * gq_qffn_gate_up_gelu -- first half of the gated FFN, one pass over both
+ * Q4_0 matrices: g = Wg x, u = Wu x (Wg, Wu [n_ff][k] packed), and
+ * h[r] = G(g[r]) * u[r] with G the tanh-form GELU
+ * G(t) = 0.5 t (1 + tanh(sqrt(2/pi) (t + 0.044715 t^3))), evaluated so that
+ * it saturates (finite t never gives NaN). x fp32 [k]; h fp32 [n_ff].
+ * The down projection is a separate gq_qmv_q4_0(Wd, h) call: every row of
+ * it needs all of h. A fused [gate | up] weight is passed as two pointers
+ * into it. Maximum k: 65536.
+ */
+int gq_qffn_gate_up_gelu(const uint8_t *g_qs, const uint16_t *g_d,
+                         const uint8_t *u_qs, const uint16_t *u_d,
+                         int64_t n_ff, int64_t k, const float *x, float *h,
+                         void *stream);
+
+/*
+ * gq_qmm_tile_m -- small-M prefill tile, Q4_0 weights [n][k] against m
+ * Q8_0 activation rows (xq int8 [m][k], xd binary16 bits [m][k/32]):
+ * S[mi][r][b] exact in int32, y[mi][r] = sum_b dw[r][b] dx[mi][b] S (fp32),
+ * y fp32 [m][n]. blockdots, if not NULL, receives S as int32 [m][n][k/32].
+ * m must be 8, 16 or 32 (else GQ_ERR_UNSUPPORTED). Maximum k: 8192.
+ */
+int gq_qmm_tile_m(const uint8_t *qs, const uint16_t *d, int64_t n, int64_t k, int m,
+                  const int8_t *xq, const uint16_t *xd, float *y,
+                  int32_t *blockdots, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQ_H */

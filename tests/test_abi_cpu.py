@@ -1,0 +1,125 @@
+"""The C-ABI library on the host, no GPU needed: it loads, exports every
+symbol include/gq.h declares, reports sizes, and rejects every invalid
+argument combination with the documented status before any HIP call (so no
+kernel is ever launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gq.h")
+
+gq = pytest.importorskip("gguf_block_quant_amd")
+
+OK, NULL, SHAPE, ALIGN, ALIAS, UNSUP = 0, 1, 2, 3, 4, 5
+Q4, Q8 = 2, 8
+
+# Fake, never-dereferenced addresses: every call below fails validation first.
+A = 0x10000000          # 256-byte aligned "buffers", far apart
+B = 0x20000000
+C = 0x30000000
+D = 0x40000000
+E = 0x50000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char \*)\s*(gq_\w+)\s*\(", text, re.M)))
+
+
+def test_header_symbols_all_exported():
+    names = declared_functions()
+    assert len(names) >= 13
+    lib = ctypes.CDLL(gq.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+    # the binding wraps exactly the declared set
+    assert set(names) == set(gq._SIGS)
+
+
+def test_version_and_status_strings():
+    assert gq.abi_version() == 1
+    for s in range(7):
+        assert gq.status_str(s)
+    assert gq.status_str(99) == "unknown status"
+
+
+def test_sizes():
+    assert gq.block_bytes(Q8) == 34 and gq.block_bytes(Q4) == 18 and gq.block_bytes(3) == 0
+    assert gq.packed_qs_bytes(Q8, 64, 256) == 64 * 256
+    assert gq.packed_qs_bytes(Q4, 2048, 2048) == 2048 * 1024
+    assert gq.packed_d_bytes(2048, 2048) == 2048 * 64 * 2
+    # packed bytes equal the GGUF block bytes
+    assert gq.packed_qs_bytes(Q4, 10, 64) + gq.packed_d_bytes(10, 64) == 10 * 2 * 18
+    assert gq.packed_qs_bytes(Q8, 10, 64) + gq.packed_d_bytes(10, 64) == 10 * 2 * 34
+    assert gq.packed_qs_bytes(Q8, 10, 33) == 0 and gq.packed_d_bytes(0, 64) == 0
+
+
+L = gq.raw()
+
+
+def qmv(fn, qs=A, d=B, n=64, k=256, x=C, y=D):
+    return getattr(L, fn)(qs, d, n, k, x, y, None)
+
+
+@pytest.mark.parametrize("fn", ["gq_qmv_q8_0", "gq_qmv_q4_0"])
+def test_qmv_validation(fn):
+    assert qmv(fn, qs=None) == NULL
+    assert qmv(fn, d=None) == NULL
+    assert qmv(fn, x=None) == NULL
+    assert qmv(fn, y=None) == NULL
+    assert qmv(fn, n=0) == SHAPE
+    assert qmv(fn, k=0) == SHAPE
+    assert qmv(fn, k=48) == SHAPE
+    assert qmv(fn, k=-32) == SHAPE
+    assert qmv(fn, k=65536) == UNSUP
+    assert qmv(fn, n=(1 << 30) + 1) == UNSUP
+    assert qmv(fn, qs=A + 8) == ALIGN
+    assert qmv(fn, d=B + 1) == ALIGN
+    assert qmv(fn, x=C + 4) == ALIGN
+    assert qmv(fn, y=D + 2) == ALIGN
+    assert qmv(fn, y=A) == ALIAS              # output over the quants
+    assert qmv(fn, y=B + 64) == ALIAS         # output inside the scales
+    assert qmv(fn, y=C - 128) == ALIAS        # output running into x
+
+
+@pytest.mark.parametrize("fn", ["gq_qmv_q8_0_q8", "gq_qmv_q4_0_q8"])
+def test_qmv_q8_validation(fn):
+    f = getattr(L, fn)
+    assert f(A, B, 64, 256, C, None, D, None, None) == NULL
+    assert f(A, B, 64, 250, C, E, D, None, None) == SHAPE
+    assert f(A, B, 64, 256, C + 8, E, D, None, None) == ALIGN
+    assert f(A, B, 64, 256, C, E, D, D + 2, None) == ALIGN
+    assert f(A, B, 64, 256, C, E, D, D + 128, None) == ALIAS      # blockdots over y
+    assert f(A, B, 64, 256, C, E, D, A + 1024, None) == ALIAS     # blockdots over qs
+
+
+def test_ffn_validation():
+    f = L.gq_qffn_gate_up_gelu
+    assert f(A, B, None, B, 64, 256, C, D, None) == NULL
+    assert f(A, B, A, B, 64, 100, C, D, None) == SHAPE
+    assert f(A, B, A + 4, B, 64, 256, C, D, None) == ALIGN
+    assert f(A, B, C, B, 64, 256, E, B, None) == ALIAS
+    assert f(A, B, C, E, 64, 65536, C, D, None) == UNSUP
+
+
+def test_tile_validation():
+    f = L.gq_qmm_tile_m
+    assert f(A, B, 64, 256, 12, C, E, D, None, None) == UNSUP
+    assert f(A, B, 64, 256, 4, C, E, D, None, None) == UNSUP
+    assert f(A, B, 64, 256, 16, C, None, D, None, None) == NULL
+    assert f(A, B, 64, 0, 16, C, E, D, None, None) == SHAPE
+    assert f(A, B, 64, 256, 16, C + 1, E, D, None, None) == ALIGN
+    assert f(A, B, 64, 256, 16, C, E, D, D + 4 * 512, None) == ALIAS   # blockdots inside y
+
+
+def test_pack_and_quantize_validation():
+    assert L.gq_pack(3, A, 64, 256, B, C, None) == UNSUP
+    assert L.gq_pack(Q8, A, 64, 256, B + 8, C, None) == ALIGN
+    assert L.gq_pack(Q8, A, 64, 256, A + 34 * 16, C, None) == ALIAS
+    assert L.gq_pack(Q8, None, 64, 256, B, C, None) == NULL
+    assert L.gq_quantize_q8_0(A, 2, 100, B, C, None) == SHAPE
+    assert L.gq_quantize_q8_0(A + 4, 2, 128, B, C, None) == ALIGN
+    assert L.gq_quantize_q8_0(A, 2, 128, A + 16, C, None) == ALIAS
