@@ -7,6 +7,10 @@ prefix dropped), and raises ``GQError`` on a non-zero status. All compute
 runs in libgq's HIP kernels; there is no fallback. Importing this module
 fails loudly when libgq.so has not been built.
 
+The shared library is loaded on first use (so that the build step can run
+before it exists); using any entry point without a built libgq.so raises
+ImportError.
+
 Tensors are torch tensors (PyTorch supplies device memory and streams).
 Binary16 scale arrays are carried as int16/uint16 tensors of raw bits.
 """
@@ -25,12 +29,6 @@ GQ_OK = 0
 STATUS_NAMES = {0: "GQ_OK", 1: "GQ_ERR_NULL", 2: "GQ_ERR_SHAPE", 3: "GQ_ERR_ALIGN",
                 4: "GQ_ERR_ALIAS", 5: "GQ_ERR_UNSUPPORTED", 6: "GQ_ERR_LAUNCH"}
 
-if not os.path.exists(LIB_PATH):
-    raise ImportError(
-        "libgq.so is not built (expected at %s); run `python -m gguf_block_quant_amd.build` "
-        "or __graft_entry__.build()" % LIB_PATH)
-
-_lib = ctypes.CDLL(LIB_PATH)
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I = ctypes.c_int
@@ -38,6 +36,7 @@ _I = ctypes.c_int
 _SIGS = {
     "gq_abi_version": ([], _I),
     "gq_status_str": ([_I], ctypes.c_char_p),
+    "gq_last_hip_error": ([], _I),
     "gq_block_bytes": ([_I], ctypes.c_size_t),
     "gq_packed_qs_bytes": ([_I, _I64, _I64], ctypes.c_size_t),
     "gq_packed_d_bytes": ([_I64, _I64], ctypes.c_size_t),
@@ -50,42 +49,58 @@ _SIGS = {
     "gq_qffn_gate_up_gelu": ([_P, _P, _P, _P, _I64, _I64, _P, _P, _P], _I),
     "gq_qmm_tile_m": ([_P, _P, _I64, _I64, _I, _P, _P, _P, _P, _P], _I),
 }
-for _name, (_args, _res) in _SIGS.items():
-    _f = getattr(_lib, _name)
-    _f.argtypes = _args
-    _f.restype = _res
+_handle = None
 
 
 def raw():
-    """The ctypes handle of libgq (for tests that call the C ABI directly)."""
-    return _lib
+    """The ctypes handle of libgq, loaded on first use."""
+    global _handle
+    if _handle is None:
+        # libgq must resolve libamdhip64 to the HIP runtime torch already
+        # carries (same SONAME), so that device pointers and streams handed
+        # over from torch belong to the runtime that launches the kernels.
+        # Loading libgq first would pull in a second runtime.
+        import torch  # noqa: F401
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                "libgq.so is not built (expected at %s); run `python -m gguf_block_quant_amd.build` "
+                "or __graft_entry__.build()" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(lib, name)
+            f.argtypes = args
+            f.restype = res
+        _handle = lib
+    return _handle
 
 
 class GQError(RuntimeError):
     def __init__(self, status, fn):
         self.status = status
-        super().__init__("%s failed: %s (%s)" % (fn, STATUS_NAMES.get(status, status),
-                                                 status_str(status)))
+        self.hip_error = raw().gq_last_hip_error() if status == 6 else 0
+        extra = " [hipError %d]" % self.hip_error if status == 6 else ""
+        super().__init__("%s failed: %s (%s)%s" % (fn, STATUS_NAMES.get(status, status),
+                                                   status_str(status), extra))
 
 
 def abi_version() -> int:
-    return _lib.gq_abi_version()
+    return raw().gq_abi_version()
 
 
 def status_str(status: int) -> str:
-    return _lib.gq_status_str(status).decode()
+    return raw().gq_status_str(status).decode()
 
 
 def block_bytes(qtype: int) -> int:
-    return _lib.gq_block_bytes(qtype)
+    return raw().gq_block_bytes(qtype)
 
 
 def packed_qs_bytes(qtype: int, n: int, k: int) -> int:
-    return _lib.gq_packed_qs_bytes(qtype, n, k)
+    return raw().gq_packed_qs_bytes(qtype, n, k)
 
 
 def packed_d_bytes(n: int, k: int) -> int:
-    return _lib.gq_packed_d_bytes(n, k)
+    return raw().gq_packed_d_bytes(n, k)
 
 
 # ----------------------------------------------------------------------------
@@ -117,7 +132,7 @@ def _stream(stream):
 
 
 def _call(fn, *args):
-    st = getattr(_lib, fn)(*args)
+    st = getattr(raw(), fn)(*args)
     if st != GQ_OK:
         raise GQError(st, fn)
 

@@ -53,7 +53,13 @@ inline size_t qs_bytes(int type, int64_t n, int64_t k) {
 }
 inline size_t d_bytes(int64_t n, int64_t k) { return static_cast<size_t>(n) * static_cast<size_t>(k / 32) * 2; }
 
-inline int status_of(hipError_t e) { return e == hipSuccess ? GQ_OK : GQ_ERR_LAUNCH; }
+// HIP status of this thread's most recent launch attempt (diagnostics only).
+thread_local int t_last_hip_error = 0;
+
+inline int status_of(hipError_t e) {
+    t_last_hip_error = static_cast<int>(e);
+    return e == hipSuccess ? GQ_OK : GQ_ERR_LAUNCH;
+}
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 // Checks shared by the two matvec families: packed weights, n, k.
@@ -97,6 +103,8 @@ int qmv_q8(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k, co
 extern "C" {
 
 int gq_abi_version(void) { return GQ_ABI_VERSION; }
+
+int gq_last_hip_error(void) { return t_last_hip_error; }
 
 const char* gq_status_str(int status) {
     switch (status) {

@@ -6,7 +6,26 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <type_traits>
+
 namespace gq {
+
+// Launch through hipLaunchKernel so the returned status belongs to this
+// launch alone (a triple-chevron launch is only observable through
+// hipGetLastError, which also reports errors left behind by other callers).
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                         Args... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+    std::tuple<std::decay_t<KArgs>...> vals(static_cast<std::decay_t<KArgs>>(args)...);
+    void* ptrs[sizeof...(KArgs)];
+    std::apply([&ptrs](auto&... v) {
+        size_t i = 0;
+        ((ptrs[i++] = static_cast<void*>(&v)), ...);
+    }, vals);
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, 0, stream);
+}
 
 constexpr int64_t kMaxK = 32768;          // every compute entry point
 constexpr int64_t kMaxRows = int64_t(1) << 30;

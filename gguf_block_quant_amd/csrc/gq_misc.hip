@@ -37,13 +37,9 @@ hipError_t launch_pack(int type, const uint8_t* blocks, int64_t n, int64_t k, ui
                        uint16_t* d, hipStream_t stream) {
     const int64_t nblocks = n * (k / 32);
     const int64_t grid = (nblocks + kBlockThreads - 1) / kBlockThreads;
-    if (type == kTypeQ8_0)
-        hipLaunchKernelGGL(pack_kernel<kTypeQ8_0>, dim3(static_cast<unsigned>(grid)), dim3(kBlockThreads),
-                           0, stream, blocks, nblocks, qs, d);
-    else
-        hipLaunchKernelGGL(pack_kernel<kTypeQ4_0>, dim3(static_cast<unsigned>(grid)), dim3(kBlockThreads),
-                           0, stream, blocks, nblocks, qs, d);
-    return hipGetLastError();
+    const dim3 g(static_cast<unsigned>(grid)), b(kBlockThreads);
+    if (type == kTypeQ8_0) return launch_kernel(pack_kernel<kTypeQ8_0>, g, b, stream, blocks, nblocks, qs, d);
+    return launch_kernel(pack_kernel<kTypeQ4_0>, g, b, stream, blocks, nblocks, qs, d);
 }
 
 // ---------------------------------------------------------------------------
@@ -102,9 +98,8 @@ hipError_t launch_quantize_q8_0(const float* x, int64_t m, int64_t k, int8_t* xq
                                 hipStream_t stream) {
     const int64_t nblocks = m * (k / 32);
     const int64_t grid = (nblocks + kBlockThreads - 1) / kBlockThreads;
-    hipLaunchKernelGGL(quantize_q8_0_kernel, dim3(static_cast<unsigned>(grid)), dim3(kBlockThreads), 0,
-                       stream, x, nblocks, xq, xd);
-    return hipGetLastError();
+    return launch_kernel(quantize_q8_0_kernel, dim3(static_cast<unsigned>(grid)), dim3(kBlockThreads), stream,
+                         x, nblocks, xq, xd);
 }
 
 }  // namespace gq

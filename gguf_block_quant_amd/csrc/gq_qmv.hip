@@ -279,9 +279,7 @@ hipError_t launch_cfg(QmvParams p, hipStream_t stream) {
     const int64_t iters = (static_cast<int64_t>(p.row_groups) + SUBS - 1) / SUBS;
     const int64_t max_grid = kMaxGrid * 4 / WAVES;
     const int grid = static_cast<int>(iters < max_grid ? iters : max_grid);
-    hipLaunchKernelGGL((qmv_kernel<TYPE, MODE, NI, WS, kRows>), dim3(grid), dim3(WAVES * kWave),
-                       0, stream, p);
-    return hipGetLastError();
+    return launch_kernel(qmv_kernel<TYPE, MODE, NI, WS, kRows>, dim3(grid), dim3(WAVES * kWave), stream, p);
 }
 
 // units per lane needed when the row is split over ws waves

@@ -131,12 +131,10 @@ hipError_t launch_tile_q4_0(const uint8_t* qs, const uint16_t* d, int64_t n, int
     const int grid = static_cast<int>((n + 15) / 16);
     const int nb = static_cast<int>(k / 32);
     if (m <= 16)
-        hipLaunchKernelGGL(tile_kernel<1>, dim3(grid), dim3(kBlockThreads), 0, stream, qs, d,
-                           static_cast<int>(n), nb, m, xq, xd, y, blockdots);
-    else
-        hipLaunchKernelGGL(tile_kernel<2>, dim3(grid), dim3(kBlockThreads), 0, stream, qs, d,
-                           static_cast<int>(n), nb, m, xq, xd, y, blockdots);
-    return hipGetLastError();
+        return launch_kernel(tile_kernel<1>, dim3(grid), dim3(kBlockThreads), stream, qs, d,
+                             static_cast<int>(n), nb, m, xq, xd, y, blockdots);
+    return launch_kernel(tile_kernel<2>, dim3(grid), dim3(kBlockThreads), stream, qs, d,
+                         static_cast<int>(n), nb, m, xq, xd, y, blockdots);
 }
 
 }  // namespace gq

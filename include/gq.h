@@ -52,9 +52,10 @@
  *  - An output range overlapping any input range gives GQ_ERR_ALIAS.
  *  - All validation is synchronous and happens before any HIP call: a call
  *    that returns an error has launched nothing and written nothing.
- *  - GQ_ERR_LAUNCH reports a failed kernel launch (hipGetLastError right
- *    after the launch). Faults inside a kernel are asynchronous and surface
- *    at the caller's next synchronisation.
+ *  - GQ_ERR_LAUNCH reports a failed kernel launch: the status returned by
+ *    hipLaunchKernel for that launch (gq_last_hip_error() gives the HIP
+ *    code). Faults inside a kernel are asynchronous and surface at the
+ *    caller's next synchronisation.
  *  - No global state: calls are reentrant and thread-safe. Identical inputs
  *    give bitwise-identical outputs (fixed reduction order, no atomics).
  */
@@ -90,6 +91,12 @@ int gq_abi_version(void);
 
 /* Static, never-NULL description of a status code. */
 const char *gq_status_str(int status);
+
+/* The hipError_t value (as int) returned by the calling thread's most recent
+ * kernel launch inside libgq: 0 after a successful launch, the HIP error
+ * behind a GQ_ERR_LAUNCH otherwise. Thread-local; validation failures do
+ * not change it. */
+int gq_last_hip_error(void);
 
 /* Bytes of one GGUF block of `type` (34 or 18), 0 for an unknown type. */
 size_t gq_block_bytes(int type);

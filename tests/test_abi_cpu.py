@@ -57,7 +57,7 @@ def test_sizes():
     assert gq.packed_qs_bytes(Q8, 10, 33) == 0 and gq.packed_d_bytes(0, 64) == 0
 
 
-L = gq.raw()
+L = gq.raw()  # loads libgq.so
 
 
 def qmv(fn, qs=A, d=B, n=64, k=256, x=C, y=D):
