@@ -1,0 +1,415 @@
+#!/usr/bin/env python3
+"""Benchmark: effective weight GB/s of the block-quantised decode hot path.
+
+One *step* is one pass of the whole hot path over one batch of synthetic
+inputs, shaped like one decode step that streams many different weights
+(the pages define effective bandwidth as bytes per token x tokens/s):
+
+  1. quantize_q8_0      x[2048] -> Q8_0 codes + scales
+  2. qmv_q4_0           Q4_0 2048 x 2048, fp32 x
+  3. qmv_q4_0_q8        Q4_0 2048 x 2048, Q8_0 x (int path, own weight copy)
+  4. qffn_gate_up_gelu  Q4_0 gate and up 8192 x 2048 -> h = G(gate x) * up x
+  5. qmv_q4_0           Q4_0 down 2048 x 8192 against h
+  6. qmv_q8_0           Q8_0 vocab 262144 x 2048 (0.57 GB of blocks), fp32 x
+  7. qmm_tile_m         Q4_0 8192 x 2048 against M = 8, 16, 32 Q8_0 rows
+
+Every weight matrix is a distinct allocation, and ``--sets`` full copies of
+the step's weights are rotated so nothing is served from the 256 MB
+last-level cache between its uses. Inputs are resident in HBM before the
+timed region. ``value`` = weight-block bytes streamed per step x steps /
+wall time of the timed steps.
+
+The roofline object is for the dominant kernel (the Q8_0 vocab matvec,
+about 90 % of the step's bytes): algorithmic bytes per launch (weight
+blocks + x + y) / its average duration from HIP events recorded around each
+of its launches on the launch stream inside the timed region.
+
+Modes:
+  python bench.py [--steps K --warmup W]    the benchmark (one JSON line)
+  python bench.py --mode pmc                 vocab kernel + a calibration copy
+                                             only, for rocprofv3 --pmc runs
+  python bench.py --pmc-summary DIR --counter FETCH_SIZE|WRITE_SIZE
+                                             summarise a rocprofv3 counter run
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective weight GB/s and % of HBM peak for Q4_0/Q8_0 matvec at M=1"
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "qmv_q8_0_vocab_262144x2048_hbm_traffic.txt")
+DOMINANT = "qmv_q8_0 262144x2048 (vocab)"
+COPY_BYTES = 512 * 1024 * 1024        # calibration copy for the HBM counters
+
+
+def kernel_source_hash() -> str:
+    """Hash of the sources the dominant kernel is built from."""
+    h = hashlib.sha256()
+    for name in ("gq_qmv.hip", "gq_device.hpp", "gq_launch.hpp"):
+        with open(os.path.join(ROOT, "gguf_block_quant_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------
+# workload
+# ----------------------------------------------------------------------------
+
+class Step:
+    """The step's launches, with every pointer and size precomputed so the
+    host issues each C-ABI call directly (a few microseconds each)."""
+
+    def __init__(self, sets: int, log):
+        import ctypes
+
+        import numpy as np
+        import torch
+
+        import gguf_block_quant_amd as gq
+        import synth
+
+        self.torch = torch
+        self.gq = gq
+        L = gq.raw()
+        dev = torch.device("cuda:0")
+        self.stream = torch.cuda.current_stream()
+        sp = ctypes.c_void_p(self.stream.cuda_stream)
+        P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+
+        def up(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                a = a.view(np.int16)
+            return torch.from_numpy(a).to(dev)
+
+        def pack(qtype, blocks, n, k):
+            raw = up(synth.as_bytes(blocks).reshape(-1))
+            qs, d = gq.pack(qtype, raw, n, k)
+            torch.cuda.synchronize()
+            del raw
+            return qs, d
+
+        t0 = time.time()
+        c2 = synth.workload_q4_0_2048()
+        c3 = synth.workload_ffn()
+        c5 = synth.workload_tile()
+        log("generated small workloads in %.1fs" % (time.time() - t0))
+        t0 = time.time()
+        c4 = synth.workload_vocab()
+        log("generated vocab workload in %.1fs" % (time.time() - t0))
+        self.host = {"c2": c2, "c3": c3, "c4": c4, "c5": c5}
+
+        Q4, Q8 = gq.TYPE_Q4_0, gq.TYPE_Q8_0
+        x2, x3, x4 = up(c2["x"]), up(c3["x"]), up(c4["x"])
+        xq2 = torch.empty(2048, dtype=torch.int8, device=dev)
+        xd2 = torch.empty(64, dtype=torch.int16, device=dev)
+        y2a = torch.empty(2048, dtype=torch.float32, device=dev)
+        y2b = torch.empty(2048, dtype=torch.float32, device=dev)
+        h3 = torch.empty(8192, dtype=torch.float32, device=dev)
+        y3 = torch.empty(2048, dtype=torch.float32, device=dev)
+        y4 = torch.empty(262144, dtype=torch.float32, device=dev)
+        acts = {m: (up(c5["acts"][m][0]), up(c5["acts"][m][1])) for m in (8, 16, 32)}
+        yt = {m: torch.empty((m, 8192), dtype=torch.float32, device=dev) for m in (8, 16, 32)}
+        self.keep = [x2, x3, x4, xq2, xd2, y2a, y2b, h3, y3, y4, acts, yt]
+        self.outputs = {"y2a": y2a, "y2b": y2b, "h3": h3, "y3": y3, "y4": y4, "yt": yt}
+
+        t0 = time.time()
+        self.sets = []
+        for s in range(sets):
+            w2a = pack(Q4, c2["w"], 2048, 2048)
+            w2b = pack(Q4, c2["w"], 2048, 2048)
+            wg = pack(Q4, c3["wg"], 8192, 2048)
+            wu = pack(Q4, c3["wu"], 8192, 2048)
+            wd = pack(Q4, c3["wd"], 2048, 8192)
+            wv = pack(Q8, c4["w"], 262144, 2048)
+            wt = {m: pack(Q4, c5["w"], 8192, 2048) for m in (8, 16, 32)}
+            self.keep.append((w2a, w2b, wg, wu, wd, wv, wt))
+            launches = [
+                ("quantize_q8_0 2048", L.gq_quantize_q8_0, (P(x2), 1, 2048, P(xq2), P(xd2), sp), 0, 2048 * 4 + 2048 + 128),
+                ("qmv_q4_0 2048x2048", L.gq_qmv_q4_0, (P(w2a[0]), P(w2a[1]), 2048, 2048, P(x2), P(y2a), sp),
+                 2048 * 64 * 18, 8192 + 8192),
+                ("qmv_q4_0_q8 2048x2048", L.gq_qmv_q4_0_q8,
+                 (P(w2b[0]), P(w2b[1]), 2048, 2048, P(xq2), P(xd2), P(y2b), None, sp), 2048 * 64 * 18, 2176 + 8192),
+                ("qffn_gate_up_gelu 8192x2048", L.gq_qffn_gate_up_gelu,
+                 (P(wg[0]), P(wg[1]), P(wu[0]), P(wu[1]), 8192, 2048, P(x3), P(h3), sp), 2 * 8192 * 64 * 18,
+                 8192 + 32768),
+                ("qmv_q4_0 2048x8192 (down)", L.gq_qmv_q4_0, (P(wd[0]), P(wd[1]), 2048, 8192, P(h3), P(y3), sp),
+                 2048 * 256 * 18, 32768 + 8192),
+                (DOMINANT, L.gq_qmv_q8_0, (P(wv[0]), P(wv[1]), 262144, 2048, P(x4), P(y4), sp),
+                 262144 * 64 * 34, 8192 + 262144 * 4),
+            ]
+            for m in (8, 16, 32):
+                launches.append(("qmm_tile_m 8192x2048 M=%d" % m, L.gq_qmm_tile_m,
+                                 (P(wt[m][0]), P(wt[m][1]), 8192, 2048, m, P(acts[m][0]), P(acts[m][1]),
+                                  P(yt[m]), None, sp), 8192 * 64 * 18, m * 2176 + m * 8192 * 4))
+            self.sets.append(launches)
+        torch.cuda.synchronize()
+        log("packed %d weight set(s) in %.1fs" % (sets, time.time() - t0))
+        self.names = [l[0] for l in self.sets[0]]
+        self.weight_bytes = {l[0]: l[3] for l in self.sets[0]}
+        self.other_bytes = {l[0]: l[4] for l in self.sets[0]}
+        self.step_weight_bytes = sum(self.weight_bytes.values())
+
+    def run(self, i, events=None):
+        """Enqueue step i; events maps a launch name to a list collecting
+        (start, end) event pairs recorded around that launch."""
+        for name, fn, args, _, _ in self.sets[i % len(self.sets)]:
+            if events is not None and name in events:
+                a = self.torch.cuda.Event(enable_timing=True)
+                b = self.torch.cuda.Event(enable_timing=True)
+                a.record(self.stream)
+                st = fn(*args)
+                b.record(self.stream)
+                events[name].append((a, b))
+            else:
+                st = fn(*args)
+            if st != 0:
+                raise self.gq.GQError(st, name)
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle, as it stands, on the same inputs
+# ----------------------------------------------------------------------------
+
+def cpu_baseline(host, weight_bytes_per_step, seconds, log):
+    import numpy as np
+
+    import oracle
+
+    c2, c3, c4, c5 = host["c2"], host["c3"], host["c4"], host["c5"]
+    Q4, Q8 = oracle.TYPE_Q4_0, oracle.TYPE_Q8_0
+
+    def one_pass():
+        oracle.matvec(Q4, c2["w"], 2048, 2048, c2["x"])
+        xq, xd = oracle.quantize_q8_0(c2["x"])
+        oracle.blockdots(Q4, c2["w"], 2048, 2048, xq, xd, want_s=False)
+        f = oracle.ffn_gate_up(Q4, c3["wg"], c3["wu"], 8192, 2048, c3["x"])
+        oracle.matvec(Q4, c3["wd"], 2048, 8192, f["h"])
+        oracle.matvec(Q8, c4["w"], 262144, 2048, c4["x"])
+        for m in (8, 16, 32):
+            oracle.blockdots(Q4, c5["w"], 8192, 2048, c5["acts"][m][0], c5["acts"][m][1], want_s=False)
+
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        one_pass()
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    log("oracle: %d pass(es) in %.1fs" % (passes, el))
+    return {
+        "value": round(weight_bytes_per_step * passes / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "%d full pass(es) of the step's workload (every kernel once, same inputs) through the "
+                  "single-threaded fp64 C oracle, %.1f s; weight-block bytes / time" % (passes, el),
+        "seconds_per_step": round(el / passes, 3),
+        "cpu": platform.processor() or platform.machine(),
+    }
+
+
+# ----------------------------------------------------------------------------
+# rocprofv3 counter runs
+# ----------------------------------------------------------------------------
+
+def pmc_mode(args, log):
+    """Only the vocab kernel (3 launches) and a calibration copy of known
+    size (3 launches), so a rocprofv3 --pmc pass stays short."""
+    import torch
+
+    step = Step(1, log)
+    name, fn, fargs, _, _ = [l for l in step.sets[0] if l[0] == DOMINANT][0]
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        if fn(*fargs) != 0:
+            raise RuntimeError("launch failed")
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("pmc pass done: 3 x %s, 3 x copy of %d bytes" % (name, COPY_BYTES))
+
+
+def pmc_summary(args):
+    """Average a counter per kernel from a rocprofv3 counter_collection.csv and
+    scale it by the same counter's reading for the calibration copy."""
+    files = glob.glob(os.path.join(args.pmc_summary, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % args.pmc_summary)
+    per = {}
+    for fn in files:
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != args.counter:
+                    continue
+                per.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    out = {}
+    for k, v in per.items():
+        out[k] = sum(v) / len(v)
+    copy = [v for k, v in out.items() if "copy" in k.lower() or "elementwise" in k.lower()]
+    gq_k = [v for k, v in out.items() if "qmv_kernel" in k]
+    res = {"counter": args.counter, "per_kernel_avg": out}
+    if args.counter == "FETCH_SIZE":
+        # the copy reads COPY_BYTES: factor turns counter units into bytes
+        res["calibration_factor"] = COPY_BYTES / (max(copy) if copy else float("nan"))
+    elif args.counter == "WRITE_SIZE":
+        res["calibration_factor"] = COPY_BYTES / (max(copy) if copy else float("nan"))
+    res["qmv_kernel_avg"] = gq_k[0] if gq_k else None
+    print(json.dumps(res, indent=1))
+
+
+# ----------------------------------------------------------------------------
+# main
+# ----------------------------------------------------------------------------
+
+def load_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None if it is missing or was taken from other kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["fetch_bytes_per_launch"]) + float(vals["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=2, help="rotated copies of the step's weights")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["bench", "pmc"], default="bench")
+    ap.add_argument("--pmc-summary", default=None)
+    ap.add_argument("--counter", default="FETCH_SIZE")
+    args = ap.parse_args()
+
+    def log(msg):
+        print("[bench] " + msg, file=sys.stderr, flush=True)
+
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this path runs on a single MI355X and has no multi-GPU "
+              "mode (asked for --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.mode == "pmc":
+        pmc_mode(args, log)
+        return
+
+    step = Step(args.sets, log)
+    for i in range(args.warmup):
+        step.run(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, synchronised on both sides
+    ev = {DOMINANT: []}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step.run(i, ev)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    value = step.step_weight_bytes * args.steps / elapsed / 1e9
+
+    dom_ms = [a.elapsed_time(b) for a, b in ev[DOMINANT]]
+    dom_avg_s = sum(dom_ms) / len(dom_ms) / 1e3
+    dom_bytes = step.weight_bytes[DOMINANT] + step.other_bytes[DOMINANT]
+    achieved = dom_bytes / dom_avg_s / 1e9
+
+    # per-kernel breakdown (separate, untimed pass with events around every launch)
+    bev = {n: [] for n in step.names}
+    nb = min(20, max(4, args.steps // 10))
+    for i in range(nb):
+        step.run(i, bev)
+    torch.cuda.synchronize()
+    breakdown = {}
+    for n in step.names:
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in bev[n])
+        med = us[len(us) // 2]
+        wb = step.weight_bytes[n]
+        breakdown[n] = {"median_us": round(med, 2), "weight_bytes": wb,
+                        "weight_GBps": round(wb / med / 1e3, 1) if wb else None,
+                        "total_GBps": round((wb + step.other_bytes[n]) / med / 1e3, 1)}
+
+    traffic = load_traffic()
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(step.host, step.step_weight_bytes, args.cpu_seconds, log)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode step over distinct weights: q4_0 2048x2048 (fp32 x; and q8_0 x incl. "
+                        "quantize), ffn q4_0 gate+up 8192x2048 + down 2048x8192, q8_0 vocab 262144x2048, "
+                        "prefill tile q4_0 8192x2048 at M=8,16,32",
+            "weight_bytes_per_step": step.step_weight_bytes,
+            "weight_sets_rotated": args.sets,
+            "launches_per_step": len(step.names),
+        },
+        "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
+        "tokens_per_s_equiv": round(1e3 / ms_per_step, 1),
+        "roofline": {
+            "kernel": DOMINANT,
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": dom_bytes,
+            "avg_launch_us": round(dom_avg_s * 1e6, 2),
+            "launches_timed": len(dom_ms),
+        },
+        "cpu_baseline": cpu,
+        "breakdown": breakdown,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
