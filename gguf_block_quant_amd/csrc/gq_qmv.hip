@@ -23,6 +23,19 @@
 #include "gq_device.hpp"
 #include "gq_launch.hpp"
 
+#ifndef GQ_QMV_ROWS
+#define GQ_QMV_ROWS 4          // rows per wave step
+#endif
+#ifndef GQ_QMV_MAX_GRID
+#define GQ_QMV_MAX_GRID 1024   // workgroups of 4 waves (4 per CU on 256 CUs)
+#endif
+#ifndef GQ_QMV_PIPE
+#define GQ_QMV_PIPE 0          // prefetch the next row group's quants
+#endif
+#ifndef GQ_QMV_NT
+#define GQ_QMV_NT 1            // non-temporal loads for the quant stream (read once)
+#endif
+
 namespace gq {
 
 enum Mode { kF32 = 0, kQ8X = 1, kFFN = 2 };
@@ -160,19 +173,12 @@ void qmv_kernel(const QmvParams p) {
 
     __shared__ float part[WAVES][NMAT][R];
 
-    for (int it = blockIdx.x; it * SUBS < p.row_groups; it += gridDim.x) {
-        const int g = it * SUBS + sub;
-        const int r0 = g * R;
-        float acc[NMAT][R];
+    // Quant chunks and scales of one row group, for every unit of the lane.
+    uint4 q[2][NI][NMAT][R];
+    uint16_t db[2][NI][NMAT][R];
+    auto load_group = [&](int buf, int r0) {
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-            for (int r = 0; r < R; ++r) acc[m][r] = 0.f;
-
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            uint4 q[NMAT][R];
-            uint16_t db[NMAT][R];
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
             for (int m = 0; m < NMAT; ++m) {
                 const uint8_t* qsm = (m == 0) ? p.qs : p.qs2;
@@ -181,24 +187,51 @@ void qmv_kernel(const QmvParams p) {
                 for (int r = 0; r < R; ++r) {
                     const int row = min(r0 + r, p.n - 1);   // rows past n: in-bounds, discarded
                     if (uvalid[i]) {
-                        q[m][r] = *reinterpret_cast<const uint4*>(
+                        const uint4* src = reinterpret_cast<const uint4*>(
                             qsm + static_cast<int64_t>(row) * row_bytes + unit[i] * 16);
-                        db[m][r] = dm[static_cast<int64_t>(row) * p.nb + (unit[i] >> SH)];
+#if GQ_QMV_NT
+                        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+                        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+                        q[buf][i][m][r] = make_uint4(t.x, t.y, t.z, t.w);
+#else
+                        q[buf][i][m][r] = *src;
+#endif
+                        db[buf][i][m][r] = dm[static_cast<int64_t>(row) * p.nb + (unit[i] >> SH)];
                     } else {
-                        q[m][r] = make_uint4(0u, 0u, 0u, 0u);
-                        db[m][r] = 0;
+                        q[buf][i][m][r] = make_uint4(0u, 0u, 0u, 0u);
+                        db[buf][i][m][r] = 0;
                     }
                 }
             }
+    };
+
+    int it = blockIdx.x;
+    if (it * SUBS < p.row_groups) load_group(0, (it * SUBS + sub) * R);
+    for (; it * SUBS < p.row_groups; it += gridDim.x) {
+        const int g = it * SUBS + sub;
+        const int r0 = g * R;
+        const int itn = it + gridDim.x;
+#if GQ_QMV_PIPE
+        // issue the next row group's loads before computing this one
+        if (itn * SUBS < p.row_groups) load_group(1, (itn * SUBS + sub) * R);
+#endif
+        float acc[NMAT][R];
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[m][r] = 0.f;
+
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const float dw = half_bits_to_float(db[m][r]);
+                    const float dw = half_bits_to_float(db[0][i][m][r]);
                     if constexpr (MODE != kQ8X) {
-                        acc[m][r] = fmaf(dw, unit_dot_f32<TYPE>(q[m][r], xr[i]), acc[m][r]);
+                        acc[m][r] = fmaf(dw, unit_dot_f32<TYPE>(q[0][i][m][r], xr[i]), acc[m][r]);
                     } else {
-                        int s = unit_dot_q8<TYPE>(q[m][r], xqr[i], sxr[i]);
+                        int s = unit_dot_q8<TYPE>(q[0][i][m][r], xqr[i], sxr[i]);
                         if constexpr (TYPE == kTypeQ8_0) {
                             // a block is two adjacent lanes' units: S_b = s(2t) + s(2t+1)
                             s += dpp_i32<kDppQuadSwap1>(s);
@@ -212,6 +245,19 @@ void qmv_kernel(const QmvParams p) {
                     }
                 }
         }
+#if GQ_QMV_PIPE
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    q[0][i][m][r] = q[1][i][m][r];
+                    db[0][i][m][r] = db[1][i][m][r];
+                }
+#else
+        if (itn * SUBS < p.row_groups) load_group(0, (itn * SUBS + sub) * R);
+#endif
 
         // ---- cross-lane and cross-wave reduction ---------------------------
 #pragma unroll
@@ -268,8 +314,8 @@ void qmv_kernel(const QmvParams p) {
 
 namespace {
 
-constexpr int kRows = 4;            // rows per wave step
-constexpr int kMaxGrid = 1024;      // workgroups (4 per CU on 256 CUs)
+constexpr int kRows = GQ_QMV_ROWS;
+constexpr int kMaxGrid = GQ_QMV_MAX_GRID;
 
 template <int TYPE, int MODE, int NI, int WS>
 hipError_t launch_cfg(QmvParams p, hipStream_t stream) {

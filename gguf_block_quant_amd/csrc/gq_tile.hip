@@ -8,20 +8,25 @@
 // so it goes to MFMA, while the M = 1 path stays a streaming matvec.
 //
 // One v_mfma_i32_16x16x32_i8 covers exactly one 32-element block (K = 32),
-// so every MFMA result is a per-block integer dot S[n][m] -- exact, and
+// so every MFMA result is a per-block integer dot S[m][n] -- exact, and
 // separable from the per-block scales. The fp32 epilogue then adds
-// dw[n][b] * dx[m][b] * S into the accumulators.
+// dx[m][b] * dw[n][b] * S into the accumulators.
 //
-// Operand layout (gfx950 MFMA 16x16x32 int8; lane l, s = l / 16):
-//   A (weights, 16 rows x 32 k): lane holds row l % 16, k = 8s .. 8s+7;
-//   B (activations, 32 k x 16 cols): lane holds col l % 16, k = 8s .. 8s+7;
-//   D (16 x 16 int32): lane holds rows 4s .. 4s+3 of col l % 16.
+// Operand layout (gfx950 MFMA 16x16x32 int8; lane l, s = l / 16, c = l % 16):
+//   A (activations, 16 rows x 32 k): lane holds row c, k = 8s .. 8s+7;
+//   B (weights, 32 k x 16 cols):     lane holds col c, k = 8s .. 8s+7;
+//   D (16 x 16 int32):               lane holds rows 4s .. 4s+3 of col c.
 // Q4_0 byte j of a block holds elements j (low nibble) and j+16 (high), so
 // k = 8s..8s+7 is bytes 8(s&1)..+7, low nibbles for s < 2, high for s >= 2.
 //
-// Work split: a wave owns 16 weight rows (one A tile) and 1/4 of the blocks
-// of k; the four waves of a workgroup cover all of k for the same rows and
-// add their fp32 partials through LDS in slice order (deterministic).
+// Work split: a workgroup owns 16 weight rows and walks k in chunks of
+// kChunk blocks. Each chunk's weight rows, activation codes and both scale
+// sets are staged in LDS with contiguous 16-byte global loads (the weight
+// rows stream from HBM one 512-byte run per row; the activations are
+// shared by every workgroup and come from L2), while the registers already
+// hold the next chunk's loads. The four waves split the chunk's blocks; their
+// fp32 partials meet in LDS and are added in wave order (deterministic).
+// LDS rows are padded so the MFMA fragment reads are bank-conflict free.
 #include "gq_device.hpp"
 #include "gq_launch.hpp"
 
@@ -31,36 +36,94 @@ typedef int int32x4_t __attribute__((ext_vector_type(4)));
 
 namespace {
 
-// 8 unsigned nibbles (two dwords of bytes 0..15) -> 8 signed bytes (q - 8):
+constexpr int kChunk = 32;                         // blocks per chunk
+constexpr int kWPitch = kChunk * 16 + 16;          // weight row bytes in LDS (mod 256 = 16)
+constexpr int kXPitch = kChunk * 32 + 32;          // activation row bytes in LDS (mod 256 = 32)
+constexpr int kRows = 16;                          // weight rows per workgroup
+constexpr int kWavePart = kChunk / kWavesPerBlock; // blocks per wave per chunk
+constexpr int kBatch = 4;                          // MFMAs issued before their epilogues
+
+// 8 unsigned nibbles (4 bytes) -> 8 signed bytes q - 8:
 // (q + 120) ^ 0x80 per byte is q - 8 in two's complement; q + 120 <= 135
 // never carries into the next byte.
 __device__ __forceinline__ uint32_t nib_to_s8(uint32_t v) {
     return (v + 0x78787878u) ^ 0x80808080u;
 }
 
-template <int MT>   // number of 16-column activation tiles (M = 16 * MT, M = 8 uses MT = 1)
+template <int MT>
+struct Stage {                                      // one chunk's global loads, in registers
+    static constexpr int MR = 16 * MT;
+    static constexpr int WV = kRows * kChunk / kBlockThreads;           // 16-B weight pieces / thread
+    static constexpr int XV = MR * kChunk * 2 / kBlockThreads;         // 16-B activation pieces / thread
+    static constexpr int DXV = MR * kChunk / kBlockThreads;            // activation scales / thread
+    static constexpr int DWV = kRows * kChunk / kBlockThreads;         // weight scales / thread
+    uint4 w[WV];
+    uint4 x[XV];
+    uint16_t dx[DXV];
+    uint16_t dw[DWV];
+};
+
+template <int MT>
+__device__ __forceinline__ void stage_load(Stage<MT>& st, int tid, int cb, int cn, int n0, int n, int nb,
+                                           int m, int64_t k, const uint8_t* qs, const uint16_t* d,
+                                           const int8_t* xq, const uint16_t* xd) {
+    constexpr int MR = Stage<MT>::MR;
+    const int row_bytes = nb * 16;
+#pragma unroll
+    for (int i = 0; i < Stage<MT>::WV; ++i) {
+        const int e = tid + i * kBlockThreads;
+        const int row = e / kChunk, b = e % kChunk;          // a row's pieces are consecutive
+        const uint8_t* src = qs + static_cast<int64_t>(min(n0 + row, n - 1)) * row_bytes + (cb + b) * 16;
+        if (b < cn) {
+            typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+            st.w[i] = make_uint4(t.x, t.y, t.z, t.w);
+        } else {
+            st.w[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < Stage<MT>::XV; ++i) {
+        const int e = tid + i * kBlockThreads;
+        const int row = e / (2 * kChunk), piece = e % (2 * kChunk);
+        st.x[i] = (row < m && piece < 2 * cn)
+                      ? *reinterpret_cast<const uint4*>(xq + row * k + cb * 32 + piece * 16)
+                      : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < Stage<MT>::DXV; ++i) {
+        const int e = tid + i * kBlockThreads;
+        const int b = e / MR, row = e % MR;
+        st.dx[i] = (row < m && b < cn) ? xd[static_cast<int64_t>(row) * nb + cb + b] : uint16_t(0);
+    }
+#pragma unroll
+    for (int i = 0; i < Stage<MT>::DWV; ++i) {
+        const int e = tid + i * kBlockThreads;
+        const int b = e / kRows, row = e % kRows;
+        st.dw[i] = (b < cn) ? d[static_cast<int64_t>(min(n0 + row, n - 1)) * nb + cb + b] : uint16_t(0);
+    }
+}
+
+template <int MT>   // MT activation tiles of 16 rows (M = 8, 16 -> 1; M = 32 -> 2)
 __global__ __launch_bounds__(kBlockThreads)
 void tile_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d, int n, int nb,
                  int m, const int8_t* __restrict__ xq, const uint16_t* __restrict__ xd,
                  float* __restrict__ y, int32_t* __restrict__ blockdots) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int s = lane >> 4;                  // k group
-    const int c = lane & 15;                  // A row / B col / D col within tile
-    const int n0 = blockIdx.x * 16;
+    constexpr int MR = 16 * MT;
+    __shared__ __align__(16) uint8_t ws[kRows][kWPitch];
+    __shared__ __align__(16) int8_t xs[MR][kXPitch];
+    __shared__ __align__(16) float dxs[kChunk][MR];
+    __shared__ __align__(16) float dws[kChunk][kRows];
+    __shared__ __align__(16) float part[kWavesPerBlock][MT][4][kWave];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int s = lane >> 4;
+    const int c = lane & 15;
+    const int n0 = blockIdx.x * kRows;
     const int64_t k = static_cast<int64_t>(nb) * 32;
-    const int row_bytes = nb * 16;
-
-    // this wave's slice of blocks
-    const int b_begin = static_cast<int>((static_cast<int64_t>(nb) * wave) / kWavesPerBlock);
-    const int b_end = static_cast<int>((static_cast<int64_t>(nb) * (wave + 1)) / kWavesPerBlock);
-
-    const int arow = min(n0 + c, n - 1);                  // A operand row (clamped, masked later)
-    const uint8_t* arow_ptr = qs + static_cast<int64_t>(arow) * row_bytes + 8 * (s & 1);
     const int ashift = (s >> 1) * 4;
-    int drow[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) drow[v] = min(n0 + 4 * s + v, n - 1);
 
     float acc[MT][4];
 #pragma unroll
@@ -68,58 +131,107 @@ void tile_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[t][v] = 0.f;
 
-#pragma unroll 2
-    for (int b = b_begin; b < b_end; ++b) {
-        const uint2 wq = *reinterpret_cast<const uint2*>(arow_ptr + 16 * b);
-        const uint32_t a0 = nib_to_s8((wq.x >> ashift) & 0x0F0F0F0Fu);
-        const uint32_t a1 = nib_to_s8((wq.y >> ashift) & 0x0F0F0F0Fu);
-        const long a = static_cast<long>((static_cast<uint64_t>(a1) << 32) | a0);
-        float dw[4];
+    Stage<MT> st;
+    stage_load<MT>(st, tid, 0, min(kChunk, nb), n0, n, nb, m, k, qs, d, xq, xd);
+
+    for (int cb = 0; cb < nb; cb += kChunk) {
+        const int cn = min(kChunk, nb - cb);
+        // registers -> LDS
 #pragma unroll
-        for (int v = 0; v < 4; ++v) dw[v] = half_bits_to_float(d[static_cast<int64_t>(drow[v]) * nb + b]);
+        for (int i = 0; i < Stage<MT>::WV; ++i) {
+            const int e = tid + i * kBlockThreads;
+            *reinterpret_cast<uint4*>(&ws[e / kChunk][(e % kChunk) * 16]) = st.w[i];
+        }
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            const int mcol = 16 * t + c;
-            long bop = 0;
-            float dx = 0.f;
-            if (mcol < m) {
-                bop = *reinterpret_cast<const long*>(xq + static_cast<int64_t>(mcol) * k + 32 * b + 8 * s);
-                dx = half_bits_to_float(xd[static_cast<int64_t>(mcol) * nb + b]);
+        for (int i = 0; i < Stage<MT>::XV; ++i) {
+            const int e = tid + i * kBlockThreads;
+            *reinterpret_cast<uint4*>(&xs[e / (2 * kChunk)][(e % (2 * kChunk)) * 16]) = st.x[i];
+        }
+#pragma unroll
+        for (int i = 0; i < Stage<MT>::DXV; ++i) {
+            const int e = tid + i * kBlockThreads;
+            dxs[e / MR][e % MR] = half_bits_to_float(st.dx[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < Stage<MT>::DWV; ++i) {
+            const int e = tid + i * kBlockThreads;
+            dws[e / kRows][e % kRows] = half_bits_to_float(st.dw[i]);
+        }
+        __syncthreads();
+        // the next chunk's global loads fly while this chunk computes
+        if (cb + kChunk < nb)
+            stage_load<MT>(st, tid, cb + kChunk, min(kChunk, nb - cb - kChunk), n0, n, nb, m, k, qs, d, xq, xd);
+
+        // this wave's blocks of the chunk, kBatch at a time: MFMAs first,
+        // then their epilogues (the MFMA latency hides behind the batch)
+        const int b0 = wave * kWavePart;
+#pragma unroll
+        for (int jb = 0; jb < kWavePart; jb += kBatch) {
+            int32x4_t S[kBatch][MT];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int bl = b0 + jb + j;
+                const uint2 wq = *reinterpret_cast<const uint2*>(&ws[c][bl * 16 + 8 * (s & 1)]);
+                const uint32_t lo = nib_to_s8((wq.x >> ashift) & 0x0F0F0F0Fu);
+                const uint32_t hi = nib_to_s8((wq.y >> ashift) & 0x0F0F0F0Fu);
+                const long bop = static_cast<long>((static_cast<uint64_t>(hi) << 32) | lo);
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                    const long aop = *reinterpret_cast<const long*>(&xs[16 * t + c][bl * 32 + 8 * s]);
+                    const int32x4_t zero = {0, 0, 0, 0};
+                    S[j][t] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop, zero, 0, 0, 0);
+                }
             }
-            const int32x4_t zero = {0, 0, 0, 0};
-            const int32x4_t S = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bop, zero, 0, 0, 0);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(dw[v] * dx, static_cast<float>(S[v]), acc[t][v]);
-            if (blockdots != nullptr && mcol < m) {
+            for (int j = 0; j < kBatch; ++j) {
+                const int bl = b0 + jb + j;
+                if (bl < cn) {
+                    const float dw = dws[bl][c];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int row = n0 + 4 * s + v;
-                    if (row < n)
-                        blockdots[(static_cast<int64_t>(mcol) * n + row) * nb + b] = S[v];
+                    for (int t = 0; t < MT; ++t) {
+                        const float4 dx = *reinterpret_cast<const float4*>(&dxs[bl][16 * t + 4 * s]);
+                        const float dxv[4] = {dx.x, dx.y, dx.z, dx.w};
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            acc[t][v] = fmaf(dw * dxv[v], static_cast<float>(S[j][t][v]), acc[t][v]);
+                    }
+                }
+            }
+            if (blockdots != nullptr) {
+                const int col = n0 + c;
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    const int bl = b0 + jb + j;
+#pragma unroll
+                    for (int t = 0; t < MT; ++t)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int mrow = 16 * t + 4 * s + v;
+                            if (bl < cn && mrow < m && col < n)
+                                blockdots[(static_cast<int64_t>(mrow) * n + col) * nb + cb + bl] = S[j][t][v];
+                        }
                 }
             }
         }
+        __syncthreads();   // LDS is rewritten by the next chunk
     }
 
-    __shared__ float part[kWavesPerBlock][MT][4][kWave];
+    // add the four waves' partials in wave order and store
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
         for (int v = 0; v < 4; ++v) part[wave][t][v][lane] = acc[t][v];
     __syncthreads();
-    if (wave == 0) {
+    for (int e = tid; e < MT * 4 * kWave; e += kBlockThreads) {
+        const int l = e % kWave;
+        const int v = (e / kWave) % 4;
+        const int t = e / (kWave * 4);
+        float tot = part[0][t][v][l];
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            const int mcol = 16 * t + c;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                float tot = part[0][t][v][lane];
-#pragma unroll
-                for (int w = 1; w < kWavesPerBlock; ++w) tot += part[w][t][v][lane];
-                const int row = n0 + 4 * s + v;
-                if (mcol < m && row < n) y[static_cast<int64_t>(mcol) * n + row] = tot;
-            }
-        }
+        for (int w = 1; w < kWavesPerBlock; ++w) tot += part[w][t][v][l];
+        const int mrow = 16 * t + 4 * (l >> 4) + v;
+        const int col = n0 + (l & 15);
+        if (mrow < m && col < n) y[static_cast<int64_t>(mrow) * n + col] = tot;
     }
 }
 
@@ -128,7 +240,7 @@ void tile_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
 hipError_t launch_tile_q4_0(const uint8_t* qs, const uint16_t* d, int64_t n, int64_t k, int m,
                             const int8_t* xq, const uint16_t* xd, float* y, int32_t* blockdots,
                             hipStream_t stream) {
-    const int grid = static_cast<int>((n + 15) / 16);
+    const int grid = static_cast<int>((n + kRows - 1) / kRows);
     const int nb = static_cast<int>(k / 32);
     if (m <= 16)
         return launch_kernel(tile_kernel<1>, dim3(grid), dim3(kBlockThreads), stream, qs, d,
