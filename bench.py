@@ -28,8 +28,9 @@ Modes:
   python bench.py [--steps K --warmup W]    the benchmark (one JSON line)
   python bench.py --mode pmc                 vocab kernel + a calibration copy
                                              only, for rocprofv3 --pmc runs
-  python bench.py --pmc-summary DIR --counter FETCH_SIZE|WRITE_SIZE
-                                             summarise a rocprofv3 counter run
+  python bench.py --pmc-summary FETCH_DIR,WRITE_DIR [--write-profile]
+                                             HBM bytes per launch from the two
+                                             rocprofv3 counter runs
 """
 from __future__ import annotations
 
@@ -245,32 +246,65 @@ def pmc_mode(args, log):
     log("pmc pass done: 3 x %s, 3 x copy of %d bytes" % (name, COPY_BYTES))
 
 
-def pmc_summary(args):
-    """Average a counter per kernel from a rocprofv3 counter_collection.csv and
-    scale it by the same counter's reading for the calibration copy."""
-    files = glob.glob(os.path.join(args.pmc_summary, "**", "*counter_collection.csv"), recursive=True)
+def _read_counter(run_dir, counter):
+    """Per-dispatch values of one counter from a rocprofv3 counter_collection.csv."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
     if not files:
-        raise SystemExit("no counter_collection.csv under %s" % args.pmc_summary)
-    per = {}
+        raise SystemExit("no counter_collection.csv under %s" % run_dir)
+    rows = []
     for fn in files:
         with open(fn) as f:
             for row in csv.DictReader(f):
-                if row.get("Counter_Name") != args.counter:
-                    continue
-                per.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+                if row.get("Counter_Name") == counter:
+                    rows.append((row["Kernel_Name"], int(row["Grid_Size"]), float(row["Counter_Value"])))
+    return rows
+
+
+def pmc_summary(args):
+    """Turn the FETCH_SIZE and WRITE_SIZE runs of ``--mode pmc`` into HBM bytes
+    per launch of the dominant kernel. Each counter (KiB per dispatch) is
+    scaled by what it reads for the 512 MiB device copy of the same run (the
+    largest copy dispatch), so the result is in bytes."""
+    fetch_dir, write_dir = args.pmc_summary.split(",")
     out = {}
-    for k, v in per.items():
-        out[k] = sum(v) / len(v)
-    copy = [v for k, v in out.items() if "copy" in k.lower() or "elementwise" in k.lower()]
-    gq_k = [v for k, v in out.items() if "qmv_kernel" in k]
-    res = {"counter": args.counter, "per_kernel_avg": out}
-    if args.counter == "FETCH_SIZE":
-        # the copy reads COPY_BYTES: factor turns counter units into bytes
-        res["calibration_factor"] = COPY_BYTES / (max(copy) if copy else float("nan"))
-    elif args.counter == "WRITE_SIZE":
-        res["calibration_factor"] = COPY_BYTES / (max(copy) if copy else float("nan"))
-    res["qmv_kernel_avg"] = gq_k[0] if gq_k else None
-    print(json.dumps(res, indent=1))
+    for counter, run_dir in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _read_counter(run_dir, counter)
+        copies = [r for r in rows if "copy" in r[0].lower()]
+        big = max(r[1] for r in copies)
+        cal = [r[2] for r in copies if r[1] == big]
+        factor = COPY_BYTES / (1024.0 * (sum(cal) / len(cal)))
+        kern = [r[2] for r in rows if "qmv_kernel<8, 0," in r[0]]
+        out[counter] = (sum(kern) / len(kern), factor, len(kern), sum(cal) / len(cal))
+    fetch = out["FETCH_SIZE"][0] * 1024.0 * out["FETCH_SIZE"][1]
+    write = out["WRITE_SIZE"][0] * 1024.0 * out["WRITE_SIZE"][1]
+    alg = 262144 * 64 * 34 + 2048 * 4 + 262144 * 4
+    lines = [
+        "# HBM traffic of the Q8_0 vocab matvec (262144 x 2048, fp32 x), MI355X",
+        "# commands (repository root R on the GPU host; one counter per run):",
+        "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc_fetch -o run \\",
+        "#       --output-format csv -- python3 $R/bench.py --mode pmc",
+        "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/pmc_write -o run \\",
+        "#       --output-format csv -- python3 $R/bench.py --mode pmc",
+        "#   python3 bench.py --pmc-summary gpurun_out/pmc_fetch,gpurun_out/pmc_write",
+        "# calibration: the same counter on a %d-byte device copy in the same run" % COPY_BYTES,
+        "fetch_kib_per_launch_raw = %.3f" % out["FETCH_SIZE"][0],
+        "fetch_copy_kib_raw = %.3f" % out["FETCH_SIZE"][3],
+        "fetch_calibration_factor = %.5f" % out["FETCH_SIZE"][1],
+        "write_kib_per_launch_raw = %.3f" % out["WRITE_SIZE"][0],
+        "write_copy_kib_raw = %.3f" % out["WRITE_SIZE"][3],
+        "write_calibration_factor = %.5f" % out["WRITE_SIZE"][1],
+        "launches = %d" % out["FETCH_SIZE"][2],
+        "fetch_bytes_per_launch = %.0f" % fetch,
+        "write_bytes_per_launch = %.0f" % write,
+        "algorithmic_bytes_per_launch = %d" % alg,
+        "traffic_over_algorithmic = %.4f" % ((fetch + write) / alg),
+        "kernel_source_hash = %s" % kernel_source_hash(),
+    ]
+    text = "\n".join(lines) + "\n"
+    print(text)
+    if args.write_profile:
+        with open(TRAFFIC_FILE, "w") as f:
+            f.write(text)
 
 
 # ----------------------------------------------------------------------------
@@ -306,7 +340,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=["bench", "pmc"], default="bench")
     ap.add_argument("--pmc-summary", default=None)
-    ap.add_argument("--counter", default="FETCH_SIZE")
+    ap.add_argument("--write-profile", action="store_true",
+                    help="with --pmc-summary: write the summary under profiles/")
     args = ap.parse_args()
 
     def log(msg):
