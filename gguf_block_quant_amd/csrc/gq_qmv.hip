@@ -23,14 +23,11 @@
 #include "gq_device.hpp"
 #include "gq_launch.hpp"
 
-#ifndef GQ_QMV_ROWS
-#define GQ_QMV_ROWS 4          // rows per wave step
-#endif
 #ifndef GQ_QMV_MAX_GRID
 #define GQ_QMV_MAX_GRID 1024   // workgroups of 4 waves (4 per CU on 256 CUs)
 #endif
-#ifndef GQ_QMV_PIPE
-#define GQ_QMV_PIPE 0          // prefetch the next row group's quants
+#ifndef GQ_QMV_CARRY
+#define GQ_QMV_CARRY 1         // issue the next row group's loads before this one's reduction
 #endif
 #ifndef GQ_QMV_NT
 #define GQ_QMV_NT 1            // non-temporal loads for the quant stream (read once)
@@ -78,17 +75,33 @@ __device__ __forceinline__ float unit_dot_f32(const uint4 q, const float* xr) {
             for (int b = 0; b < 4; ++b)
                 p = fmaf(static_cast<float>(static_cast<int8_t>(w[j] >> (8 * b))), xr[4 * j + b], p);
     } else {
-        // nibble ^ 8 read as a 4-bit two's-complement number is nibble - 8.
+        // Two nibbles at bits 0..3 and 16..19, OR-ed under the binary16
+        // exponent of 1024 (0x6400), are the half2 (1024 + q_a, 1024 + q_b);
+        // one packed fp16 add of -1032 leaves q - 8 exactly, and
+        // v_fma_mix_f32 multiplies that half by the fp32 activation with a
+        // single rounding -- the same value as an fp32 FMA on (float)(q - 8).
+        typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+        const half2_t off = {static_cast<_Float16>(-1032.0f), static_cast<_Float16>(-1032.0f)};
+        // keep the exponent pattern in a VGPR: gfx9 VOP3 takes no literal, and
+        // with one register operand the mask-and-or is a single v_and_or_b32
+        uint32_t magic = 0x64006400u;
+        asm volatile("" : "+v"(magic));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint32_t v = w[j] ^ 0x88888888u;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const float lo = static_cast<float>(static_cast<int32_t>(v << (28 - 8 * b)) >> 28);
-                const float hi = static_cast<float>(static_cast<int32_t>(v << (24 - 8 * b)) >> 28);
-                p = fmaf(lo, xr[4 * j + b], p);        // element 4j+b
-                p = fmaf(hi, xr[16 + 4 * j + b], p);   // element 16+4j+b
-            }
+            const uint32_t v = w[j];
+            const half2_t lo02 = __builtin_bit_cast(half2_t, (v & 0x000F000Fu) | magic) + off;
+            const half2_t lo13 = __builtin_bit_cast(half2_t, ((v >> 8) & 0x000F000Fu) | magic) + off;
+            const half2_t hi02 = __builtin_bit_cast(half2_t, ((v >> 4) & 0x000F000Fu) | magic) + off;
+            const half2_t hi13 = __builtin_bit_cast(half2_t, ((v >> 12) & 0x000F000Fu) | magic) + off;
+            // element order: 4j+b (low nibble of byte b), then 16+4j+b (its high nibble)
+            p = fmaf(static_cast<float>(lo02.x), xr[4 * j + 0], p);
+            p = fmaf(static_cast<float>(hi02.x), xr[16 + 4 * j + 0], p);
+            p = fmaf(static_cast<float>(lo13.x), xr[4 * j + 1], p);
+            p = fmaf(static_cast<float>(hi13.x), xr[16 + 4 * j + 1], p);
+            p = fmaf(static_cast<float>(lo02.y), xr[4 * j + 2], p);
+            p = fmaf(static_cast<float>(hi02.y), xr[16 + 4 * j + 2], p);
+            p = fmaf(static_cast<float>(lo13.y), xr[4 * j + 3], p);
+            p = fmaf(static_cast<float>(hi13.y), xr[16 + 4 * j + 3], p);
         }
     }
     return p;
@@ -174,9 +187,15 @@ void qmv_kernel(const QmvParams p) {
     __shared__ float part[WAVES][NMAT][R];
 
     // Quant chunks and scales of one row group, for every unit of the lane.
-    uint4 q[2][NI][NMAT][R];
-    uint16_t db[2][NI][NMAT][R];
-    auto load_group = [&](int buf, int r0) {
+    // Lanes past the end of a short row load a clamped (valid) unit and
+    // contribute nothing: their activations are zero and their scale is
+    // masked to zero below, so no load sits behind a divergent branch.
+    uint32_t uload[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) uload[i] = static_cast<uint32_t>(min(unit[i], p.units - 1));
+    uint4 q[NI][NMAT][R];
+    uint16_t db[NI][NMAT][R];
+    auto load_group = [&](int r0) {
 #pragma unroll
         for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -185,35 +204,32 @@ void qmv_kernel(const QmvParams p) {
                 const uint16_t* dm = (m == 0) ? p.d : p.d2;
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const int row = min(r0 + r, p.n - 1);   // rows past n: in-bounds, discarded
-                    if (uvalid[i]) {
-                        const uint4* src = reinterpret_cast<const uint4*>(
-                            qsm + static_cast<int64_t>(row) * row_bytes + unit[i] * 16);
+                    // rows past n re-read row n-1 (in bounds); their results are discarded
+                    const uint32_t row = static_cast<uint32_t>(min(r0 + r, p.n - 1));
+                    const uint8_t* src = qsm + static_cast<uint64_t>(row) * static_cast<uint32_t>(row_bytes) +
+                                         uload[i] * 16u;
 #if GQ_QMV_NT
-                        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-                        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
-                        q[buf][i][m][r] = make_uint4(t.x, t.y, t.z, t.w);
+                    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+                    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+                    q[i][m][r] = make_uint4(t.x, t.y, t.z, t.w);
 #else
-                        q[buf][i][m][r] = *src;
+                    q[i][m][r] = *reinterpret_cast<const uint4*>(src);
 #endif
-                        db[buf][i][m][r] = dm[static_cast<int64_t>(row) * p.nb + (unit[i] >> SH)];
-                    } else {
-                        q[buf][i][m][r] = make_uint4(0u, 0u, 0u, 0u);
-                        db[buf][i][m][r] = 0;
-                    }
+                    db[i][m][r] = dm[static_cast<uint64_t>(row) * static_cast<uint32_t>(p.nb) + (uload[i] >> SH)];
                 }
             }
     };
 
     int it = blockIdx.x;
-    if (it * SUBS < p.row_groups) load_group(0, (it * SUBS + sub) * R);
+#if GQ_QMV_CARRY
+    if (it * SUBS < p.row_groups) load_group((it * SUBS + sub) * R);
+#endif
     for (; it * SUBS < p.row_groups; it += gridDim.x) {
         const int g = it * SUBS + sub;
         const int r0 = g * R;
         const int itn = it + gridDim.x;
-#if GQ_QMV_PIPE
-        // issue the next row group's loads before computing this one
-        if (itn * SUBS < p.row_groups) load_group(1, (itn * SUBS + sub) * R);
+#if !GQ_QMV_CARRY
+        load_group(r0);
 #endif
         float acc[NMAT][R];
 #pragma unroll
@@ -227,11 +243,11 @@ void qmv_kernel(const QmvParams p) {
             for (int m = 0; m < NMAT; ++m)
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const float dw = half_bits_to_float(db[0][i][m][r]);
+                    const float dw = uvalid[i] ? half_bits_to_float(db[i][m][r]) : 0.f;
                     if constexpr (MODE != kQ8X) {
-                        acc[m][r] = fmaf(dw, unit_dot_f32<TYPE>(q[0][i][m][r], xr[i]), acc[m][r]);
+                        acc[m][r] = fmaf(dw, unit_dot_f32<TYPE>(q[i][m][r], xr[i]), acc[m][r]);
                     } else {
-                        int s = unit_dot_q8<TYPE>(q[0][i][m][r], xqr[i], sxr[i]);
+                        int s = unit_dot_q8<TYPE>(q[i][m][r], xqr[i], sxr[i]);
                         if constexpr (TYPE == kTypeQ8_0) {
                             // a block is two adjacent lanes' units: S_b = s(2t) + s(2t+1)
                             s += dpp_i32<kDppQuadSwap1>(s);
@@ -245,18 +261,9 @@ void qmv_kernel(const QmvParams p) {
                     }
                 }
         }
-#if GQ_QMV_PIPE
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    q[0][i][m][r] = q[1][i][m][r];
-                    db[0][i][m][r] = db[1][i][m][r];
-                }
-#else
-        if (itn * SUBS < p.row_groups) load_group(0, (itn * SUBS + sub) * R);
+#if GQ_QMV_CARRY
+        // the next row group's loads fly during the reduction and stores
+        if (itn * SUBS < p.row_groups) load_group((itn * SUBS + sub) * R);
 #endif
 
         // ---- cross-lane and cross-wave reduction ---------------------------
@@ -314,18 +321,31 @@ void qmv_kernel(const QmvParams p) {
 
 namespace {
 
-constexpr int kRows = GQ_QMV_ROWS;
 constexpr int kMaxGrid = GQ_QMV_MAX_GRID;
 
-template <int TYPE, int MODE, int NI, int WS>
-hipError_t launch_cfg(QmvParams p, hipStream_t stream) {
+template <int TYPE, int MODE, int NI, int WS, int R>
+hipError_t launch_rows(QmvParams p, hipStream_t stream) {
     constexpr int WAVES = Waves<WS>::value;
     constexpr int SUBS = WAVES / WS;
-    p.row_groups = (p.n + kRows - 1) / kRows;
+    p.row_groups = (p.n + R - 1) / R;
     const int64_t iters = (static_cast<int64_t>(p.row_groups) + SUBS - 1) / SUBS;
     const int64_t max_grid = kMaxGrid * 4 / WAVES;
     const int grid = static_cast<int>(iters < max_grid ? iters : max_grid);
-    return launch_kernel(qmv_kernel<TYPE, MODE, NI, WS, kRows>, dim3(grid), dim3(WAVES * kWave), stream, p);
+    return launch_kernel(qmv_kernel<TYPE, MODE, NI, WS, R>, dim3(grid), dim3(WAVES * kWave), stream, p);
+}
+
+// Rows per wave step (measured on MI355X): rows split over >= 4 waves
+// stream 8 rows at a time to keep enough bytes in flight per wave; very tall
+// matrices take 4 (each wave loops over many groups); shorter ones take 2
+// so more waves share the dequantisation work.
+template <int TYPE, int MODE, int NI, int WS>
+hipError_t launch_cfg(QmvParams p, hipStream_t stream) {
+    if constexpr (WS >= 4) {
+        return launch_rows<TYPE, MODE, NI, WS, 8>(p, stream);
+    } else {
+        if (p.n >= 65536) return launch_rows<TYPE, MODE, NI, WS, 4>(p, stream);
+        return launch_rows<TYPE, MODE, NI, WS, 2>(p, stream);
+    }
 }
 
 // units per lane needed when the row is split over ws waves
