@@ -281,11 +281,11 @@ def pmc_summary(args):
     lines = [
         "# HBM traffic of the Q8_0 vocab matvec (262144 x 2048, fp32 x), MI355X",
         "# commands (repository root R on the GPU host; one counter per run):",
-        "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc_fetch -o run \\",
+        "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -d $R/%s -o run \\" % fetch_dir,
         "#       --output-format csv -- python3 $R/bench.py --mode pmc",
-        "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/pmc_write -o run \\",
+        "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -d $R/%s -o run \\" % write_dir,
         "#       --output-format csv -- python3 $R/bench.py --mode pmc",
-        "#   python3 bench.py --pmc-summary gpurun_out/pmc_fetch,gpurun_out/pmc_write",
+        "#   python3 bench.py --pmc-summary %s,%s --write-profile" % (fetch_dir, write_dir),
         "# calibration: the same counter on a %d-byte device copy in the same run" % COPY_BYTES,
         "fetch_kib_per_launch_raw = %.3f" % out["FETCH_SIZE"][0],
         "fetch_copy_kib_raw = %.3f" % out["FETCH_SIZE"][3],
