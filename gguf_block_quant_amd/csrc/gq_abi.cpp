@@ -204,7 +204,7 @@ int gq_qmm_tile_m(const uint8_t* qs, const uint16_t* d, int64_t n, int64_t k, in
     if (qs == nullptr || d == nullptr || xq == nullptr || xd == nullptr || y == nullptr) return GQ_ERR_NULL;
     int st = check_shape(n, k);
     if (st != GQ_OK) return st;
-    if (m != 8 && m != 16 && m != 32) return GQ_ERR_UNSUPPORTED;
+    if (m < 1 || m > 32) return GQ_ERR_UNSUPPORTED;
     if (k > kMaxK) return GQ_ERR_UNSUPPORTED;
     if (!aligned(qs, 16) || !aligned(d, 2) || !aligned(xq, 16) || !aligned(xd, 2) || !aligned(y, 4) ||
         !aligned(blockdots, 4))

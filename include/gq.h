@@ -172,11 +172,15 @@ int gq_qffn_gate_up_gelu(const uint8_t *g_qs, const uint16_t *g_d,
                          void *stream);
 
 /*
- * gq_qmm_tile_m -- small-M prefill tile, Q4_0 weights [n][k] against m
- * Q8_0 activation rows (xq int8 [m][k], xd binary16 bits [m][k/32]):
+ * gq_qmm_tile_m -- small-M tile, Q4_0 weights [n][k] against m Q8_0
+ * activation rows (xq int8 [m][k], xd binary16 bits [m][k/32]):
  * S[mi][r][b] exact in int32, y[mi][r] = sum_b dw[r][b] dx[mi][b] S (fp32),
  * y fp32 [m][n]. blockdots, if not NULL, receives S as int32 [m][n][k/32].
- * m must be 8, 16 or 32 (else GQ_ERR_UNSUPPORTED). Maximum k: 8192.
+ * m = 8, 16, 32 are the prefill tiles (raw-Metal port page, "Batched
+ * prefill"; Gem native architecture page, prefill tile of up to 32 rows);
+ * any 1 <= m <= 32 is accepted, which also covers batched decode of m
+ * sequences that share every weight read (TensorSharp Gemma 4 page, batched
+ * fused decode). m outside [1, 32] gives GQ_ERR_UNSUPPORTED. Maximum k: 32768.
  */
 int gq_qmm_tile_m(const uint8_t *qs, const uint16_t *d, int64_t n, int64_t k, int m,
                   const int8_t *xq, const uint16_t *xd, float *y,

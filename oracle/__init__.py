@@ -57,8 +57,13 @@ def lib():
         L.or_gelu_tanh.argtypes = [ctypes.c_double]
         L.or_gelu_tanh.restype = ctypes.c_double
         L.or_ffn_gate_up.argtypes = [ctypes.c_int, P, P, I64, I64, P, P, P, P, P, P]
+        L.or_rmsnorm.argtypes = [P, I64, P, ctypes.c_double, P]
+        L.or_softcap.argtypes = [ctypes.c_double, ctypes.c_double]
+        L.or_softcap.restype = ctypes.c_double
+        L.or_argmax_f32.argtypes = [P, I64]
+        L.or_argmax_f32.restype = I64
         for f in ("or_dequantize", "or_matvec", "or_matvec_rows", "or_quantize_q8_0",
-                  "or_blockdots", "or_ffn_gate_up"):
+                  "or_blockdots", "or_ffn_gate_up", "or_rmsnorm"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -164,6 +169,26 @@ def ffn_gate_up(qtype, gblocks, ublocks, n_ff, k, x):
                                 n_ff, k, _p(xd), _p(out["g"]), _p(out["u"]), _p(out["h"]),
                                 _p(out["ag"]), _p(out["au"])), "ffn_gate_up")
     return out
+
+
+def rmsnorm(x, w=None, eps=1e-6):
+    """x * (mean(x^2) + eps)^-1/2 * w in fp64 (w None: no scale)."""
+    xd = np.ascontiguousarray(np.asarray(x, dtype=np.float64).reshape(-1))
+    wd = None if w is None else np.ascontiguousarray(np.asarray(w, dtype=np.float64).reshape(-1))
+    out = np.empty_like(xd)
+    _check(lib().or_rmsnorm(_p(xd), xd.size, _p(wd), float(eps), _p(out)), "rmsnorm")
+    return out
+
+
+def softcap(y, cap):
+    f = lib().or_softcap
+    y = np.asarray(y, dtype=np.float64).reshape(-1)
+    return np.array([f(float(v), float(cap)) for v in y], dtype=np.float64)
+
+
+def argmax_f32(v):
+    v = np.ascontiguousarray(np.asarray(v, dtype=np.float32).reshape(-1))
+    return int(lib().or_argmax_f32(_p(v), v.size))
 
 
 # Tolerances stated by the method's accuracy contract.

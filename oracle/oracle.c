@@ -295,3 +295,40 @@ int or_matvec_rows(int type, const uint8_t *blocks, int64_t n, int64_t k,
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* RMSNorm (SafeC Gemma 4 DESIGN_NOTES page, "RMSNorm"): out_i = x_i *        */
+/* (mean_j x_j^2 + eps)^(-1/2) * w_i, the weight applied directly (no +1);    */
+/* w == NULL means w_i = 1. Gemma 4 uses eps = 1e-6 ("Hyperparameters").      */
+/* ------------------------------------------------------------------------ */
+int or_rmsnorm(const double *x, int64_t k, const double *w, double eps, double *out)
+{
+    if (k <= 0) return 1;
+    double ss = 0.0;
+    for (int64_t i = 0; i < k; ++i)
+        ss += x[i] * x[i];
+    double inv = 1.0 / sqrt(ss / (double)k + eps);
+    for (int64_t i = 0; i < k; ++i)
+        out[i] = x[i] * inv * (w ? w[i] : 1.0);
+    return 0;
+}
+
+/* Final-logit soft cap (SafeC DESIGN_NOTES page, "LM head"):                 */
+/* cap * tanh(y / cap) for cap > 0; y unchanged for cap == 0.                 */
+double or_softcap(double y, double cap)
+{
+    return cap > 0.0 ? cap * tanh(y / cap) : y;
+}
+
+/* Greedy argmax over fp32 values: the largest value wins, ties go to the     */
+/* lowest index, NaN ranks below every number (so it wins only if all are     */
+/* NaN, and then index 0). Returns the index; n >= 1.                         */
+int64_t or_argmax_f32(const float *v, int64_t n)
+{
+    int64_t best = 0;
+    for (int64_t i = 1; i < n; ++i) {
+        if (isnan(v[i])) continue;
+        if (isnan(v[best]) || v[i] > v[best]) best = i;
+    }
+    return best;
+}

@@ -107,8 +107,9 @@ def test_ffn_validation():
 
 def test_tile_validation():
     f = L.gq_qmm_tile_m
-    assert f(A, B, 64, 256, 12, C, E, D, None, None) == UNSUP
-    assert f(A, B, 64, 256, 4, C, E, D, None, None) == UNSUP
+    assert f(A, B, 64, 256, 0, C, E, D, None, None) == UNSUP
+    assert f(A, B, 64, 256, 33, C, E, D, None, None) == UNSUP
+    assert f(A, B, 64, 256, -8, C, E, D, None, None) == UNSUP
     assert f(A, B, 64, 256, 16, C, None, D, None, None) == NULL
     assert f(A, B, 64, 0, 16, C, E, D, None, None) == SHAPE
     assert f(A, B, 64, 256, 16, C + 1, E, D, None, None) == ALIGN

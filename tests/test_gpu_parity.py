@@ -318,7 +318,9 @@ def test_tile_workload(m):
     check_within(y1, yr[m - 1], oracle.fp32_path_bound(ar[m - 1]), "m=1 path on last row")
 
 
-@pytest.mark.parametrize("m,n,k", [(8, 1000, 96), (16, 17, 32), (32, 100, 1056), (32, 64, 8192)])
+@pytest.mark.parametrize("m,n,k", [(8, 1000, 96), (16, 17, 32), (32, 100, 1056), (32, 64, 8192),
+                                   (1, 300, 2048), (2, 513, 512), (3, 64, 96), (5, 129, 1024),
+                                   (7, 2048, 2048), (12, 80, 256), (20, 48, 320), (31, 33, 4096)])
 def test_tile_ragged(m, n, k):
     rng = np.random.default_rng(m * n + k)
     w = synth.q4_0_weights(rng, n, k)
@@ -356,6 +358,6 @@ def test_binding_rejects_misaligned_and_host_tensors():
     with pytest.raises(ValueError):
         gq.qmv_q8_0(qs, d, n, k, torch.zeros(k))
     with pytest.raises(gq.GQError) as e:
-        gq.qmm_tile_m(qs, d, n, k, 12, torch.zeros((12, k), dtype=torch.int8, device="cuda"),
-                      torch.zeros((12, k // 32), dtype=torch.int16, device="cuda"))
+        gq.qmm_tile_m(qs, d, n, k, 33, torch.zeros((33, k), dtype=torch.int8, device="cuda"),
+                      torch.zeros((33, k // 32), dtype=torch.int16, device="cuda"))
     assert e.value.status == 5

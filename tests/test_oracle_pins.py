@@ -490,3 +490,59 @@ def test_ffn_gate_up_one_hot_rows():
     assert np.array_equal(out["g"], gvals) and np.array_equal(out["u"], uvals)
     ref = torch.nn.functional.gelu(torch.tensor(gvals, dtype=torch.float64), approximate="tanh").numpy()
     assert np.allclose(out["h"], ref * np.array(uvals), rtol=1e-14, atol=0)
+
+
+# ----------------------------------------------------------------------------
+# RMSNorm prologue, soft cap and argmax epilogue
+# ----------------------------------------------------------------------------
+
+def test_rmsnorm_against_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(21)
+    for k in (32, 2048, 8192):
+        x = rng.standard_normal(k) * 3.0
+        w = rng.uniform(0.5, 1.5, k)
+        got = oracle.rmsnorm(x, w, 1e-6)
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (k,), torch.from_numpy(w), eps=1e-6).numpy()
+        assert np.allclose(got, ref, rtol=1e-14, atol=0)
+
+
+def test_rmsnorm_closed_forms():
+    # constant input c: every output is c / sqrt(c^2 + eps) (times w)
+    for c in (1.0, -2.5, 1e-4):
+        got = oracle.rmsnorm(np.full(64, c), None, 1e-6)
+        assert np.allclose(got, c / math.sqrt(c * c + 1e-6), rtol=1e-15)
+    # eps = 0: the output has mean square exactly 1 and is scale invariant
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal(256)
+    a = oracle.rmsnorm(x, None, 0.0)
+    b = oracle.rmsnorm(8.0 * x, None, 0.0)
+    assert abs(np.mean(a * a) - 1.0) < 1e-14 and np.allclose(a, b, rtol=1e-15)
+    # the weight multiplies directly (no 1 + w)
+    w = np.zeros(256)
+    w[3] = 2.0
+    c = oracle.rmsnorm(x, w, 0.0)
+    assert np.count_nonzero(c) == 1 and c[3] == pytest.approx(2.0 * a[3], rel=1e-15)
+
+
+def test_softcap_values():
+    y = np.array([0.0, 1e-3, -1e-3, 15.0, -45.0, 1e6, -1e6, 30.0])
+    got = oracle.softcap(y, 30.0)
+    assert np.allclose(got, 30.0 * np.tanh(y / 30.0), rtol=1e-15, atol=0)
+    assert got[5] == 30.0 and got[6] == -30.0                 # saturates, no NaN
+    assert np.allclose(oracle.softcap(y, 0.0), y)             # cap 0: identity
+    assert np.all(np.diff(oracle.softcap(np.linspace(-100, 100, 1001), 30.0)) >= 0)   # monotone
+
+
+def test_argmax_rules_brute_force():
+    rng = np.random.default_rng(23)
+    for _ in range(200):
+        v = rng.integers(-3, 4, size=rng.integers(1, 40)).astype(np.float32)   # many ties
+        best = max(range(v.size), key=lambda i: (v[i], -i))
+        assert oracle.argmax_f32(v) == best
+    v = np.array([np.nan, 1.0, 3.0, np.nan, 3.0], np.float32)
+    assert oracle.argmax_f32(v) == 2                          # NaN skipped, tie -> lowest
+    assert oracle.argmax_f32(np.array([np.nan, np.nan], np.float32)) == 0
+    assert oracle.argmax_f32(np.array([-np.inf, -1e30, np.inf], np.float32)) == 2
+    big = rng.standard_normal(262144).astype(np.float32)
+    assert oracle.argmax_f32(big) == int(np.argmax(big))
