@@ -27,11 +27,12 @@ TYPE_Q8_0 = 8
 
 GQ_OK = 0
 STATUS_NAMES = {0: "GQ_OK", 1: "GQ_ERR_NULL", 2: "GQ_ERR_SHAPE", 3: "GQ_ERR_ALIGN",
-                4: "GQ_ERR_ALIAS", 5: "GQ_ERR_UNSUPPORTED", 6: "GQ_ERR_LAUNCH"}
+                4: "GQ_ERR_ALIAS", 5: "GQ_ERR_UNSUPPORTED", 6: "GQ_ERR_LAUNCH", 7: "GQ_ERR_VALUE"}
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I = ctypes.c_int
+_F = ctypes.c_float
 
 _SIGS = {
     "gq_abi_version": ([], _I),
@@ -47,6 +48,12 @@ _SIGS = {
     "gq_qmv_q8_0_q8": ([_P, _P, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "gq_qmv_q4_0_q8": ([_P, _P, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "gq_qffn_gate_up_gelu": ([_P, _P, _P, _P, _I64, _I64, _P, _P, _P], _I),
+    "gq_qffn_gate_up_gelu_ex": ([_P, _P, _P, _P, _I64, _I64, _P, _P, _F, _P, _P], _I),
+    "gq_qmv_q8_0_ex": ([_P, _P, _I64, _I64, _P, _P, _F, _P, _P, _P], _I),
+    "gq_qmv_q4_0_ex": ([_P, _P, _I64, _I64, _P, _P, _F, _P, _P, _P], _I),
+    "gq_argmax_workspace_bytes": ([], ctypes.c_size_t),
+    "gq_qmv_q8_0_argmax": ([_P, _P, _I64, _I64, _P, _P, _F, _F, _P, _P, ctypes.c_size_t, _P, _P, _P], _I),
+    "gq_qmv_q4_0_argmax": ([_P, _P, _I64, _I64, _P, _P, _F, _F, _P, _P, ctypes.c_size_t, _P, _P, _P], _I),
     "gq_qmm_tile_m": ([_P, _P, _I64, _I64, _I, _P, _P, _P, _P, _P], _I),
 }
 _handle = None
@@ -201,6 +208,66 @@ def qmv_q8_0_q8(qs, d, n, k, xq, xd, y=None, blockdots=None, stream=None):
 
 def qmv_q4_0_q8(qs, d, n, k, xq, xd, y=None, blockdots=None, stream=None):
     return _qmv_q8("gq_qmv_q4_0_q8", qs, d, n, k, xq, xd, y, blockdots, stream)
+
+
+def qmv_q8_0_ex(qs, d, n, k, x, norm_weight=None, norm_eps=1e-6, residual=None, y=None, stream=None):
+    return _qmv_ex("gq_qmv_q8_0_ex", qs, d, n, k, x, norm_weight, norm_eps, residual, y, stream)
+
+
+def qmv_q4_0_ex(qs, d, n, k, x, norm_weight=None, norm_eps=1e-6, residual=None, y=None, stream=None):
+    return _qmv_ex("gq_qmv_q4_0_ex", qs, d, n, k, x, norm_weight, norm_eps, residual, y, stream)
+
+
+def _qmv_ex(fn, qs, d, n, k, x, norm_weight, norm_eps, residual, y, stream):
+    torch = _torch()
+    if y is None:
+        y = _like(x, (n,), torch.float32)
+    _call(fn, _ptr(qs, "qs"), _ptr(d, "d"), n, k, _ptr(x, "x"), _ptr(norm_weight, "norm_weight"),
+          float(norm_eps), _ptr(residual, "residual"), _ptr(y, "y"), _stream(stream))
+    return y
+
+
+def argmax_workspace_bytes() -> int:
+    return raw().gq_argmax_workspace_bytes()
+
+
+def _qmv_argmax(fn, qs, d, n, k, x, norm_weight, norm_eps, softcap, logits, workspace, stream):
+    torch = _torch()
+    if logits is None:
+        logits = _like(x, (n,), torch.float32)
+    if workspace is None:
+        workspace = _like(x, (argmax_workspace_bytes(),), torch.uint8)
+    index = _like(x, (1,), torch.int32)
+    value = _like(x, (1,), torch.float32)
+    _call(fn, _ptr(qs, "qs"), _ptr(d, "d"), n, k, _ptr(x, "x"), _ptr(norm_weight, "norm_weight"),
+          float(norm_eps), float(softcap), _ptr(logits, "logits"), _ptr(workspace, "workspace"),
+          workspace.numel() * workspace.element_size(), _ptr(index, "index"), _ptr(value, "value"),
+          _stream(stream))
+    return index, value, logits
+
+
+def qmv_q8_0_argmax(qs, d, n, k, x, norm_weight=None, norm_eps=1e-6, softcap=30.0, logits=None,
+                    workspace=None, stream=None):
+    """Vocabulary head: returns (index int32[1], value fp32[1], logits fp32[n])."""
+    return _qmv_argmax("gq_qmv_q8_0_argmax", qs, d, n, k, x, norm_weight, norm_eps, softcap, logits,
+                       workspace, stream)
+
+
+def qmv_q4_0_argmax(qs, d, n, k, x, norm_weight=None, norm_eps=1e-6, softcap=30.0, logits=None,
+                    workspace=None, stream=None):
+    return _qmv_argmax("gq_qmv_q4_0_argmax", qs, d, n, k, x, norm_weight, norm_eps, softcap, logits,
+                       workspace, stream)
+
+
+def qffn_gate_up_gelu_ex(g_qs, g_d, u_qs, u_d, n_ff, k, x, norm_weight=None, norm_eps=1e-6, h=None,
+                         stream=None):
+    torch = _torch()
+    if h is None:
+        h = _like(x, (n_ff,), torch.float32)
+    _call("gq_qffn_gate_up_gelu_ex", _ptr(g_qs, "g_qs"), _ptr(g_d, "g_d"), _ptr(u_qs, "u_qs"),
+          _ptr(u_d, "u_d"), n_ff, k, _ptr(x, "x"), _ptr(norm_weight, "norm_weight"), float(norm_eps),
+          _ptr(h, "h"), _stream(stream))
+    return h
 
 
 def qffn_gate_up_gelu(g_qs, g_d, u_qs, u_d, n_ff, k, x, h=None, stream=None):

@@ -72,16 +72,53 @@ int check_weights(int type, const void* qs, const uint16_t* d, int64_t n, int64_
     return GQ_OK;
 }
 
+// Shared checks of the optional prologue / epilogue arguments.
+int check_fold(const float* norm_w, float norm_eps, const float* residual) {
+    if (norm_w != nullptr && (!aligned(norm_w, 16) || !(norm_eps >= 0.0f) || !(norm_eps < 1e30f)))
+        return norm_w != nullptr && !aligned(norm_w, 16) ? GQ_ERR_ALIGN : GQ_ERR_VALUE;
+    if (residual != nullptr && !aligned(residual, 4)) return GQ_ERR_ALIGN;
+    return GQ_OK;
+}
+
 int qmv_f32(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k, const float* x,
-            float* y, void* stream) {
+            const float* norm_w, float norm_eps, const float* residual, float* y, void* stream) {
     if (x == nullptr || y == nullptr) return GQ_ERR_NULL;
     int st = check_weights(type, qs, d, n, k);
     if (st != GQ_OK) return st;
     if (!aligned(x, 16) || !aligned(y, 4)) return GQ_ERR_ALIGN;
-    const Range outs[] = {{y, static_cast<size_t>(n) * 4}};
-    const Range ins[] = {{qs, qs_bytes(type, n, k)}, {d, d_bytes(n, k)}, {x, static_cast<size_t>(k) * 4}};
+    st = check_fold(norm_w, norm_eps, residual);
+    if (st != GQ_OK) return st;
+    const size_t nb4 = static_cast<size_t>(n) * 4;
+    const Range outs[] = {{y, nb4}};
+    // y may be the residual itself (in-place accumulate), but no other overlap
+    const Range ins[] = {{qs, qs_bytes(type, n, k)}, {d, d_bytes(n, k)}, {x, static_cast<size_t>(k) * 4},
+                         {norm_w, norm_w ? static_cast<size_t>(k) * 4 : 0},
+                         {residual, (residual && residual != y) ? nb4 : 0}};
     if (any_alias(outs, ins)) return GQ_ERR_ALIAS;
-    return status_of(gq::launch_qmv_f32(type, qs, d, n, k, x, y, as_stream(stream)));
+    return status_of(gq::launch_qmv_f32(type, qs, d, n, k, x, norm_w, norm_eps, residual, y,
+                                        as_stream(stream)));
+}
+
+int qmv_argmax(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k, const float* x,
+               const float* norm_w, float norm_eps, float softcap, float* logits, void* workspace,
+               size_t workspace_bytes, int32_t* index, float* value, void* stream) {
+    if (x == nullptr || logits == nullptr || workspace == nullptr || index == nullptr || value == nullptr)
+        return GQ_ERR_NULL;
+    int st = check_weights(type, qs, d, n, k);
+    if (st != GQ_OK) return st;
+    if (!aligned(x, 16) || !aligned(logits, 4) || !aligned(workspace, 8) || !aligned(index, 4) ||
+        !aligned(value, 4))
+        return GQ_ERR_ALIGN;
+    st = check_fold(norm_w, norm_eps, nullptr);
+    if (st != GQ_OK) return st;
+    if (!(softcap >= 0.0f) || !(softcap < 1e30f) || workspace_bytes < gq::kArgmaxWorkspaceBytes) return GQ_ERR_VALUE;
+    const Range outs[] = {{logits, static_cast<size_t>(n) * 4}, {workspace, gq::kArgmaxWorkspaceBytes},
+                          {index, 4}, {value, 4}};
+    const Range ins[] = {{qs, qs_bytes(type, n, k)}, {d, d_bytes(n, k)}, {x, static_cast<size_t>(k) * 4},
+                         {norm_w, norm_w ? static_cast<size_t>(k) * 4 : 0}};
+    if (any_alias(outs, ins)) return GQ_ERR_ALIAS;
+    return status_of(gq::launch_qmv_argmax(type, qs, d, n, k, x, norm_w, norm_eps, softcap, logits, workspace,
+                                           index, value, as_stream(stream)));
 }
 
 int qmv_q8(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k, const int8_t* xq,
@@ -115,6 +152,7 @@ const char* gq_status_str(int status) {
         case GQ_ERR_ALIAS: return "an output overlaps an input";
         case GQ_ERR_UNSUPPORTED: return "unsupported type, k, n or m";
         case GQ_ERR_LAUNCH: return "kernel launch failed";
+        case GQ_ERR_VALUE: return "invalid scalar argument (eps, soft cap) or workspace too small";
         default: return "unknown status";
     }
 }
@@ -162,12 +200,38 @@ int gq_quantize_q8_0(const float* x, int64_t m, int64_t k, int8_t* xq, uint16_t*
 
 int gq_qmv_q8_0(const int8_t* qs, const uint16_t* d, int64_t n, int64_t k, const float* x, float* y,
                 void* stream) {
-    return qmv_f32(GQ_TYPE_Q8_0, qs, d, n, k, x, y, stream);
+    return qmv_f32(GQ_TYPE_Q8_0, qs, d, n, k, x, nullptr, 0.0f, nullptr, y, stream);
 }
 
 int gq_qmv_q4_0(const uint8_t* qs, const uint16_t* d, int64_t n, int64_t k, const float* x, float* y,
                 void* stream) {
-    return qmv_f32(GQ_TYPE_Q4_0, qs, d, n, k, x, y, stream);
+    return qmv_f32(GQ_TYPE_Q4_0, qs, d, n, k, x, nullptr, 0.0f, nullptr, y, stream);
+}
+
+int gq_qmv_q8_0_ex(const int8_t* qs, const uint16_t* d, int64_t n, int64_t k, const float* x,
+                   const float* norm_weight, float norm_eps, const float* residual, float* y, void* stream) {
+    return qmv_f32(GQ_TYPE_Q8_0, qs, d, n, k, x, norm_weight, norm_eps, residual, y, stream);
+}
+
+int gq_qmv_q4_0_ex(const uint8_t* qs, const uint16_t* d, int64_t n, int64_t k, const float* x,
+                   const float* norm_weight, float norm_eps, const float* residual, float* y, void* stream) {
+    return qmv_f32(GQ_TYPE_Q4_0, qs, d, n, k, x, norm_weight, norm_eps, residual, y, stream);
+}
+
+size_t gq_argmax_workspace_bytes(void) { return gq::kArgmaxWorkspaceBytes; }
+
+int gq_qmv_q8_0_argmax(const int8_t* qs, const uint16_t* d, int64_t n, int64_t k, const float* x,
+                       const float* norm_weight, float norm_eps, float softcap, float* logits, void* workspace,
+                       size_t workspace_bytes, int32_t* index, float* value, void* stream) {
+    return qmv_argmax(GQ_TYPE_Q8_0, qs, d, n, k, x, norm_weight, norm_eps, softcap, logits, workspace,
+                      workspace_bytes, index, value, stream);
+}
+
+int gq_qmv_q4_0_argmax(const uint8_t* qs, const uint16_t* d, int64_t n, int64_t k, const float* x,
+                       const float* norm_weight, float norm_eps, float softcap, float* logits, void* workspace,
+                       size_t workspace_bytes, int32_t* index, float* value, void* stream) {
+    return qmv_argmax(GQ_TYPE_Q4_0, qs, d, n, k, x, norm_weight, norm_eps, softcap, logits, workspace,
+                      workspace_bytes, index, value, stream);
 }
 
 int gq_qmv_q8_0_q8(const int8_t* qs, const uint16_t* d, int64_t n, int64_t k, const int8_t* xq,
@@ -180,9 +244,11 @@ int gq_qmv_q4_0_q8(const uint8_t* qs, const uint16_t* d, int64_t n, int64_t k, c
     return qmv_q8(GQ_TYPE_Q4_0, qs, d, n, k, xq, xd, y, blockdots, stream);
 }
 
-int gq_qffn_gate_up_gelu(const uint8_t* g_qs, const uint16_t* g_d, const uint8_t* u_qs,
-                         const uint16_t* u_d, int64_t n_ff, int64_t k, const float* x, float* h,
-                         void* stream) {
+}  // extern "C"
+
+namespace {
+int ffn(const uint8_t* g_qs, const uint16_t* g_d, const uint8_t* u_qs, const uint16_t* u_d, int64_t n_ff,
+        int64_t k, const float* x, const float* norm_w, float norm_eps, float* h, void* stream) {
     if (g_qs == nullptr || g_d == nullptr || u_qs == nullptr || u_d == nullptr || x == nullptr ||
         h == nullptr)
         return GQ_ERR_NULL;
@@ -192,11 +258,30 @@ int gq_qffn_gate_up_gelu(const uint8_t* g_qs, const uint16_t* g_d, const uint8_t
     if (!aligned(g_qs, 16) || !aligned(u_qs, 16) || !aligned(g_d, 2) || !aligned(u_d, 2) ||
         !aligned(x, 16) || !aligned(h, 4))
         return GQ_ERR_ALIGN;
+    st = check_fold(norm_w, norm_eps, nullptr);
+    if (st != GQ_OK) return st;
     const size_t qb = qs_bytes(GQ_TYPE_Q4_0, n_ff, k), db = d_bytes(n_ff, k);
     const Range outs[] = {{h, static_cast<size_t>(n_ff) * 4}};
-    const Range ins[] = {{g_qs, qb}, {g_d, db}, {u_qs, qb}, {u_d, db}, {x, static_cast<size_t>(k) * 4}};
+    const Range ins[] = {{g_qs, qb}, {g_d, db}, {u_qs, qb}, {u_d, db}, {x, static_cast<size_t>(k) * 4},
+                         {norm_w, norm_w ? static_cast<size_t>(k) * 4 : 0}};
     if (any_alias(outs, ins)) return GQ_ERR_ALIAS;
-    return status_of(gq::launch_ffn_gate_up(g_qs, g_d, u_qs, u_d, n_ff, k, x, h, as_stream(stream)));
+    return status_of(gq::launch_ffn_gate_up(g_qs, g_d, u_qs, u_d, n_ff, k, x, norm_w, norm_eps, h,
+                                            as_stream(stream)));
+}
+}  // namespace
+
+extern "C" {
+
+int gq_qffn_gate_up_gelu(const uint8_t* g_qs, const uint16_t* g_d, const uint8_t* u_qs,
+                         const uint16_t* u_d, int64_t n_ff, int64_t k, const float* x, float* h,
+                         void* stream) {
+    return ffn(g_qs, g_d, u_qs, u_d, n_ff, k, x, nullptr, 0.0f, h, stream);
+}
+
+int gq_qffn_gate_up_gelu_ex(const uint8_t* g_qs, const uint16_t* g_d, const uint8_t* u_qs,
+                            const uint16_t* u_d, int64_t n_ff, int64_t k, const float* x,
+                            const float* norm_weight, float norm_eps, float* h, void* stream) {
+    return ffn(g_qs, g_d, u_qs, u_d, n_ff, k, x, norm_weight, norm_eps, h, stream);
 }
 
 int gq_qmm_tile_m(const uint8_t* qs, const uint16_t* d, int64_t n, int64_t k, int m, const int8_t* xq,

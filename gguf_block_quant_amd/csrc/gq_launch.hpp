@@ -36,8 +36,15 @@ hipError_t launch_pack(int type, const uint8_t* blocks, int64_t n, int64_t k, ui
 hipError_t launch_quantize_q8_0(const float* x, int64_t m, int64_t k, int8_t* xq, uint16_t* xd,
                                 hipStream_t stream);
 
+constexpr size_t kArgmaxWorkspaceBytes = 8192;   // >= 8 bytes x the largest matvec grid
+
 hipError_t launch_qmv_f32(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k,
-                          const float* x, float* y, hipStream_t stream);
+                          const float* x, const float* norm_w, float norm_eps, const float* residual,
+                          float* y, hipStream_t stream);
+
+hipError_t launch_qmv_argmax(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k,
+                             const float* x, const float* norm_w, float norm_eps, float softcap,
+                             float* y, void* workspace, int32_t* index, float* value, hipStream_t stream);
 
 hipError_t launch_qmv_q8(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k,
                          const int8_t* xq, const uint16_t* xd, float* y, int32_t* blockdots,
@@ -45,7 +52,7 @@ hipError_t launch_qmv_q8(int type, const void* qs, const uint16_t* d, int64_t n,
 
 hipError_t launch_ffn_gate_up(const uint8_t* g_qs, const uint16_t* g_d, const uint8_t* u_qs,
                               const uint16_t* u_d, int64_t n_ff, int64_t k, const float* x,
-                              float* h, hipStream_t stream);
+                              const float* norm_w, float norm_eps, float* h, hipStream_t stream);
 
 hipError_t launch_tile_q4_0(const uint8_t* qs, const uint16_t* d, int64_t n, int64_t k, int m,
                             const int8_t* xq, const uint16_t* xd, float* y, int32_t* blockdots,

@@ -57,11 +57,27 @@ struct QmvParams {
     const uint16_t* xd;     // Q8_0 activation scales [k/32]
     float* y;               // output [n]
     int32_t* blockdots;     // optional S [n][nb]
+    const float* norm_w;    // optional RMSNorm weight [k] (prologue on x)
+    const float* residual;  // optional residual [n] added to the output
+    unsigned long long* part;  // optional argmax partials [gridDim.x]
+    float norm_eps;
+    float softcap;          // > 0: output = softcap * tanh(output / softcap)
     int n;
+    int k;
     int units;              // 16-byte units per row
     int nb;                 // blocks per row
     int row_groups;         // ceil(n / R)
 };
+
+// Order-preserving 64-bit key of (value, row) for a greedy argmax: a larger
+// value gives a larger key, and for equal values the lower row does; -0 is
+// folded into +0 and NaN ranks below every number. 0 means "no row".
+__device__ __forceinline__ unsigned long long argmax_key(float v, int row) {
+    uint32_t u = __builtin_bit_cast(uint32_t, v == 0.0f ? 0.0f : v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    if (v != v) u = 0u;
+    return (static_cast<unsigned long long>(u) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(row));
+}
 
 // fp32-activation dot of one unit against the lane's activation registers.
 template <int TYPE>
@@ -183,16 +199,64 @@ void qmv_kernel(const QmvParams p) {
             sxr[i] = sx;
         }
     }
+    uint32_t uload[NI];     // clamped unit index (lanes past a short row)
+#pragma unroll
+    for (int i = 0; i < NI; ++i) uload[i] = static_cast<uint32_t>(min(unit[i], p.units - 1));
 
-    __shared__ float part[WAVES][NMAT][R];
+    // ---- optional RMSNorm prologue: x <- x * (mean(x^2) + eps)^-1/2 * w -----
+    // (SafeC Gemma 4 DESIGN_NOTES page, "RMSNorm"; the weight multiplies
+    // directly). The lanes of the WS waves of a workgroup hold all of x, so
+    // the sum of squares is a wave sum plus, for split rows, an LDS sum over
+    // the slices in fixed order; every wave then gets the same scale.
+    if constexpr (MODE != kQ8X) {
+        if (p.norm_w != nullptr) {
+            float ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+#pragma unroll
+                for (int e = 0; e < EPU; ++e) ss = fmaf(xr[i][e], xr[i][e], ss);
+            ss = wave_sum(ss);
+            if constexpr (WS > 1) {
+                __shared__ float nss[WAVES];
+                if (lane == 0) nss[wave] = ss;
+                __syncthreads();
+                float t = nss[sub * WS];
+#pragma unroll
+                for (int sl = 1; sl < WS; ++sl) t += nss[sub * WS + sl];
+                ss = t;
+            }
+            const float inv = 1.0f / sqrtf(ss / static_cast<float>(p.k) + p.norm_eps);
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const float4* ws4 = reinterpret_cast<const float4*>(p.norm_w + uload[i] * EPU);
+#pragma unroll
+                for (int v = 0; v < EPU / 4; ++v) {
+                    const float4 g = ws4[v];
+                    xr[i][4 * v + 0] = (xr[i][4 * v + 0] * inv) * g.x;
+                    xr[i][4 * v + 1] = (xr[i][4 * v + 1] * inv) * g.y;
+                    xr[i][4 * v + 2] = (xr[i][4 * v + 2] * inv) * g.z;
+                    xr[i][4 * v + 3] = (xr[i][4 * v + 3] * inv) * g.w;
+                }
+            }
+        }
+    }
+
+    // ---- epilogue of one finished row: residual, soft cap, store, argmax --
+    unsigned long long best = 0ull;
+    auto emit = [&](int row, float v) {
+        if (p.residual != nullptr) v += p.residual[row];
+        if (p.softcap > 0.0f) v = p.softcap * tanhf(v / p.softcap);
+        p.y[row] = v;
+        const unsigned long long key = argmax_key(v, row);
+        best = key > best ? key : best;
+    };
+
+    __shared__ float lpart[WAVES][NMAT][R];
 
     // Quant chunks and scales of one row group, for every unit of the lane.
     // Lanes past the end of a short row load a clamped (valid) unit and
     // contribute nothing: their activations are zero and their scale is
     // masked to zero below, so no load sits behind a divergent branch.
-    uint32_t uload[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) uload[i] = static_cast<uint32_t>(min(unit[i], p.units - 1));
     uint4 q[NI][NMAT][R];
     uint16_t db[NI][NMAT][R];
     auto load_group = [&](int r0) {
@@ -279,9 +343,9 @@ void qmv_kernel(const QmvParams p) {
                     const int row = r0 + r;
                     if (row < p.n) {
                         if constexpr (MODE == kFFN)
-                            p.y[row] = gelu_tanh(acc[0][r]) * acc[1][r];
+                            emit(row, gelu_tanh(acc[0][r]) * acc[1][r]);
                         else
-                            p.y[row] = acc[0][r];
+                            emit(row, acc[0][r]);
                     }
                 }
             }
@@ -290,7 +354,7 @@ void qmv_kernel(const QmvParams p) {
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-                    for (int r = 0; r < R; ++r) part[wave][m][r] = acc[m][r];
+                    for (int r = 0; r < R; ++r) lpart[wave][m][r] = acc[m][r];
             }
             __syncthreads();
             if (slice == 0 && lane < R) {
@@ -298,20 +362,60 @@ void qmv_kernel(const QmvParams p) {
                 float tot[NMAT];
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m) {
-                    float t = part[wave][m][lane];
+                    float t = lpart[wave][m][lane];
 #pragma unroll
-                    for (int s = 1; s < WS; ++s) t += part[wave + s][m][lane];
+                    for (int s = 1; s < WS; ++s) t += lpart[wave + s][m][lane];
                     tot[m] = t;
                 }
                 if (row < p.n) {
                     if constexpr (MODE == kFFN)
-                        p.y[row] = gelu_tanh(tot[0]) * tot[1];
+                        emit(row, gelu_tanh(tot[0]) * tot[1]);
                     else
-                        p.y[row] = tot[0];
+                        emit(row, tot[0]);
                 }
             }
             __syncthreads();
         }
+    }
+
+    // ---- argmax partial of this workgroup (fixed-shape tree, exact) --------
+    if (p.part != nullptr) {
+        __shared__ unsigned long long keys[WAVES * kWave];
+        keys[threadIdx.x] = best;
+        __syncthreads();
+        for (int st = WAVES * kWave / 2; st > 0; st >>= 1) {
+            if (static_cast<int>(threadIdx.x) < st) {
+                const unsigned long long o = keys[threadIdx.x + st];
+                keys[threadIdx.x] = o > keys[threadIdx.x] ? o : keys[threadIdx.x];
+            }
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) p.part[blockIdx.x] = keys[0];
+    }
+}
+
+// Second stage of the argmax: one workgroup folds the per-workgroup keys.
+__global__ __launch_bounds__(1024)
+void argmax_reduce_kernel(const unsigned long long* __restrict__ part, int nparts, int32_t* __restrict__ index,
+                          float* __restrict__ value) {
+    __shared__ unsigned long long keys[1024];
+    unsigned long long b = 0ull;
+    for (int i = threadIdx.x; i < nparts; i += 1024) b = part[i] > b ? part[i] : b;
+    keys[threadIdx.x] = b;
+    __syncthreads();
+    for (int st = 512; st > 0; st >>= 1) {
+        if (static_cast<int>(threadIdx.x) < st) {
+            const unsigned long long o = keys[threadIdx.x + st];
+            keys[threadIdx.x] = o > keys[threadIdx.x] ? o : keys[threadIdx.x];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        const unsigned long long k = keys[0];
+        const uint32_t hi = static_cast<uint32_t>(k >> 32);
+        const uint32_t u = (hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi;
+        *index = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(k & 0xFFFFFFFFull));
+        *value = hi == 0u ? __builtin_nanf("") : __builtin_bit_cast(float, u);
     }
 }
 
@@ -324,13 +428,14 @@ namespace {
 constexpr int kMaxGrid = GQ_QMV_MAX_GRID;
 
 template <int TYPE, int MODE, int NI, int WS, int R>
-hipError_t launch_rows(QmvParams p, hipStream_t stream) {
+hipError_t launch_rows(QmvParams p, hipStream_t stream, int* grid_out) {
     constexpr int WAVES = Waves<WS>::value;
     constexpr int SUBS = WAVES / WS;
     p.row_groups = (p.n + R - 1) / R;
     const int64_t iters = (static_cast<int64_t>(p.row_groups) + SUBS - 1) / SUBS;
     const int64_t max_grid = kMaxGrid * 4 / WAVES;
     const int grid = static_cast<int>(iters < max_grid ? iters : max_grid);
+    if (grid_out != nullptr) *grid_out = grid;
     return launch_kernel(qmv_kernel<TYPE, MODE, NI, WS, R>, dim3(grid), dim3(WAVES * kWave), stream, p);
 }
 
@@ -339,12 +444,12 @@ hipError_t launch_rows(QmvParams p, hipStream_t stream) {
 // matrices take 4 (each wave loops over many groups); shorter ones take 2
 // so more waves share the dequantisation work.
 template <int TYPE, int MODE, int NI, int WS>
-hipError_t launch_cfg(QmvParams p, hipStream_t stream) {
+hipError_t launch_cfg(QmvParams p, hipStream_t stream, int* grid_out) {
     if constexpr (WS >= 4) {
-        return launch_rows<TYPE, MODE, NI, WS, 8>(p, stream);
+        return launch_rows<TYPE, MODE, NI, WS, 8>(p, stream, grid_out);
     } else {
-        if (p.n >= 65536) return launch_rows<TYPE, MODE, NI, WS, 4>(p, stream);
-        return launch_rows<TYPE, MODE, NI, WS, 2>(p, stream);
+        if (p.n >= 65536) return launch_rows<TYPE, MODE, NI, WS, 4>(p, stream, grid_out);
+        return launch_rows<TYPE, MODE, NI, WS, 2>(p, stream, grid_out);
     }
 }
 
@@ -355,16 +460,16 @@ inline int units_per_lane(int units, int ws) {
 }
 
 template <int TYPE, int MODE>
-hipError_t dispatch(QmvParams p, hipStream_t stream) {
+hipError_t dispatch(QmvParams p, hipStream_t stream, int* grid_out = nullptr) {
     // The lane's activation slice stays at <= 32 values in VGPRs (Q8_0: two
     // units, Q4_0: one unit); longer rows are split over more waves.
     constexpr int kNiMax = (TYPE == kTypeQ8_0) ? 2 : 1;
-    if (units_per_lane(p.units, 1) == 1) return launch_cfg<TYPE, MODE, 1, 1>(p, stream);
-    if (units_per_lane(p.units, 1) <= kNiMax) return launch_cfg<TYPE, MODE, kNiMax, 1>(p, stream);
-    if (units_per_lane(p.units, 2) <= kNiMax) return launch_cfg<TYPE, MODE, kNiMax, 2>(p, stream);
-    if (units_per_lane(p.units, 4) <= kNiMax) return launch_cfg<TYPE, MODE, kNiMax, 4>(p, stream);
-    if (units_per_lane(p.units, 8) <= kNiMax) return launch_cfg<TYPE, MODE, kNiMax, 8>(p, stream);
-    if (units_per_lane(p.units, 16) <= kNiMax) return launch_cfg<TYPE, MODE, kNiMax, 16>(p, stream);
+    if (units_per_lane(p.units, 1) == 1) return launch_cfg<TYPE, MODE, 1, 1>(p, stream, grid_out);
+    if (units_per_lane(p.units, 1) <= kNiMax) return launch_cfg<TYPE, MODE, kNiMax, 1>(p, stream, grid_out);
+    if (units_per_lane(p.units, 2) <= kNiMax) return launch_cfg<TYPE, MODE, kNiMax, 2>(p, stream, grid_out);
+    if (units_per_lane(p.units, 4) <= kNiMax) return launch_cfg<TYPE, MODE, kNiMax, 4>(p, stream, grid_out);
+    if (units_per_lane(p.units, 8) <= kNiMax) return launch_cfg<TYPE, MODE, kNiMax, 8>(p, stream, grid_out);
+    if (units_per_lane(p.units, 16) <= kNiMax) return launch_cfg<TYPE, MODE, kNiMax, 16>(p, stream, grid_out);
     return hipErrorInvalidValue;    // beyond the documented maximum k (32768)
 }
 
@@ -375,21 +480,32 @@ QmvParams base_params(const void* qs, const uint16_t* d, int64_t n, int64_t k, i
     p.n = static_cast<int>(n);
     p.units = static_cast<int>(k / 32 * bytes_per_32 / 16);
     p.nb = static_cast<int>(k / 32);
+    p.k = static_cast<int>(k);
     return p;
 }
 
 }  // namespace
 
 hipError_t launch_qmv_f32(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k,
-                          const float* x, float* y, hipStream_t stream) {
-    if (type == kTypeQ8_0) {
-        QmvParams p = base_params(qs, d, n, k, 32);
-        p.x = x; p.y = y;
-        return dispatch<kTypeQ8_0, kF32>(p, stream);
-    }
-    QmvParams p = base_params(qs, d, n, k, 16);
-    p.x = x; p.y = y;
-    return dispatch<kTypeQ4_0, kF32>(p, stream);
+                          const float* x, const float* norm_w, float norm_eps, const float* residual,
+                          float* y, hipStream_t stream) {
+    QmvParams p = base_params(qs, d, n, k, type == kTypeQ8_0 ? 32 : 16);
+    p.x = x; p.y = y; p.norm_w = norm_w; p.norm_eps = norm_eps; p.residual = residual;
+    return type == kTypeQ8_0 ? dispatch<kTypeQ8_0, kF32>(p, stream) : dispatch<kTypeQ4_0, kF32>(p, stream);
+}
+
+hipError_t launch_qmv_argmax(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k,
+                             const float* x, const float* norm_w, float norm_eps, float softcap,
+                             float* y, void* workspace, int32_t* index, float* value, hipStream_t stream) {
+    QmvParams p = base_params(qs, d, n, k, type == kTypeQ8_0 ? 32 : 16);
+    p.x = x; p.y = y; p.norm_w = norm_w; p.norm_eps = norm_eps; p.softcap = softcap;
+    p.part = static_cast<unsigned long long*>(workspace);
+    int grid = 0;
+    hipError_t e = type == kTypeQ8_0 ? dispatch<kTypeQ8_0, kF32>(p, stream, &grid)
+                                     : dispatch<kTypeQ4_0, kF32>(p, stream, &grid);
+    if (e != hipSuccess) return e;
+    return launch_kernel(argmax_reduce_kernel, dim3(1), dim3(1024), stream,
+                         static_cast<const unsigned long long*>(workspace), grid, index, value);
 }
 
 hipError_t launch_qmv_q8(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k,
@@ -407,9 +523,9 @@ hipError_t launch_qmv_q8(int type, const void* qs, const uint16_t* d, int64_t n,
 
 hipError_t launch_ffn_gate_up(const uint8_t* g_qs, const uint16_t* g_d, const uint8_t* u_qs,
                               const uint16_t* u_d, int64_t n_ff, int64_t k, const float* x,
-                              float* h, hipStream_t stream) {
+                              const float* norm_w, float norm_eps, float* h, hipStream_t stream) {
     QmvParams p = base_params(g_qs, g_d, n_ff, k, 16);
-    p.qs2 = u_qs; p.d2 = u_d; p.x = x; p.y = h;
+    p.qs2 = u_qs; p.d2 = u_d; p.x = x; p.y = h; p.norm_w = norm_w; p.norm_eps = norm_eps;
     return dispatch<kTypeQ4_0, kFFN>(p, stream);
 }
 

@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define GQ_ABI_VERSION 1
+#define GQ_ABI_VERSION 2
 
 enum {
     GQ_OK = 0,
@@ -78,7 +78,8 @@ enum {
     GQ_ERR_ALIGN = 3,        /* a pointer violates its alignment */
     GQ_ERR_ALIAS = 4,        /* an output overlaps an input */
     GQ_ERR_UNSUPPORTED = 5,  /* unknown type, k or m beyond what is built */
-    GQ_ERR_LAUNCH = 6        /* the kernel launch failed */
+    GQ_ERR_LAUNCH = 6,       /* the kernel launch failed */
+    GQ_ERR_VALUE = 7         /* bad eps / soft cap, or workspace too small */
 };
 
 enum {
@@ -142,6 +143,54 @@ int gq_qmv_q4_0(const uint8_t *qs, const uint16_t *d, int64_t n, int64_t k,
                 const float *x, float *y, void *stream);
 
 /*
+ * gq_qmv_q8_0_ex / gq_qmv_q4_0_ex -- the same matvec with the folds that
+ * sit on either side of a decode projection (Gemma-4-E2B raw-Metal port page,
+ * "Architecture", kernels bullet: rmsnorm prologue and residual epilogue
+ * folds; Gem native architecture page, residual epilogues):
+ *  - if norm_weight is not NULL, x is first replaced by the Gemma RMSNorm
+ *    x * (mean(x^2) + norm_eps)^(-1/2) * norm_weight, with the weight
+ *    applied directly (SafeC Gemma 4 DESIGN_NOTES page, "RMSNorm"; Gemma 4
+ *    uses norm_eps = 1e-6); norm_weight fp32 [k], 16-byte aligned;
+ *    norm_eps >= 0 and finite, else GQ_ERR_VALUE;
+ *  - if residual is not NULL, y[r] = residual[r] + (W x)[r]; residual fp32
+ *    [n], 4-byte aligned; y may equal residual (in-place accumulate) but
+ *    may not overlap it otherwise.
+ * With both NULL these are gq_qmv_q8_0 / gq_qmv_q4_0.
+ */
+int gq_qmv_q8_0_ex(const int8_t *qs, const uint16_t *d, int64_t n, int64_t k,
+                   const float *x, const float *norm_weight, float norm_eps,
+                   const float *residual, float *y, void *stream);
+int gq_qmv_q4_0_ex(const uint8_t *qs, const uint16_t *d, int64_t n, int64_t k,
+                   const float *x, const float *norm_weight, float norm_eps,
+                   const float *residual, float *y, void *stream);
+
+/*
+ * gq_qmv_q8_0_argmax / gq_qmv_q4_0_argmax -- the vocabulary head of greedy
+ * decode: optional RMSNorm prologue (as in the _ex entries), the matvec,
+ * then per row the final-logit soft cap logits[r] = softcap * tanh(y[r] /
+ * softcap) (SafeC DESIGN_NOTES page, "LM head"; Gemma 4 uses 30; softcap =
+ * 0 leaves y unchanged), all written to logits fp32 [n], and a two-stage
+ * on-GPU argmax (raw-Metal port page, "Architecture"): *index receives the
+ * row of the largest logit, ties going to the lowest row, NaN ranking below
+ * every number; *value receives that logit. workspace is caller-owned
+ * device scratch of at least gq_argmax_workspace_bytes() bytes, 8-byte
+ * aligned, holding the per-workgroup partials between the two stages; its
+ * contents on entry are ignored. softcap must be >= 0 and finite, else
+ * GQ_ERR_VALUE (also for a short workspace).
+ */
+size_t gq_argmax_workspace_bytes(void);
+int gq_qmv_q8_0_argmax(const int8_t *qs, const uint16_t *d, int64_t n, int64_t k,
+                       const float *x, const float *norm_weight, float norm_eps,
+                       float softcap, float *logits, void *workspace,
+                       size_t workspace_bytes, int32_t *index, float *value,
+                       void *stream);
+int gq_qmv_q4_0_argmax(const uint8_t *qs, const uint16_t *d, int64_t n, int64_t k,
+                       const float *x, const float *norm_weight, float norm_eps,
+                       float softcap, float *logits, void *workspace,
+                       size_t workspace_bytes, int32_t *index, float *value,
+                       void *stream);
+
+/*
  * gq_qmv_q8_0_q8 / gq_qmv_q4_0_q8 -- decode matvec against one Q8_0
  * activation row (xq int8 [k], xd binary16 bits [k/32]):
  * S[r][b] = sum_i qw[r][b][i] * xq[b][i] computed exactly in int32
@@ -170,6 +219,15 @@ int gq_qffn_gate_up_gelu(const uint8_t *g_qs, const uint16_t *g_d,
                          const uint8_t *u_qs, const uint16_t *u_d,
                          int64_t n_ff, int64_t k, const float *x, float *h,
                          void *stream);
+
+/* The gate+up FFN pass with the pre-FFN RMSNorm folded in as a prologue
+ * (norm_weight / norm_eps as in gq_qmv_q4_0_ex; NULL weight = no norm). The
+ * residual after the down projection is gq_qmv_q4_0_ex's epilogue. */
+int gq_qffn_gate_up_gelu_ex(const uint8_t *g_qs, const uint16_t *g_d,
+                            const uint8_t *u_qs, const uint16_t *u_d,
+                            int64_t n_ff, int64_t k, const float *x,
+                            const float *norm_weight, float norm_eps, float *h,
+                            void *stream);
 
 /*
  * gq_qmm_tile_m -- small-M tile, Q4_0 weights [n][k] against m Q8_0

@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "gq.h")
 
 gq = pytest.importorskip("gguf_block_quant_amd")
 
-OK, NULL, SHAPE, ALIGN, ALIAS, UNSUP = 0, 1, 2, 3, 4, 5
+OK, NULL, SHAPE, ALIGN, ALIAS, UNSUP, VALUE = 0, 1, 2, 3, 4, 5, 7
 Q4, Q8 = 2, 8
 
 # Fake, never-dereferenced addresses: every call below fails validation first.
@@ -40,8 +40,8 @@ def test_header_symbols_all_exported():
 
 
 def test_version_and_status_strings():
-    assert gq.abi_version() == 1
-    for s in range(7):
+    assert gq.abi_version() == 2
+    for s in range(8):
         assert gq.status_str(s)
     assert gq.status_str(99) == "unknown status"
 
@@ -124,3 +124,43 @@ def test_pack_and_quantize_validation():
     assert L.gq_quantize_q8_0(A, 2, 100, B, C, None) == SHAPE
     assert L.gq_quantize_q8_0(A + 4, 2, 128, B, C, None) == ALIGN
     assert L.gq_quantize_q8_0(A, 2, 128, A + 16, C, None) == ALIAS
+
+
+@pytest.mark.parametrize("fn", ["gq_qmv_q8_0_ex", "gq_qmv_q4_0_ex"])
+def test_qmv_ex_validation(fn):
+    f = getattr(L, fn)
+    NW = 0x60000000
+    # (qs, d, n, k, x, norm_w, eps, residual, y, stream)
+    assert f(A, B, 64, 256, C, NW + 4, 1e-6, None, D, None) == ALIGN      # norm weight 16-B
+    assert f(A, B, 64, 256, C, NW, -1.0, None, D, None) == VALUE           # negative eps
+    assert f(A, B, 64, 256, C, NW, float("nan"), None, D, None) == VALUE
+    assert f(A, B, 64, 256, C, NW, float("inf"), None, D, None) == VALUE
+    assert f(A, B, 64, 256, C, None, 1e-6, E + 2, D, None) == ALIGN        # residual 4-B
+    assert f(A, B, 64, 256, C, None, 0.0, D + 8, D, None) == ALIAS         # residual overlaps y
+    assert f(A, B, 64, 256, C, NW, 1e-6, None, NW + 64, None) == ALIAS     # y over the norm weight
+    assert f(A, B, 64, 250, C, NW, 1e-6, None, D, None) == SHAPE
+
+
+@pytest.mark.parametrize("fn", ["gq_qmv_q8_0_argmax", "gq_qmv_q4_0_argmax"])
+def test_argmax_validation(fn):
+    f = getattr(L, fn)
+    W, I, V = 0x70000000, 0x71000000, 0x72000000
+    ws = gq.argmax_workspace_bytes()
+    assert ws >= 8 * 1024
+    # (qs, d, n, k, x, norm_w, eps, softcap, logits, ws, ws_bytes, index, value, stream)
+    assert f(A, B, 64, 256, C, None, 0.0, 30.0, D, None, ws, I, V, None) == NULL
+    assert f(A, B, 64, 256, C, None, 0.0, 30.0, D, W, ws, None, V, None) == NULL
+    assert f(A, B, 64, 256, C, None, 0.0, 30.0, D, W, ws - 8, I, V, None) == VALUE
+    assert f(A, B, 64, 256, C, None, 0.0, -1.0, D, W, ws, I, V, None) == VALUE
+    assert f(A, B, 64, 256, C, None, 0.0, float("nan"), D, W, ws, I, V, None) == VALUE
+    assert f(A, B, 64, 256, C, None, 0.0, 30.0, D, W + 4, ws, I, V, None) == ALIGN
+    assert f(A, B, 64, 256, C, None, 0.0, 30.0, D, D + 64, ws, I, V, None) == ALIAS   # workspace over logits
+    assert f(A, B, 64, 256, C, None, 0.0, 30.0, D, W, ws, W + 16, V, None) == ALIAS   # index inside workspace
+
+
+def test_ffn_ex_validation():
+    f = L.gq_qffn_gate_up_gelu_ex
+    NW = 0x60000000
+    assert f(A, B, C, E, 64, 256, D, NW, -1e-6, 0x61000000, None) == VALUE
+    assert f(A, B, C, E, 64, 256, D, NW + 8, 1e-6, 0x61000000, None) == ALIGN
+    assert f(A, B, C, E, 64, 256, D, NW, 1e-6, NW + 128, None) == ALIAS
