@@ -156,6 +156,34 @@ class Step:
                                  (P(wt[m][0]), P(wt[m][1]), 8192, 2048, m, P(acts[m][0]), P(acts[m][1]),
                                   P(yt[m]), None, sp), 8192 * 64 * 18, m * 2176 + m * 8192 * 4))
             self.sets.append(launches)
+            if s == 0:
+                # entry points beyond the step (the folds around a projection,
+                # the vocabulary head, a batched-decode tile), timed on their own
+                rng = np.random.default_rng(1)
+                g2 = up(rng.uniform(0.5, 1.5, 2048).astype(np.float32))
+                res2 = up(rng.standard_normal(2048).astype(np.float32))
+                y2c = torch.empty(2048, dtype=torch.float32, device=dev)
+                logits = torch.empty(262144, dtype=torch.float32, device=dev)
+                ws = torch.empty(gq.argmax_workspace_bytes(), dtype=torch.uint8, device=dev)
+                idx = torch.empty(1, dtype=torch.int32, device=dev)
+                val = torch.empty(1, dtype=torch.float32, device=dev)
+                xq4, xd4 = (up(c5["acts"][8][0][:4].copy()), up(c5["acts"][8][1][:4].copy()))
+                y4t = torch.empty((4, 8192), dtype=torch.float32, device=dev)
+                self.keep += [g2, res2, y2c, logits, ws, idx, val, xq4, xd4, y4t]
+                self.extras = [
+                    ("qmv_q4_0_ex 2048x2048 (rmsnorm + residual)", L.gq_qmv_q4_0_ex,
+                     (P(w2a[0]), P(w2a[1]), 2048, 2048, P(x2), P(g2), ctypes.c_float(1e-6), P(res2), P(y2c), sp),
+                     2048 * 64 * 18, 8192 * 3 + 8192),
+                    ("qffn_gate_up_gelu_ex 8192x2048 (rmsnorm)", L.gq_qffn_gate_up_gelu_ex,
+                     (P(wg[0]), P(wg[1]), P(wu[0]), P(wu[1]), 8192, 2048, P(x3), P(g2), ctypes.c_float(1e-6),
+                      P(h3), sp), 2 * 8192 * 64 * 18, 8192 * 2 + 32768),
+                    ("qmv_q8_0_argmax 262144x2048 (rmsnorm + softcap 30 + argmax)", L.gq_qmv_q8_0_argmax,
+                     (P(wv[0]), P(wv[1]), 262144, 2048, P(x4), P(g2), ctypes.c_float(1e-6), ctypes.c_float(30.0),
+                      P(logits), P(ws), ws.numel(), P(idx), P(val), sp), 262144 * 64 * 34, 8192 * 2 + 262144 * 4),
+                    ("qmm_tile_m 8192x2048 M=4 (batched decode)", L.gq_qmm_tile_m,
+                     (P(wt[8][0]), P(wt[8][1]), 8192, 2048, 4, P(xq4), P(xd4), P(y4t), None, sp),
+                     8192 * 64 * 18, 4 * 2176 + 4 * 8192 * 4),
+                ]
         torch.cuda.synchronize()
         log("packed %d weight set(s) in %.1fs" % (sets, time.time() - t0))
         self.names = [l[0] for l in self.sets[0]]
@@ -400,6 +428,26 @@ def main():
                         "weight_GBps": round(wb / med / 1e3, 1) if wb else None,
                         "total_GBps": round((wb + step.other_bytes[n]) / med / 1e3, 1)}
 
+    # entry points beyond the step, each on its own (set-0 weights, MALL-cold
+    # only to the extent the step's rotation left them)
+    extras = {}
+    for name, fn, fargs, wb, ob in step.extras:
+        evs = []
+        for _ in range(nb):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(step.stream)
+            if fn(*fargs) != 0:
+                raise RuntimeError("launch failed: " + name)
+            b.record(step.stream)
+            evs.append((a, b))
+            step.run(0)        # stream other weights between repeats
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        med = us[len(us) // 2]
+        extras[name] = {"median_us": round(med, 2), "weight_bytes": wb,
+                        "weight_GBps": round(wb / med / 1e3, 1), "total_GBps": round((wb + ob) / med / 1e3, 1)}
+
     traffic = load_traffic()
     cpu = None
     if not args.no_cpu_baseline:
@@ -442,6 +490,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "breakdown": breakdown,
+        "extras": extras,
     }
     print(json.dumps(out), flush=True)
 

@@ -147,7 +147,11 @@ __device__ __forceinline__ int unit_dot_q8(const uint4 q, const uint32_t* xr, in
 // Waves per workgroup for a K split over WS waves: at least 4.
 template <int WS> struct Waves { static constexpr int value = WS < 4 ? 4 : WS; };
 
-template <int TYPE, int MODE, int NI, int WS, int R>
+// FOLD selects the variant with the optional RMSNorm prologue and the
+// residual / soft-cap / argmax epilogue (runtime flags in QmvParams); the
+// plain variant carries none of that code, so its register budget is
+// untouched.
+template <int TYPE, int MODE, int NI, int WS, int R, bool FOLD>
 __global__ __launch_bounds__(Waves<WS>::value * kWave)
 void qmv_kernel(const QmvParams p) {
     constexpr int EPU = Fmt<TYPE>::kElemsPerUnit;
@@ -203,52 +207,18 @@ void qmv_kernel(const QmvParams p) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) uload[i] = static_cast<uint32_t>(min(unit[i], p.units - 1));
 
-    // ---- optional RMSNorm prologue: x <- x * (mean(x^2) + eps)^-1/2 * w -----
-    // (SafeC Gemma 4 DESIGN_NOTES page, "RMSNorm"; the weight multiplies
-    // directly). The lanes of the WS waves of a workgroup hold all of x, so
-    // the sum of squares is a wave sum plus, for split rows, an LDS sum over
-    // the slices in fixed order; every wave then gets the same scale.
-    if constexpr (MODE != kQ8X) {
-        if (p.norm_w != nullptr) {
-            float ss = 0.f;
-#pragma unroll
-            for (int i = 0; i < NI; ++i)
-#pragma unroll
-                for (int e = 0; e < EPU; ++e) ss = fmaf(xr[i][e], xr[i][e], ss);
-            ss = wave_sum(ss);
-            if constexpr (WS > 1) {
-                __shared__ float nss[WAVES];
-                if (lane == 0) nss[wave] = ss;
-                __syncthreads();
-                float t = nss[sub * WS];
-#pragma unroll
-                for (int sl = 1; sl < WS; ++sl) t += nss[sub * WS + sl];
-                ss = t;
-            }
-            const float inv = 1.0f / sqrtf(ss / static_cast<float>(p.k) + p.norm_eps);
-#pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                const float4* ws4 = reinterpret_cast<const float4*>(p.norm_w + uload[i] * EPU);
-#pragma unroll
-                for (int v = 0; v < EPU / 4; ++v) {
-                    const float4 g = ws4[v];
-                    xr[i][4 * v + 0] = (xr[i][4 * v + 0] * inv) * g.x;
-                    xr[i][4 * v + 1] = (xr[i][4 * v + 1] * inv) * g.y;
-                    xr[i][4 * v + 2] = (xr[i][4 * v + 2] * inv) * g.z;
-                    xr[i][4 * v + 3] = (xr[i][4 * v + 3] * inv) * g.w;
-                }
-            }
-        }
-    }
-
     // ---- epilogue of one finished row: residual, soft cap, store, argmax --
     unsigned long long best = 0ull;
     auto emit = [&](int row, float v) {
-        if (p.residual != nullptr) v += p.residual[row];
-        if (p.softcap > 0.0f) v = p.softcap * tanhf(v / p.softcap);
+        if constexpr (FOLD) {
+            if (p.residual != nullptr) v += p.residual[row];
+            if (p.softcap > 0.0f) v = p.softcap * tanhf(v / p.softcap);
+        }
         p.y[row] = v;
-        const unsigned long long key = argmax_key(v, row);
-        best = key > best ? key : best;
+        if constexpr (FOLD) {
+            const unsigned long long key = argmax_key(v, row);
+            best = key > best ? key : best;
+        }
     };
 
     __shared__ float lpart[WAVES][NMAT][R];
@@ -288,6 +258,50 @@ void qmv_kernel(const QmvParams p) {
 #if GQ_QMV_CARRY
     if (it * SUBS < p.row_groups) load_group((it * SUBS + sub) * R);
 #endif
+    // ---- optional RMSNorm prologue (SafeC Gemma 4 DESIGN_NOTES page,
+    // "RMSNorm"): x <- x * (mean(x^2) + eps)^-1/2 * w, the weight multiplying
+    // directly. The scale is one scalar per activation vector, so the lanes
+    // fold only w into their registers now and apply the scalar to each
+    // finished row: y = inv * (W (x * w)). The sum of squares is taken from
+    // the raw x; the WS waves of a workgroup hold all of x, so it is a wave
+    // sum plus, for split rows, an LDS sum over the slices in fixed order.
+    float ss = 0.f;
+    if constexpr (MODE != kQ8X && FOLD) {
+        if (p.norm_w != nullptr) {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const float4* ws4 = reinterpret_cast<const float4*>(
+                    p.norm_w + static_cast<uint32_t>(min(unit[i], p.units - 1)) * EPU);
+#pragma unroll
+                for (int v = 0; v < EPU / 4; ++v) {
+                    const float4 g = ws4[v];
+                    ss = fmaf(xr[i][4 * v + 0], xr[i][4 * v + 0], ss);
+                    ss = fmaf(xr[i][4 * v + 1], xr[i][4 * v + 1], ss);
+                    ss = fmaf(xr[i][4 * v + 2], xr[i][4 * v + 2], ss);
+                    ss = fmaf(xr[i][4 * v + 3], xr[i][4 * v + 3], ss);
+                    xr[i][4 * v + 0] *= g.x; xr[i][4 * v + 1] *= g.y;
+                    xr[i][4 * v + 2] *= g.z; xr[i][4 * v + 3] *= g.w;
+                }
+            }
+        }
+    }
+    // the norm's scalar, while the first rows are in flight
+    float inv = 1.0f;
+    if constexpr (MODE != kQ8X && FOLD) {
+        if (p.norm_w != nullptr) {
+            ss = wave_sum(ss);
+            if constexpr (WS > 1) {
+                __shared__ float nss[WAVES];
+                if (lane == 0) nss[wave] = ss;
+                __syncthreads();
+                float t = nss[sub * WS];
+#pragma unroll
+                for (int sl = 1; sl < WS; ++sl) t += nss[sub * WS + sl];
+                ss = t;
+            }
+            inv = 1.0f / sqrtf(ss / static_cast<float>(p.k) + p.norm_eps);
+        }
+    }
     for (; it * SUBS < p.row_groups; it += gridDim.x) {
         const int g = it * SUBS + sub;
         const int r0 = g * R;
@@ -343,9 +357,9 @@ void qmv_kernel(const QmvParams p) {
                     const int row = r0 + r;
                     if (row < p.n) {
                         if constexpr (MODE == kFFN)
-                            emit(row, gelu_tanh(acc[0][r]) * acc[1][r]);
+                            emit(row, gelu_tanh(inv * acc[0][r]) * (inv * acc[1][r]));
                         else
-                            emit(row, acc[0][r]);
+                            emit(row, inv * acc[0][r]);
                     }
                 }
             }
@@ -369,9 +383,9 @@ void qmv_kernel(const QmvParams p) {
                 }
                 if (row < p.n) {
                     if constexpr (MODE == kFFN)
-                        emit(row, gelu_tanh(tot[0]) * tot[1]);
+                        emit(row, gelu_tanh(inv * tot[0]) * (inv * tot[1]));
                     else
-                        emit(row, tot[0]);
+                        emit(row, inv * tot[0]);
                 }
             }
             __syncthreads();
@@ -379,7 +393,7 @@ void qmv_kernel(const QmvParams p) {
     }
 
     // ---- argmax partial of this workgroup (fixed-shape tree, exact) --------
-    if (p.part != nullptr) {
+    if (FOLD && p.part != nullptr) {
         __shared__ unsigned long long keys[WAVES * kWave];
         keys[threadIdx.x] = best;
         __syncthreads();
@@ -427,25 +441,56 @@ namespace {
 
 constexpr int kMaxGrid = GQ_QMV_MAX_GRID;
 
-template <int TYPE, int MODE, int NI, int WS, int R>
-hipError_t launch_rows(QmvParams p, hipStream_t stream, int* grid_out) {
+// Workgroups of a kernel that can be resident at once on the device: the
+// persistent grid is never larger, so no workgroup waits for a second round.
+// The per-kernel occupancy is a property of the code object, queried once.
+template <typename K>
+int resident_workgroups(K kernel, int threads) {
+    static const int per_cu = [&] {
+        int b = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kernel, threads, 0) != hipSuccess || b < 1) b = 1;
+        return b;
+    }();
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
+    return per_cu * cus;
+}
+
+template <int TYPE, int MODE, int NI, int WS, int R, bool FOLD>
+hipError_t launch_variant(QmvParams p, hipStream_t stream, int* grid_out) {
     constexpr int WAVES = Waves<WS>::value;
     constexpr int SUBS = WAVES / WS;
     p.row_groups = (p.n + R - 1) / R;
     const int64_t iters = (static_cast<int64_t>(p.row_groups) + SUBS - 1) / SUBS;
+    const auto kernel = qmv_kernel<TYPE, MODE, NI, WS, R, FOLD>;
+    int64_t cap = resident_workgroups(kernel, WAVES * kWave);
     const int64_t max_grid = kMaxGrid * 4 / WAVES;
-    const int grid = static_cast<int>(iters < max_grid ? iters : max_grid);
+    cap = cap < max_grid ? cap : max_grid;
+    const int grid = static_cast<int>(iters < cap ? iters : cap);
     if (grid_out != nullptr) *grid_out = grid;
-    return launch_kernel(qmv_kernel<TYPE, MODE, NI, WS, R>, dim3(grid), dim3(WAVES * kWave), stream, p);
+    return launch_kernel(kernel, dim3(grid), dim3(WAVES * kWave), stream, p);
 }
 
-// Rows per wave step (measured on MI355X): rows split over >= 4 waves
+template <int TYPE, int MODE, int NI, int WS, int R>
+hipError_t launch_rows(QmvParams p, hipStream_t stream, int* grid_out) {
+    const bool fold = p.norm_w != nullptr || p.residual != nullptr || p.softcap > 0.0f || p.part != nullptr;
+    if (fold) return launch_variant<TYPE, MODE, NI, WS, R, true>(p, stream, grid_out);
+    return launch_variant<TYPE, MODE, NI, WS, R, false>(p, stream, grid_out);
+}
+
+// Rows per wave step (measured on MI355X): rows split over 4 or 8 waves
 // stream 8 rows at a time to keep enough bytes in flight per wave; very tall
 // matrices take 4 (each wave loops over many groups); shorter ones take 2
 // so more waves share the dequantisation work.
 template <int TYPE, int MODE, int NI, int WS>
 hipError_t launch_cfg(QmvParams p, hipStream_t stream, int* grid_out) {
-    if constexpr (WS >= 4) {
+    if constexpr (WS >= 16) {
+        // 1024-thread workgroups cap a lane at 128 VGPRs: 4 rows (2 row pairs
+        // for the gate+up FFN) fit unspilled
+        return launch_rows<TYPE, MODE, NI, WS, (MODE == kFFN ? 2 : 4)>(p, stream, grid_out);
+    } else if constexpr (WS >= 4) {
         return launch_rows<TYPE, MODE, NI, WS, 8>(p, stream, grid_out);
     } else {
         if (p.n >= 65536) return launch_rows<TYPE, MODE, NI, WS, 4>(p, stream, grid_out);
