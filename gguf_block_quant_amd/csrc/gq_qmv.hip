@@ -29,6 +29,9 @@
 #ifndef GQ_QMV_CARRY
 #define GQ_QMV_CARRY 1         // issue the next row group's loads before this one's reduction
 #endif
+#ifndef GQ_QMV_WAVES1
+#define GQ_QMV_WAVES1 4        // waves per workgroup for un-split rows (they share one LDS copy of x)
+#endif
 #ifndef GQ_QMV_NT
 #define GQ_QMV_NT 1            // non-temporal loads for the quant stream (read once)
 #endif
@@ -146,6 +149,7 @@ __device__ __forceinline__ int unit_dot_q8(const uint4 q, const uint32_t* xr, in
 
 // Waves per workgroup for a K split over WS waves: at least 4.
 template <int WS> struct Waves { static constexpr int value = WS < 4 ? 4 : WS; };
+template <> struct Waves<1> { static constexpr int value = GQ_QMV_WAVES1; };
 
 // FOLD selects the variant with the optional RMSNorm prologue and the
 // residual / soft-cap / argmax epilogue (runtime flags in QmvParams); the
@@ -164,64 +168,22 @@ void qmv_kernel(const QmvParams p) {
     const int slice = wave % WS;
     const int sub = wave / WS;
     const int row_bytes = p.units * 16;
+    // fp32 activations of un-split rows are staged through LDS (below)
+    constexpr bool kStage = (MODE != kQ8X) && (WS == 1);
+    constexpr int kPitch = EPU + 4;
+    __shared__ float xstage[kStage ? NI * kWave * kPitch : 1];
+    __shared__ float nss[WAVES];
 
-    // ---- activation registers for this lane's units ----------------------
+    // ---- this lane's units ------------------------------------------------
     int unit[NI];
     bool uvalid[NI];
-    float xr[(MODE == kQ8X) ? 1 : NI][(MODE == kQ8X) ? 1 : EPU];
-    uint32_t xqr[(MODE == kQ8X) ? NI : 1][(MODE == kQ8X) ? EPU / 4 : 1];
-    float dxr[NI];
-    int sxr[NI];
+    uint32_t uload[NI];     // clamped unit index (lanes past a short row)
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         unit[i] = (slice * NI + i) * kWave + lane;
         uvalid[i] = unit[i] < p.units;
-        const int e0 = unit[i] * EPU;
-        if constexpr (MODE != kQ8X) {
-            const float4* xs = reinterpret_cast<const float4*>(p.x + e0);
-#pragma unroll
-            for (int v = 0; v < EPU / 4; ++v) {
-                const float4 t = uvalid[i] ? xs[v] : make_float4(0.f, 0.f, 0.f, 0.f);
-                xr[i][4 * v + 0] = t.x; xr[i][4 * v + 1] = t.y;
-                xr[i][4 * v + 2] = t.z; xr[i][4 * v + 3] = t.w;
-            }
-            dxr[i] = 0.f; sxr[i] = 0;
-        } else {
-            const uint4* xs = reinterpret_cast<const uint4*>(p.xq + e0);
-#pragma unroll
-            for (int v = 0; v < EPU / 16; ++v) {
-                const uint4 t = uvalid[i] ? xs[v] : make_uint4(0u, 0u, 0u, 0u);
-                xqr[i][4 * v + 0] = t.x; xqr[i][4 * v + 1] = t.y;
-                xqr[i][4 * v + 2] = t.z; xqr[i][4 * v + 3] = t.w;
-            }
-            dxr[i] = uvalid[i] ? half_bits_to_float(p.xd[unit[i] >> SH]) : 0.f;
-            int sx = 0;
-            if constexpr (TYPE == kTypeQ4_0) {
-#pragma unroll
-                for (int v = 0; v < EPU / 4; ++v) sx = dot4(xqr[i][v], 0x01010101u, sx);
-            }
-            sxr[i] = sx;
-        }
+        uload[i] = static_cast<uint32_t>(min(unit[i], p.units - 1));
     }
-    uint32_t uload[NI];     // clamped unit index (lanes past a short row)
-#pragma unroll
-    for (int i = 0; i < NI; ++i) uload[i] = static_cast<uint32_t>(min(unit[i], p.units - 1));
-
-    // ---- epilogue of one finished row: residual, soft cap, store, argmax --
-    unsigned long long best = 0ull;
-    auto emit = [&](int row, float v) {
-        if constexpr (FOLD) {
-            if (p.residual != nullptr) v += p.residual[row];
-            if (p.softcap > 0.0f) v = p.softcap * tanhf(v / p.softcap);
-        }
-        p.y[row] = v;
-        if constexpr (FOLD) {
-            const unsigned long long key = argmax_key(v, row);
-            best = key > best ? key : best;
-        }
-    };
-
-    __shared__ float lpart[WAVES][NMAT][R];
 
     // Quant chunks and scales of one row group, for every unit of the lane.
     // Lanes past the end of a short row load a clamped (valid) unit and
@@ -254,44 +216,123 @@ void qmv_kernel(const QmvParams p) {
             }
     };
 
+    // The first row group's loads go out before the activations are read:
+    // they do not depend on them and are the long-latency (HBM) part.
     int it = blockIdx.x;
 #if GQ_QMV_CARRY
     if (it * SUBS < p.row_groups) load_group((it * SUBS + sub) * R);
 #endif
-    // ---- optional RMSNorm prologue (SafeC Gemma 4 DESIGN_NOTES page,
-    // "RMSNorm"): x <- x * (mean(x^2) + eps)^-1/2 * w, the weight multiplying
-    // directly. The scale is one scalar per activation vector, so the lanes
-    // fold only w into their registers now and apply the scalar to each
-    // finished row: y = inv * (W (x * w)). The sum of squares is taken from
-    // the raw x; the WS waves of a workgroup hold all of x, so it is a wave
-    // sum plus, for split rows, an LDS sum over the slices in fixed order.
+
+    // ---- activation registers for this lane's units ----------------------
+    // Optional RMSNorm prologue (SafeC Gemma 4 DESIGN_NOTES page, "RMSNorm"):
+    // x <- x * (mean(x^2) + eps)^-1/2 * w, the weight multiplying directly.
+    // The scale is one scalar per activation vector, so only w is folded into
+    // the activations here and the scalar multiplies each finished row:
+    // y = inv * (W (x * w)). The sum of squares is taken from the raw x.
+    float xr[(MODE == kQ8X) ? 1 : NI][(MODE == kQ8X) ? 1 : EPU];
+    uint32_t xqr[(MODE == kQ8X) ? NI : 1][(MODE == kQ8X) ? EPU / 4 : 1];
+    float dxr[NI];
+    int sxr[NI];
     float ss = 0.f;
-    if constexpr (MODE != kQ8X && FOLD) {
-        if (p.norm_w != nullptr) {
-#pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                const float4* ws4 = reinterpret_cast<const float4*>(
-                    p.norm_w + static_cast<uint32_t>(min(unit[i], p.units - 1)) * EPU);
-#pragma unroll
-                for (int v = 0; v < EPU / 4; ++v) {
-                    const float4 g = ws4[v];
-                    ss = fmaf(xr[i][4 * v + 0], xr[i][4 * v + 0], ss);
-                    ss = fmaf(xr[i][4 * v + 1], xr[i][4 * v + 1], ss);
-                    ss = fmaf(xr[i][4 * v + 2], xr[i][4 * v + 2], ss);
-                    ss = fmaf(xr[i][4 * v + 3], xr[i][4 * v + 3], ss);
-                    xr[i][4 * v + 0] *= g.x; xr[i][4 * v + 1] *= g.y;
-                    xr[i][4 * v + 2] *= g.z; xr[i][4 * v + 3] *= g.w;
+    bool norm = false;
+    if constexpr (MODE != kQ8X && FOLD) norm = p.norm_w != nullptr;
+    if constexpr (kStage) {
+        // Un-split rows: every wave of the workgroup needs all of x, so the
+        // workgroup reads it (and w) from memory once into LDS, padded to a
+        // pitch of EPU + 4 floats per unit so the lanes' 16-byte reads of
+        // consecutive units do not collide in a bank, and the waves copy
+        // their slices from there. Without this each wave re-reads the same
+        // few KiB, which for short matrices is more traffic than the weights.
+        const int nf4 = p.k >> 2;
+        for (int j = threadIdx.x; j < nf4; j += WAVES * kWave) {
+            float4 t = reinterpret_cast<const float4*>(p.x)[j];
+            if constexpr (FOLD) {
+                if (norm) {
+                    const float4 g = reinterpret_cast<const float4*>(p.norm_w)[j];
+                    ss = fmaf(t.x, t.x, ss); ss = fmaf(t.y, t.y, ss);
+                    ss = fmaf(t.z, t.z, ss); ss = fmaf(t.w, t.w, ss);
+                    t.x *= g.x; t.y *= g.y; t.z *= g.z; t.w *= g.w;
                 }
             }
+            const int e = j << 2;
+            *reinterpret_cast<float4*>(&xstage[(e / EPU) * kPitch + (e % EPU)]) = t;
         }
-    }
-    // the norm's scalar, while the first rows are in flight
-    float inv = 1.0f;
-    if constexpr (MODE != kQ8X && FOLD) {
-        if (p.norm_w != nullptr) {
-            ss = wave_sum(ss);
-            if constexpr (WS > 1) {
-                __shared__ float nss[WAVES];
+        if constexpr (FOLD) {
+            if (norm) {
+                ss = wave_sum(ss);
+                if (lane == 0) nss[wave] = ss;
+            }
+        }
+        __syncthreads();
+        if constexpr (FOLD) {
+            if (norm) {
+                float t = nss[0];
+#pragma unroll
+                for (int w = 1; w < WAVES; ++w) t += nss[w];
+                ss = t;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const float* xs = &xstage[uload[i] * kPitch];
+#pragma unroll
+            for (int v = 0; v < EPU / 4; ++v) {
+                const float4 t = *reinterpret_cast<const float4*>(xs + 4 * v);
+                xr[i][4 * v + 0] = uvalid[i] ? t.x : 0.f; xr[i][4 * v + 1] = uvalid[i] ? t.y : 0.f;
+                xr[i][4 * v + 2] = uvalid[i] ? t.z : 0.f; xr[i][4 * v + 3] = uvalid[i] ? t.w : 0.f;
+            }
+            dxr[i] = 0.f; sxr[i] = 0;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int e0 = unit[i] * EPU;
+            if constexpr (MODE != kQ8X) {
+                const float4* xs = reinterpret_cast<const float4*>(p.x + e0);
+#pragma unroll
+                for (int v = 0; v < EPU / 4; ++v) {
+                    const float4 t = uvalid[i] ? xs[v] : make_float4(0.f, 0.f, 0.f, 0.f);
+                    xr[i][4 * v + 0] = t.x; xr[i][4 * v + 1] = t.y;
+                    xr[i][4 * v + 2] = t.z; xr[i][4 * v + 3] = t.w;
+                }
+                dxr[i] = 0.f; sxr[i] = 0;
+            } else {
+                const uint4* xs = reinterpret_cast<const uint4*>(p.xq + e0);
+#pragma unroll
+                for (int v = 0; v < EPU / 16; ++v) {
+                    const uint4 t = uvalid[i] ? xs[v] : make_uint4(0u, 0u, 0u, 0u);
+                    xqr[i][4 * v + 0] = t.x; xqr[i][4 * v + 1] = t.y;
+                    xqr[i][4 * v + 2] = t.z; xqr[i][4 * v + 3] = t.w;
+                }
+                dxr[i] = uvalid[i] ? half_bits_to_float(p.xd[unit[i] >> SH]) : 0.f;
+                int sx = 0;
+                if constexpr (TYPE == kTypeQ4_0) {
+#pragma unroll
+                    for (int v = 0; v < EPU / 4; ++v) sx = dot4(xqr[i][v], 0x01010101u, sx);
+                }
+                sxr[i] = sx;
+            }
+        }
+        // split rows: the WS waves of a row group hold all of x between them,
+        // so the sum of squares is a wave sum plus an LDS sum over the slices
+        // in fixed order
+        if constexpr (MODE != kQ8X && FOLD) {
+            if (norm) {
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    const float4* ws4 = reinterpret_cast<const float4*>(p.norm_w + uload[i] * EPU);
+#pragma unroll
+                    for (int v = 0; v < EPU / 4; ++v) {
+                        const float4 g = ws4[v];
+                        ss = fmaf(xr[i][4 * v + 0], xr[i][4 * v + 0], ss);
+                        ss = fmaf(xr[i][4 * v + 1], xr[i][4 * v + 1], ss);
+                        ss = fmaf(xr[i][4 * v + 2], xr[i][4 * v + 2], ss);
+                        ss = fmaf(xr[i][4 * v + 3], xr[i][4 * v + 3], ss);
+                        xr[i][4 * v + 0] *= g.x; xr[i][4 * v + 1] *= g.y;
+                        xr[i][4 * v + 2] *= g.z; xr[i][4 * v + 3] *= g.w;
+                    }
+                }
+                ss = wave_sum(ss);
                 if (lane == 0) nss[wave] = ss;
                 __syncthreads();
                 float t = nss[sub * WS];
@@ -299,9 +340,28 @@ void qmv_kernel(const QmvParams p) {
                 for (int sl = 1; sl < WS; ++sl) t += nss[sub * WS + sl];
                 ss = t;
             }
-            inv = 1.0f / sqrtf(ss / static_cast<float>(p.k) + p.norm_eps);
         }
     }
+    float inv = 1.0f;
+    if constexpr (MODE != kQ8X && FOLD) {
+        if (norm) inv = 1.0f / sqrtf(ss / static_cast<float>(p.k) + p.norm_eps);
+    }
+
+    // ---- epilogue of one finished row: residual, soft cap, store, argmax --
+    unsigned long long best = 0ull;
+    auto emit = [&](int row, float v) {
+        if constexpr (FOLD) {
+            if (p.residual != nullptr) v += p.residual[row];
+            if (p.softcap > 0.0f) v = p.softcap * tanhf(v / p.softcap);
+        }
+        p.y[row] = v;
+        if constexpr (FOLD) {
+            const unsigned long long key = argmax_key(v, row);
+            best = key > best ? key : best;
+        }
+    };
+
+    __shared__ float lpart[WAVES][NMAT][R];
     for (; it * SUBS < p.row_groups; it += gridDim.x) {
         const int g = it * SUBS + sub;
         const int r0 = g * R;
