@@ -24,6 +24,19 @@ about 90 % of the step's bytes): algorithmic bytes per launch (weight
 blocks + x + y) / its average duration from HIP events recorded around each
 of its launches on the launch stream inside the timed region.
 
+Also reported beside ``value`` (none of them replaces it):
+  chained              the same step recorded once per weight set with
+                       gq_chain_* and replayed (one submission per step)
+  read_stream_ceiling  best bandwidth of a plain 16-byte read-and-XOR kernel
+                       (libgq_bench.so) over the 512 MiB vocab buffers;
+                       breakdown rows give their % of it
+  hot                  a 2048x2048 Q4_0 matvec re-launched on one copy
+                       (last-level-cache resident: a MALL figure, not HBM)
+  latency              the 64x256 Q8_0 matvec: a launch-latency point
+  cpu_baseline[_threads]  the fp64 oracle on one thread / on T threads with
+                       every matrix split by rows
+  breakdown, extras    per-launch medians from HIP events
+
 Modes:
   python bench.py [--steps K --warmup W]    the benchmark (one JSON line)
   python bench.py --mode pmc                 vocab kernel + a calibration copy
@@ -85,8 +98,11 @@ class Step:
         self.gq = gq
         L = gq.raw()
         dev = torch.device("cuda:0")
-        self.stream = torch.cuda.current_stream()
+        # a stream of its own (default priority): the step can then also be
+        # recorded as one chain, which the legacy default stream cannot
+        self.stream = torch.cuda.Stream()
         sp = ctypes.c_void_p(self.stream.cuda_stream)
+        self.sp = sp
         P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
 
         def up(a):
@@ -137,6 +153,7 @@ class Step:
             wv = pack(Q8, c4["w"], 262144, 2048)
             wt = {m: pack(Q4, c5["w"], 8192, 2048) for m in (8, 16, 32)}
             self.keep.append((w2a, w2b, wg, wu, wd, wv, wt))
+            self.vocab_qs = getattr(self, "vocab_qs", []) + [wv[0]]
             launches = [
                 ("quantize_q8_0 2048", L.gq_quantize_q8_0, (P(x2), 1, 2048, P(xq2), P(xd2), sp), 0, 2048 * 4 + 2048 + 128),
                 ("qmv_q4_0 2048x2048", L.gq_qmv_q4_0, (P(w2a[0]), P(w2a[1]), 2048, 2048, P(x2), P(y2a), sp),
@@ -170,6 +187,14 @@ class Step:
                 xq4, xd4 = (up(c5["acts"][8][0][:4].copy()), up(c5["acts"][8][1][:4].copy()))
                 y4t = torch.empty((4, 8192), dtype=torch.float32, device=dev)
                 self.keep += [g2, res2, y2c, logits, ws, idx, val, xq4, xd4, y4t]
+                # the smallest config (Q8_0 64 x 256): a launch-latency point
+                c1 = synth.workload_q8_0_small()
+                w1 = pack(Q8, c1["w"], 64, 256)
+                x1, y1 = up(c1["x"]), torch.empty(64, dtype=torch.float32, device=dev)
+                self.keep += [w1, x1, y1]
+                self.latency = ("qmv_q8_0 64x256", L.gq_qmv_q8_0, (P(w1[0]), P(w1[1]), 64, 256, P(x1), P(y1), sp))
+                self.hot = ("qmv_q4_0 2048x2048", L.gq_qmv_q4_0,
+                            (P(w2a[0]), P(w2a[1]), 2048, 2048, P(x2), P(y2a), sp), 2048 * 64 * 18)
                 self.extras = [
                     ("qmv_q4_0_ex 2048x2048 (rmsnorm + residual)", L.gq_qmv_q4_0_ex,
                      (P(w2a[0]), P(w2a[1]), 2048, 2048, P(x2), P(g2), ctypes.c_float(1e-6), P(res2), P(y2c), sp),
@@ -191,6 +216,18 @@ class Step:
         self.other_bytes = {l[0]: l[4] for l in self.sets[0]}
         self.step_weight_bytes = sum(self.weight_bytes.values())
 
+    def record_chains(self):
+        """One recorded chain per weight set: the whole step as one graph."""
+        self.chains = []
+        for i in range(len(self.sets)):
+            c = self.gq.Chain(self.stream)
+            with c:
+                self.run(i)
+            self.chains.append(c)
+
+    def replay(self, i):
+        self.chains[i % len(self.chains)].launch(self.stream)
+
     def run(self, i, events=None):
         """Enqueue step i; events maps a launch name to a list collecting
         (start, end) event pairs recorded around that launch."""
@@ -206,6 +243,63 @@ class Step:
                 st = fn(*args)
             if st != 0:
                 raise self.gq.GQError(st, name)
+
+
+def _event_times(step, fn, fargs, reps):
+    """Per-launch durations (us, sorted) from HIP events around each launch."""
+    torch = step.torch
+    evs = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(step.stream)
+        if fn(*fargs) != 0:
+            raise RuntimeError("launch failed")
+        b.record(step.stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+
+
+def read_stream_ceiling(step, log):
+    """Best bandwidth of a plain 16-byte non-temporal read-and-XOR kernel
+    (libgq_bench.so) over the rotated vocab quant buffers (512 MiB each, so
+    consecutive launches never hit in the last-level cache)."""
+    import ctypes
+
+    torch = step.torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "gguf_block_quant_amd", "libgq_bench.so"))
+    lib.gqb_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_void_p]
+    lib.gqb_read_stream.restype = ctypes.c_int
+    bufs = step.vocab_qs
+    nbytes = bufs[0].numel() * bufs[0].element_size()
+    grids = (256, 512, 1024, 2048)
+    out = torch.empty(max(grids) * 256, dtype=torch.int32, device="cuda")
+    best = (0.0, 0, 0)
+    for g, pattern in [(g, pt) for g in grids for pt in (0, 1)]:
+        def launch(i):
+            return lib.gqb_read_stream(ctypes.c_void_p(bufs[i % len(bufs)].data_ptr()), nbytes,
+                                       ctypes.c_void_p(out.data_ptr()), g, pattern, step.sp)
+        for i in range(2):
+            if launch(i) != 0:
+                raise RuntimeError("read-stream launch failed")
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        reps = 8
+        a.record(step.stream)
+        for i in range(reps):
+            launch(i)
+        b.record(step.stream)
+        torch.cuda.synchronize()
+        gbps = nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+        best = max(best, (gbps, g, pattern))
+    log("read-stream ceiling %.0f GB/s (grid %d, shape %d)" % best)
+    return {"GBps": round(best[0], 1), "grid": best[1],
+            "shape": ("lane grid-stride", "wave 8 KiB chunks")[best[2]], "bytes_per_launch": nbytes,
+            "kernel": "16-byte non-temporal loads, XOR-reduce, 256-thread workgroups; best of 4 grids x 2 "
+                      "access shapes"}
 
 
 # ----------------------------------------------------------------------------
@@ -248,6 +342,61 @@ def cpu_baseline(host, weight_bytes_per_step, seconds, log):
                   "single-threaded fp64 C oracle, %.1f s; weight-block bytes / time" % (passes, el),
         "seconds_per_step": round(el / passes, 3),
         "cpu": platform.processor() or platform.machine(),
+    }
+
+
+def cpu_baseline_threads(host, weight_bytes_per_step, seconds, log):
+    """The same oracle calls with every matrix split by rows into T contiguous
+    chunks run on T threads (a chunk never splits a dot product; the C
+    oracle runs without the interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    c2, c3, c4, c5 = host["c2"], host["c3"], host["c4"], host["c5"]
+    Q4, Q8 = oracle.TYPE_Q4_0, oracle.TYPE_Q8_0
+    T = max(1, min(os.cpu_count() or 1, 16))
+    pool = ThreadPoolExecutor(T)
+
+    def split(n):
+        step = (n + T - 1) // T
+        return [(r, min(n, r + step)) for r in range(0, n, step)]
+
+    def rows(fn, w, n, *a):
+        list(pool.map(lambda rr: fn(w[rr[0]:rr[1]], rr[1] - rr[0], *a), split(n)))
+
+    def one_pass():
+        rows(lambda w, n, k, x: oracle.matvec(Q4, w, n, k, x), c2["w"], 2048, 2048, c2["x"])
+        xq, xd = oracle.quantize_q8_0(c2["x"])
+        rows(lambda w, n, k: oracle.blockdots(Q4, w, n, k, xq, xd, want_s=False), c2["w"], 2048, 2048)
+        hs = list(pool.map(lambda rr: oracle.ffn_gate_up(Q4, c3["wg"][rr[0]:rr[1]], c3["wu"][rr[0]:rr[1]],
+                                                         rr[1] - rr[0], 2048, c3["x"])["h"], split(8192)))
+        import numpy as np
+        h = np.concatenate(hs)
+        rows(lambda w, n, k: oracle.matvec(Q4, w, n, k, h), c3["wd"], 2048, 8192)
+        rows(lambda w, n, k: oracle.matvec(Q8, w, n, k, c4["x"]), c4["w"], 262144, 2048)
+        for m in (8, 16, 32):
+            rows(lambda w, n, k: oracle.blockdots(Q4, w, n, k, c5["acts"][m][0], c5["acts"][m][1], want_s=False),
+                 c5["w"], 8192, 2048)
+
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        one_pass()
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    pool.shutdown()
+    log("oracle on %d threads: %d pass(es) in %.1fs" % (T, passes, el))
+    return {
+        "value": round(weight_bytes_per_step * passes / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": T,
+        "kind": "oracle",
+        "sample": "%d full pass(es) of the step's workload through the fp64 C oracle, every matrix split "
+                  "by rows over %d threads, %.1f s" % (passes, T, el),
+        "seconds_per_step": round(el / passes, 3),
     }
 
 
@@ -448,10 +597,42 @@ def main():
         extras[name] = {"median_us": round(med, 2), "weight_bytes": wb,
                         "weight_GBps": round(wb / med / 1e3, 1), "total_GBps": round((wb + ob) / med / 1e3, 1)}
 
+    # the same step recorded as one chain per weight set and replayed
+    # (decode-step chaining: one submission per step instead of 9 launches)
+    step.record_chains()
+    for i in range(args.warmup):
+        step.replay(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step.replay(i)
+    torch.cuda.synchronize()
+    chained_s = (time.perf_counter() - t0) / args.steps
+    chained = {"ms_per_step": round(chained_s * 1e3, 4),
+               "value": round(step.step_weight_bytes / chained_s / 1e9, 2), "unit": "GB/s",
+               "launches_per_replay": step.chains[0].launches, "replays_timed": args.steps}
+
+    ceiling = read_stream_ceiling(step, log)
+    for n, b in breakdown.items():
+        if b["weight_GBps"]:
+            b["pct_of_read_ceiling"] = round(100.0 * b["total_GBps"] / ceiling["GBps"], 1)
+
+    # MALL-hot: one small matrix launched back to back (served from the
+    # 256 MB last-level cache after the first launch; never an HBM figure)
+    name, fn, fargs, wb = step.hot
+    us = _event_times(step, fn, fargs, 100)
+    hot = {"kernel": name, "median_us": round(us[len(us) // 2], 2),
+           "MALL_GBps": round(wb / us[len(us) // 2] / 1e3, 1)}
+    name, fn, fargs = step.latency
+    us = _event_times(step, fn, fargs, 100)
+    latency = {"kernel": name, "median_us": round(us[len(us) // 2], 2), "min_us": round(us[0], 2),
+               "note": "launch-latency point (17,408 weight bytes), not a roofline point"}
+
     traffic = load_traffic()
-    cpu = None
+    cpu = cpu_threads = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(step.host, step.step_weight_bytes, args.cpu_seconds, log)
+        cpu_threads = cpu_baseline_threads(step.host, step.step_weight_bytes, args.cpu_seconds / 2, log)
 
     out = {
         "metric": METRIC,
@@ -489,6 +670,15 @@ def main():
             "launches_timed": len(dom_ms),
         },
         "cpu_baseline": cpu,
+        "cpu_baseline_threads": cpu_threads,
+        "chained": chained,
+        "read_stream_ceiling": ceiling,
+        "hot": hot,
+        "latency": latency,
+        "tokens_per_s_projection": {
+            "value": round(value / 0.783, 1),
+            "note": "effective GB/s / 0.783 GB per token (the byte budget per decoded token quoted "
+                    "for the int2/int4/int8 Gemma-4-E2B port); context only"},
         "breakdown": breakdown,
         "extras": extras,
     }

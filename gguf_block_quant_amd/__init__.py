@@ -55,6 +55,11 @@ _SIGS = {
     "gq_qmv_q8_0_argmax": ([_P, _P, _I64, _I64, _P, _P, _F, _F, _P, _P, ctypes.c_size_t, _P, _P, _P], _I),
     "gq_qmv_q4_0_argmax": ([_P, _P, _I64, _I64, _P, _P, _F, _F, _P, _P, ctypes.c_size_t, _P, _P, _P], _I),
     "gq_qmm_tile_m": ([_P, _P, _I64, _I64, _I, _P, _P, _P, _P, _P], _I),
+    "gq_chain_begin": ([_P], _I),
+    "gq_chain_end": ([_P, ctypes.POINTER(_P)], _I),
+    "gq_chain_launch": ([_P, _P], _I),
+    "gq_chain_destroy": ([_P], _I),
+    "gq_chain_launches": ([_P], ctypes.c_size_t),
 }
 _handle = None
 
@@ -231,14 +236,16 @@ def argmax_workspace_bytes() -> int:
     return raw().gq_argmax_workspace_bytes()
 
 
-def _qmv_argmax(fn, qs, d, n, k, x, norm_weight, norm_eps, softcap, logits, workspace, stream):
+def _qmv_argmax(fn, qs, d, n, k, x, norm_weight, norm_eps, softcap, logits, workspace, index, value, stream):
     torch = _torch()
     if logits is None:
         logits = _like(x, (n,), torch.float32)
     if workspace is None:
         workspace = _like(x, (argmax_workspace_bytes(),), torch.uint8)
-    index = _like(x, (1,), torch.int32)
-    value = _like(x, (1,), torch.float32)
+    if index is None:
+        index = _like(x, (1,), torch.int32)
+    if value is None:
+        value = _like(x, (1,), torch.float32)
     _call(fn, _ptr(qs, "qs"), _ptr(d, "d"), n, k, _ptr(x, "x"), _ptr(norm_weight, "norm_weight"),
           float(norm_eps), float(softcap), _ptr(logits, "logits"), _ptr(workspace, "workspace"),
           workspace.numel() * workspace.element_size(), _ptr(index, "index"), _ptr(value, "value"),
@@ -247,16 +254,16 @@ def _qmv_argmax(fn, qs, d, n, k, x, norm_weight, norm_eps, softcap, logits, work
 
 
 def qmv_q8_0_argmax(qs, d, n, k, x, norm_weight=None, norm_eps=1e-6, softcap=30.0, logits=None,
-                    workspace=None, stream=None):
+                    workspace=None, index=None, value=None, stream=None):
     """Vocabulary head: returns (index int32[1], value fp32[1], logits fp32[n])."""
     return _qmv_argmax("gq_qmv_q8_0_argmax", qs, d, n, k, x, norm_weight, norm_eps, softcap, logits,
-                       workspace, stream)
+                       workspace, index, value, stream)
 
 
 def qmv_q4_0_argmax(qs, d, n, k, x, norm_weight=None, norm_eps=1e-6, softcap=30.0, logits=None,
-                    workspace=None, stream=None):
+                    workspace=None, index=None, value=None, stream=None):
     return _qmv_argmax("gq_qmv_q4_0_argmax", qs, d, n, k, x, norm_weight, norm_eps, softcap, logits,
-                       workspace, stream)
+                       workspace, index, value, stream)
 
 
 def qffn_gate_up_gelu_ex(g_qs, g_d, u_qs, u_d, n_ff, k, x, norm_weight=None, norm_eps=1e-6, h=None,
@@ -286,3 +293,50 @@ def qmm_tile_m(qs, d, n, k, m, xq, xd, y=None, blockdots=None, stream=None):
     _call("gq_qmm_tile_m", _ptr(qs, "qs"), _ptr(d, "d"), n, k, m, _ptr(xq, "xq"), _ptr(xd, "xd"),
           _ptr(y, "y"), _ptr(blockdots, "blockdots"), _stream(stream))
     return y
+
+
+class Chain:
+    """A recorded decode step (gq_chain_*). Launches issued on ``stream``
+    inside ``with chain:`` are recorded rather than run; ``launch()`` then
+    replays the whole sequence as one graph. The stream must not be the
+    legacy default stream. Outputs must be allocated before recording and
+    kept alive (and their pointers unchanged) for as long as the chain is
+    replayed; update inputs in place between replays."""
+
+    def __init__(self, stream=None):
+        torch = _torch()
+        self._stream_obj = stream if stream is not None else torch.cuda.current_stream()
+        self._handle = ctypes.c_void_p()
+        self._recording = False
+
+    def __enter__(self):
+        _call("gq_chain_begin", _stream(self._stream_obj))
+        self._recording = True
+        return self
+
+    def __exit__(self, exc_type, exc, tb):
+        self._recording = False
+        st = raw().gq_chain_end(_stream(self._stream_obj), ctypes.byref(self._handle))
+        if st != GQ_OK and exc_type is None:
+            raise GQError(st, "gq_chain_end")
+        return False
+
+    @property
+    def launches(self) -> int:
+        return raw().gq_chain_launches(self._handle)
+
+    def launch(self, stream=None):
+        if not self._handle:
+            raise RuntimeError("chain has not been recorded")
+        _call("gq_chain_launch", self._handle, _stream(stream if stream is not None else self._stream_obj))
+
+    def close(self):
+        if self._handle:
+            h, self._handle = self._handle, ctypes.c_void_p()
+            _call("gq_chain_destroy", h)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -17,6 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgq.so")
+BENCH_LIB = os.path.join(HERE, "libgq_bench.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -72,7 +73,19 @@ def build(verbose: bool = False) -> str:
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
     subprocess.check_call(cmd)
     os.replace(tmp, LIB)
+    build_bench_helpers()
     return LIB
+
+
+def build_bench_helpers() -> str:
+    """libgq_bench.so: measurement kernels the benchmark uses beside libgq
+    (the read-stream ceiling); not part of the library's API."""
+    srcs = sorted(glob.glob(os.path.join(CSRC, "bench", "*.hip")))
+    tmp = BENCH_LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call([HIPCC, *COMPILE_FLAGS, "-shared", "-o", tmp, *srcs],
+                          stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+    os.replace(tmp, BENCH_LIB)
+    return BENCH_LIB
 
 
 if __name__ == "__main__":

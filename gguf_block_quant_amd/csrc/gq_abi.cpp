@@ -1,10 +1,14 @@
 // gq_abi.cpp -- the extern "C" boundary of libgq (declared in include/gq.h).
 // Every entry point validates all of its arguments on the host, before any
-// HIP call, then enqueues its kernel(s) on the caller's stream. No
-// allocation, no synchronisation, no global state.
+// HIP call, then enqueues its kernel(s) on the caller's stream. No device
+// allocation, no synchronisation, no global state; the chaining entries own
+// one host-side graph object per recorded chain.
 #include "../../include/gq.h"
 
 #include <hip/hip_runtime.h>
+
+#include <new>
+#include <vector>
 
 #include "gq_launch.hpp"
 
@@ -301,5 +305,71 @@ int gq_qmm_tile_m(const uint8_t* qs, const uint16_t* d, int64_t n, int64_t k, in
     if (any_alias(outs, ins)) return GQ_ERR_ALIAS;
     return status_of(gq::launch_tile_q4_0(qs, d, n, k, m, xq, xd, y, blockdots, as_stream(stream)));
 }
+
+}  // extern "C"
+
+// ---- decode-step chaining: stream capture into one executable HIP graph ----
+struct gq_chain {
+    hipGraphExec_t exec;
+    size_t launches;     // kernel nodes recorded
+};
+
+extern "C" {
+
+int gq_chain_begin(void* stream) {
+    if (stream == nullptr) return GQ_ERR_VALUE;
+    // relaxed: the caller may interleave its own (unrecorded) host-side HIP
+    // calls, e.g. allocations, while the step is being recorded
+    return status_of(hipStreamBeginCapture(as_stream(stream), hipStreamCaptureModeRelaxed));
+}
+
+int gq_chain_end(void* stream, gq_chain** chain) {
+    if (stream == nullptr) return GQ_ERR_VALUE;
+    if (chain == nullptr) return GQ_ERR_NULL;
+    *chain = nullptr;
+    hipGraph_t graph = nullptr;
+    hipError_t e = hipStreamEndCapture(as_stream(stream), &graph);
+    if (e != hipSuccess) {
+        if (graph != nullptr) hipGraphDestroy(graph);
+        return status_of(e);
+    }
+    size_t count = 0;
+    e = hipGraphGetNodes(graph, nullptr, &count);
+    size_t kernels = 0;
+    if (e == hipSuccess && count > 0) {
+        std::vector<hipGraphNode_t> nodes(count);
+        e = hipGraphGetNodes(graph, nodes.data(), &count);
+        for (size_t i = 0; e == hipSuccess && i < count; ++i) {
+            hipGraphNodeType t;
+            e = hipGraphNodeGetType(nodes[i], &t);
+            if (e == hipSuccess && t == hipGraphNodeTypeKernel) ++kernels;
+        }
+    }
+    hipGraphExec_t exec = nullptr;
+    if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    hipGraphDestroy(graph);
+    if (e != hipSuccess) return status_of(e);
+    gq_chain* c = new (std::nothrow) gq_chain{exec, kernels};
+    if (c == nullptr) {
+        hipGraphExecDestroy(exec);
+        return status_of(hipErrorOutOfMemory);
+    }
+    *chain = c;
+    return status_of(hipSuccess);
+}
+
+int gq_chain_launch(const gq_chain* chain, void* stream) {
+    if (chain == nullptr) return GQ_ERR_NULL;
+    return status_of(hipGraphLaunch(chain->exec, as_stream(stream)));
+}
+
+int gq_chain_destroy(gq_chain* chain) {
+    if (chain == nullptr) return GQ_OK;
+    const hipError_t e = hipGraphExecDestroy(chain->exec);
+    delete chain;
+    return status_of(e);
+}
+
+size_t gq_chain_launches(const gq_chain* chain) { return chain == nullptr ? 0 : chain->launches; }
 
 }  // extern "C"

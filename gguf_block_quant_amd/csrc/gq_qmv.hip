@@ -32,6 +32,9 @@
 #ifndef GQ_QMV_WAVES1
 #define GQ_QMV_WAVES1 4        // waves per workgroup for un-split rows (they share one LDS copy of x)
 #endif
+#ifndef GQ_QMV_R_TALL
+#define GQ_QMV_R_TALL 4        // rows per wave step for tall (n >= 65536) un-split matrices
+#endif
 #ifndef GQ_QMV_NT
 #define GQ_QMV_NT 1            // non-temporal loads for the quant stream (read once)
 #endif
@@ -553,7 +556,7 @@ hipError_t launch_cfg(QmvParams p, hipStream_t stream, int* grid_out) {
     } else if constexpr (WS >= 4) {
         return launch_rows<TYPE, MODE, NI, WS, 8>(p, stream, grid_out);
     } else {
-        if (p.n >= 65536) return launch_rows<TYPE, MODE, NI, WS, 4>(p, stream, grid_out);
+        if (p.n >= 65536) return launch_rows<TYPE, MODE, NI, WS, GQ_QMV_R_TALL>(p, stream, grid_out);
         return launch_rows<TYPE, MODE, NI, WS, 2>(p, stream, grid_out);
     }
 }

@@ -41,7 +41,18 @@ constexpr int kWPitch = kChunk * 16 + 16;          // weight row bytes in LDS (m
 constexpr int kXPitch = kChunk * 32 + 32;          // activation row bytes in LDS (mod 256 = 32)
 constexpr int kRows = 16;                          // weight rows per workgroup
 constexpr int kWavePart = kChunk / kWavesPerBlock; // blocks per wave per chunk
-constexpr int kBatch = 4;                          // MFMAs issued before their epilogues
+#ifndef GQ_TILE_BATCH
+#define GQ_TILE_BATCH 8
+#endif
+#ifndef GQ_TILE_BATCH2
+#define GQ_TILE_BATCH2 4
+#endif
+#ifndef GQ_TILE_JB_UNROLL
+#define GQ_TILE_JB_UNROLL 1
+#endif
+// blocks whose MFMAs issue before their epilogues (smaller for two row tiles,
+// whose batches carry twice the scales and results)
+template <int MT> struct Batch { static constexpr int value = MT == 1 ? GQ_TILE_BATCH : GQ_TILE_BATCH2; };
 
 // 8 unsigned nibbles (4 bytes) -> 8 signed bytes q - 8:
 // (q + 120) ^ 0x80 per byte is q - 8 in two's complement; q + 120 <= 135
@@ -162,12 +173,25 @@ void tile_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
         if (cb + kChunk < nb)
             stage_load<MT>(st, tid, cb + kChunk, min(kChunk, nb - cb - kChunk), n0, n, nb, m, k, qs, d, xq, xd);
 
-        // this wave's blocks of the chunk, kBatch at a time: MFMAs first,
-        // then their epilogues (the MFMA latency hides behind the batch)
+        // this wave's blocks of the chunk, kBatch at a time: the batch's
+        // scales are read from LDS first, then its MFMAs are issued, then
+        // their epilogues run (LDS and MFMA latency hide behind the batch).
+        // Blocks past the end of k need no branch: their staged weights and
+        // both scales are zero, so they add exactly 0.
         const int b0 = wave * kWavePart;
-#pragma unroll
+        constexpr int kBatch = Batch<MT>::value;
+#pragma unroll GQ_TILE_JB_UNROLL
         for (int jb = 0; jb < kWavePart; jb += kBatch) {
             int32x4_t S[kBatch][MT];
+            float dwv[kBatch];
+            float4 dxv[kBatch][MT];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int bl = b0 + jb + j;
+                dwv[j] = dws[bl][c];
+#pragma unroll
+                for (int t = 0; t < MT; ++t) dxv[j][t] = *reinterpret_cast<const float4*>(&dxs[bl][16 * t + 4 * s]);
+            }
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
                 const int bl = b0 + jb + j;
@@ -184,17 +208,12 @@ void tile_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
             }
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
-                const int bl = b0 + jb + j;
-                if (bl < cn) {
-                    const float dw = dws[bl][c];
 #pragma unroll
-                    for (int t = 0; t < MT; ++t) {
-                        const float4 dx = *reinterpret_cast<const float4*>(&dxs[bl][16 * t + 4 * s]);
-                        const float dxv[4] = {dx.x, dx.y, dx.z, dx.w};
+                for (int t = 0; t < MT; ++t) {
+                    const float dx[4] = {dxv[j][t].x, dxv[j][t].y, dxv[j][t].z, dxv[j][t].w};
 #pragma unroll
-                        for (int v = 0; v < 4; ++v)
-                            acc[t][v] = fmaf(dw * dxv[v], static_cast<float>(S[j][t][v]), acc[t][v]);
-                    }
+                    for (int v = 0; v < 4; ++v)
+                        acc[t][v] = fmaf(dwv[j] * dx[v], static_cast<float>(S[j][t][v]), acc[t][v]);
                 }
             }
             if (blockdots != nullptr) {

@@ -40,7 +40,7 @@
  * Conventions for every entry point:
  *  - Pointers named qs, d, x, y, h, xq, xd, blockdots and blocks are DEVICE
  *    pointers on the current HIP device. The caller allocates and frees all
- *    of them; libgq never allocates, frees or synchronises.
+ *    of them; libgq never allocates device memory, frees or synchronises.
  *  - Inputs are read-only. Outputs are fully overwritten.
  *  - stream is a hipStream_t passed as void*; NULL is the default stream.
  *    Work is enqueued asynchronously on that stream.
@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define GQ_ABI_VERSION 2
+#define GQ_ABI_VERSION 3
 
 enum {
     GQ_OK = 0,
@@ -135,7 +135,7 @@ int gq_quantize_q8_0(const float *x, int64_t m, int64_t k,
  * y[r] = sum_c w[r][c] * x[c] for r < n, accumulated in fp32.
  * Accuracy: |y - y_exact| <= 1e-4 * sum_c |w[r][c] x[c]| + 1e-6.
  * qs/d packed as above; x fp32 [k]; y fp32 [n].
- * Maximum k: 32768 (Q8_0), 65536 (Q4_0).
+ * Maximum k: 32768 (GQ_ERR_UNSUPPORTED beyond it).
  */
 int gq_qmv_q8_0(const int8_t *qs, const uint16_t *d, int64_t n, int64_t k,
                 const float *x, float *y, void *stream);
@@ -213,7 +213,7 @@ int gq_qmv_q4_0_q8(const uint8_t *qs, const uint16_t *d, int64_t n, int64_t k,
  * it saturates (finite t never gives NaN). x fp32 [k]; h fp32 [n_ff].
  * The down projection is a separate gq_qmv_q4_0(Wd, h) call: every row of
  * it needs all of h. A fused [gate | up] weight is passed as two pointers
- * into it. Maximum k: 65536.
+ * into it. Maximum k: 32768.
  */
 int gq_qffn_gate_up_gelu(const uint8_t *g_qs, const uint16_t *g_d,
                          const uint8_t *u_qs, const uint16_t *u_d,
@@ -243,6 +243,41 @@ int gq_qffn_gate_up_gelu_ex(const uint8_t *g_qs, const uint16_t *g_d,
 int gq_qmm_tile_m(const uint8_t *qs, const uint16_t *d, int64_t n, int64_t k, int m,
                   const int8_t *xq, const uint16_t *xd, float *y,
                   int32_t *blockdots, void *stream);
+
+/*
+ * Decode-step chaining. A decode step is a fixed sequence of many small
+ * launches over different weights; replaying it as one recorded unit
+ * removes the per-launch host cost and the host round trips between them
+ * (raw-Metal port page, "Architecture", host-loop bullet: steps encoded
+ * several per command buffer, token dependence kept on the GPU; TensorSharp
+ * Gemma 4 page, fused decode: the whole layer stack as one graph dispatch).
+ *
+ * gq_chain_begin(stream) starts recording on stream: from then until
+ * gq_chain_end on the same stream, launches enqueued on it by the calling
+ * thread -- libgq entry points and the caller's own kernels alike -- are
+ * recorded, not executed, and the entry points still validate and return
+ * their status as usual. gq_chain_end(stream, &chain) stops recording and
+ * turns the sequence into an executable HIP graph; gq_chain_launch(chain,
+ * stream) enqueues one replay of it on any stream of the same device, with
+ * the pointers and sizes fixed at recording time (update the buffers' CONTENTS
+ * between replays, e.g. a new x, never the pointers). gq_chain_destroy frees
+ * it (NULL is a no-op); the caller must not destroy a chain whose replay may
+ * still be running. gq_chain_launches reports the kernel launches recorded.
+ *
+ * The chain object is host memory owned by libgq between gq_chain_end and
+ * gq_chain_destroy (the only allocation libgq makes; no device memory).
+ * stream must not be NULL (the legacy default stream cannot be recorded):
+ * GQ_ERR_VALUE. A HIP failure while recording (e.g. the stream is already
+ * recording, or a call that cannot be recorded was made on it) gives
+ * GQ_ERR_LAUNCH with gq_last_hip_error() holding the HIP code; a failed
+ * gq_chain_end leaves the stream not recording and *chain NULL.
+ */
+typedef struct gq_chain gq_chain;
+int gq_chain_begin(void *stream);
+int gq_chain_end(void *stream, gq_chain **chain);
+int gq_chain_launch(const gq_chain *chain, void *stream);
+int gq_chain_destroy(gq_chain *chain);
+size_t gq_chain_launches(const gq_chain *chain);
 
 #ifdef __cplusplus
 }

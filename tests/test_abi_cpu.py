@@ -40,7 +40,7 @@ def test_header_symbols_all_exported():
 
 
 def test_version_and_status_strings():
-    assert gq.abi_version() == 2
+    assert gq.abi_version() == 3
     for s in range(8):
         assert gq.status_str(s)
     assert gq.status_str(99) == "unknown status"
@@ -164,3 +164,14 @@ def test_ffn_ex_validation():
     assert f(A, B, C, E, 64, 256, D, NW, -1e-6, 0x61000000, None) == VALUE
     assert f(A, B, C, E, 64, 256, D, NW + 8, 1e-6, 0x61000000, None) == ALIGN
     assert f(A, B, C, E, 64, 256, D, NW, 1e-6, NW + 128, None) == ALIAS
+
+
+def test_chain_validation():
+    """Decode-step chaining: argument checks that precede any HIP call."""
+    h = ctypes.c_void_p()
+    assert L.gq_chain_begin(None) == VALUE                 # the legacy stream cannot be recorded
+    assert L.gq_chain_end(None, ctypes.byref(h)) == VALUE
+    assert L.gq_chain_end(ctypes.c_void_p(A), None) == NULL
+    assert L.gq_chain_launch(None, ctypes.c_void_p(A)) == NULL
+    assert L.gq_chain_destroy(None) == OK                  # like free(NULL)
+    assert L.gq_chain_launches(None) == 0
