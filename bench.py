@@ -423,6 +423,80 @@ def pmc_mode(args, log):
     log("pmc pass done: 3 x %s, 3 x copy of %d bytes" % (name, COPY_BYTES))
 
 
+def pmc_step_mode(args, log):
+    """Three steps (every launch of the step, 3 times), for the VALU and
+    MFMA counter passes."""
+    import torch
+
+    step = Step(1, log)
+    torch.cuda.synchronize()
+    for i in range(3):
+        step.run(i)
+    torch.cuda.synchronize()
+    log("pmc pass done: 3 steps of %d launches" % len(step.names))
+
+
+COUNTERS_FILE = os.path.join(PROFILES, "decode_step_valu_mfma_counters.txt")
+CU_NUM, SIMD_NUM, XCD_NUM = 256, 1024, 8
+
+
+def counters_summary(args):
+    """VALU busy and MFMA utilisation per kernel of the step from two
+    rocprofv3 --pmc runs of ``--mode pmc-step``: run A with
+    SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_I8 GRBM_GUI_ACTIVE, run B
+    with SQ_ACTIVE_INST_VALU SQ_INSTS_VALU GRBM_GUI_ACTIVE. VALU busy =
+    SQ_ACTIVE_INST_VALU / CU count / GRBM_GUI_ACTIVE; MFMA utilisation =
+    SQ_VALU_MFMA_BUSY_CYCLES / (SIMD count x GRBM_GUI_ACTIVE), where the
+    csv's GRBM_GUI_ACTIVE is summed over the 8 XCDs and so divided by 8 to get
+    the busy cycles of one (the profiler's own derived metrics take the max
+    over XCDs)."""
+    dir_a, dir_b = args.counters_summary.split(",")
+
+    def per_kernel(run_dir, names):
+        out = {}
+        for name in names:
+            for kern, grid, val in _read_counter(run_dir, name):
+                key = (kern, grid)
+                out.setdefault(key, {}).setdefault(name, []).append(val)
+        return out
+
+    a = per_kernel(dir_a, ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_I8", "GRBM_GUI_ACTIVE"))
+    b = per_kernel(dir_b, ("SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU", "GRBM_GUI_ACTIVE"))
+    avg = lambda v: sum(v) / len(v)  # noqa: E731
+    lines = [
+        "# VALU and MFMA counters per kernel of one decode step (bench.py --mode pmc-step: 3 steps), MI355X",
+        "# commands (repository root R on the GPU host; one pass per run):",
+        "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_I8 \\",
+        "#       GRBM_GUI_ACTIVE -d $R/%s -o run --output-format csv -- python3 $R/bench.py --mode pmc-step" % dir_a,
+        "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc SQ_ACTIVE_INST_VALU SQ_INSTS_VALU GRBM_GUI_ACTIVE \\",
+        "#       -d $R/%s -o run --output-format csv -- python3 $R/bench.py --mode pmc-step" % dir_b,
+        "#   python3 bench.py --counters-summary %s,%s --write-profile" % (dir_a, dir_b),
+        "# valu_busy = SQ_ACTIVE_INST_VALU / %d CUs / G; mfma_util = SQ_VALU_MFMA_BUSY_CYCLES / (%d SIMDs x G);"
+        % (CU_NUM, SIMD_NUM),
+        "# G = GRBM_GUI_ACTIVE / %d (the csv sums it over the XCDs); mfma_i8_mops = SQ_INSTS_VALU_MFMA_MOPS_I8"
+        % XCD_NUM,
+        "# kernel_source_hash = %s" % kernel_source_hash(),
+        "%-58s %6s %9s %9s %11s %12s" % ("kernel", "grid", "valu_busy", "mfma_util", "valu_insts", "mfma_i8_mops"),
+    ]
+    for key in sorted(set(a) | set(b), key=lambda kg: kg[0]):
+        kern, grid = key
+        label = next((lab for k, lab in KERNEL_LABELS if k in kern), kern[:58])
+        va, vb = a.get(key, {}), b.get(key, {})
+        busy = util = insts = mops = float("nan")
+        if "SQ_ACTIVE_INST_VALU" in vb:
+            busy = 100.0 * avg(vb["SQ_ACTIVE_INST_VALU"]) / CU_NUM / (avg(vb["GRBM_GUI_ACTIVE"]) / XCD_NUM)
+            insts = avg(vb["SQ_INSTS_VALU"])
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in va:
+            util = 100.0 * avg(va["SQ_VALU_MFMA_BUSY_CYCLES"]) / (SIMD_NUM * avg(va["GRBM_GUI_ACTIVE"]) / XCD_NUM)
+            mops = avg(va["SQ_INSTS_VALU_MFMA_MOPS_I8"])
+        lines.append("%-58s %6d %8.1f%% %8.2f%% %11.0f %12.0f" % (label, grid, busy, util, insts, mops))
+    text = "\n".join(lines) + "\n"
+    print(text)
+    if args.write_profile:
+        with open(COUNTERS_FILE, "w") as f:
+            f.write(text)
+
+
 def _read_counter(run_dir, counter):
     """Per-dispatch values of one counter from a rocprofv3 counter_collection.csv."""
     files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
@@ -484,6 +558,78 @@ def pmc_summary(args):
             f.write(text)
 
 
+STATS_FILE = os.path.join(PROFILES, "decode_step_kernel_stats.txt")
+
+# what each kernel instantiation is in the default run
+KERNEL_LABELS = [
+    ("qmv_kernel<8, 0, 2, 1, 4, false>", "qmv Q8_0 fp32 x: vocab 262144x2048"),
+    ("qmv_kernel<8, 0, 2, 1, 4, true>", "qmv Q8_0 + rmsnorm + softcap + argmax stage 1: vocab"),
+    ("argmax_reduce_kernel", "argmax stage 2 (one workgroup)"),
+    ("qmv_kernel<2, 2, 1, 1, 2, false>", "FFN gate+up GELU: 2 x 8192x2048 Q4_0"),
+    ("qmv_kernel<2, 2, 1, 1, 2, true>", "FFN gate+up GELU + rmsnorm"),
+    ("qmv_kernel<2, 0, 1, 4, 8, false>", "qmv Q4_0 fp32 x: down 2048x8192"),
+    ("qmv_kernel<2, 0, 1, 1, 2, false>", "qmv Q4_0 fp32 x: 2048x2048 (step + MALL-hot runs)"),
+    ("qmv_kernel<2, 0, 1, 1, 2, true>", "qmv Q4_0 + rmsnorm + residual: 2048x2048"),
+    ("qmv_kernel<2, 1, 1, 1, 2, false>", "qmv Q4_0 Q8_0 x: 2048x2048"),
+    ("qmv_kernel<8, 0, 1, 1, 2, false>", "qmv Q8_0 fp32 x: 64x256 (latency point)"),
+    ("tile_kernel<1>", "tile M <= 16: 8192x2048 at M = 8, 16 (and 4)"),
+    ("tile_kernel<2>", "tile M = 32: 8192x2048"),
+    ("quantize_q8_0_kernel", "quantize_q8_0 1x2048"),
+    ("pack_kernel<8>", "pack Q8_0 (vocab + small)"),
+    ("pack_kernel<2>", "pack Q4_0 (all Q4_0 weights)"),
+    ("lane_stride_kernel", "read-stream ceiling, lane grid-stride (bench helper)"),
+    ("wave_chunk_kernel", "read-stream ceiling, wave chunks (bench helper)"),
+    ("copyBuffer", "runtime copy"),
+]
+
+
+def stats_summary(args):
+    """Kernel table of a rocprofv3 --kernel-trace --stats run of the default
+    benchmark, with the dominant kernel's rocprof average beside the live
+    HIP-event average of the same run."""
+    run_dir = args.stats_summary
+    files = glob.glob(os.path.join(run_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no kernel_stats.csv under %s" % run_dir)
+    rows = list(csv.DictReader(open(files[0])))
+    lines = [
+        "# rocprofv3 kernel statistics: the decode-step benchmark (bench.py, default arguments), MI355X (gfx950)",
+        "# command (repository root R on the GPU host):",
+        "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d $R/%s -o run \\" % run_dir,
+        "#       --output-format csv -- python3 $R/bench.py > $R/%s.log" % run_dir.rstrip("/"),
+        "#   python3 bench.py --stats-summary %s --write-profile" % run_dir,
+        "# durations in microseconds; kernel_source_hash = %s" % kernel_source_hash(),
+        "%-58s %6s %9s %9s %9s" % ("kernel", "calls", "avg_us", "min_us", "max_us"),
+    ]
+    dom = None
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        label = next((lab for key, lab in KERNEL_LABELS if key in r["Name"]), r["Name"][:58])
+        lines.append("%-58s %6s %9.2f %9.2f %9.2f" % (label, r["Calls"], float(r["AverageNs"]) / 1e3,
+                                                     float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+        if "qmv_kernel<8, 0, 2, 1, 4, false>" in r["Name"]:
+            dom = float(r["AverageNs"]) / 1e3
+    log_file = run_dir.rstrip("/") + ".log"
+    ev = None
+    if os.path.exists(log_file):
+        for line in open(log_file):
+            if line.startswith("{"):
+                ev = json.loads(line)["roofline"]["avg_launch_us"]
+    if dom is not None:
+        alg = 262144 * 64 * 34 + 2048 * 4 + 262144 * 4
+        lines.append("")
+        lines.append("# dominant kernel (vocab): %d B / %.2f us = %.2f TB/s = %.1f%% of 8 TB/s (rocprof average)"
+                     % (alg, dom, alg / dom / 1e6, alg / dom / 1e6 / 8.0 * 100))
+        if ev is not None:
+            lines.append("# the same run's live HIP-event average over the timed launches: %.2f us (events bracket "
+                         "each launch, so they add the event-record overhead; difference %.1f%%)"
+                         % (ev, (ev / dom - 1) * 100))
+    text = "\n".join(lines) + "\n"
+    print(text)
+    if args.write_profile:
+        with open(STATS_FILE, "w") as f:
+            f.write(text)
+
+
 # ----------------------------------------------------------------------------
 # main
 # ----------------------------------------------------------------------------
@@ -515,8 +661,12 @@ def main():
     ap.add_argument("--sets", type=int, default=2, help="rotated copies of the step's weights")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["bench", "pmc"], default="bench")
+    ap.add_argument("--mode", choices=["bench", "pmc", "pmc-step"], default="bench")
     ap.add_argument("--pmc-summary", default=None)
+    ap.add_argument("--counters-summary", default=None,
+                    help="A_DIR,B_DIR of the two --mode pmc-step counter runs -> VALU / MFMA table")
+    ap.add_argument("--stats-summary", default=None,
+                    help="rocprofv3 --kernel-trace --stats output dir of the default run -> kernel table")
     ap.add_argument("--write-profile", action="store_true",
                     help="with --pmc-summary: write the summary under profiles/")
     args = ap.parse_args()
@@ -526,6 +676,12 @@ def main():
 
     if args.pmc_summary:
         pmc_summary(args)
+        return
+    if args.stats_summary:
+        stats_summary(args)
+        return
+    if args.counters_summary:
+        counters_summary(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -539,6 +695,9 @@ def main():
         sys.exit(1)
     if args.mode == "pmc":
         pmc_mode(args, log)
+        return
+    if args.mode == "pmc-step":
+        pmc_step_mode(args, log)
         return
 
     step = Step(args.sets, log)
