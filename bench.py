@@ -78,6 +78,58 @@ def kernel_source_hash() -> str:
 
 
 # ----------------------------------------------------------------------------
+# timing events
+# ----------------------------------------------------------------------------
+
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+_hip = None
+
+
+def _hip_runtime():
+    """The HIP runtime torch has already loaded (resolved by its SONAME)."""
+    global _hip
+    if _hip is None:
+        import ctypes
+
+        import torch  # noqa: F401  (loads the runtime first)
+        _hip = ctypes.CDLL("libamdhip64.so.7")
+        _hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        _hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        _hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        _hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return _hip
+
+
+class TimingEvent:
+    """A HIP event used only for timing, created with
+    hipEventDisableSystemFence: recording it does not write back and
+    invalidate the caches (which a default event does, adding to the interval
+    it brackets and slowing the work after it). Same interface as torch's
+    timing events: record(stream), elapsed_time(end) in milliseconds."""
+
+    def __init__(self):
+        import ctypes
+        self._ctypes = ctypes
+        self.ev = ctypes.c_void_p()
+        if _hip_runtime().hipEventCreateWithFlags(ctypes.byref(self.ev), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream):
+        if _hip_runtime().hipEventRecord(self.ev, self._ctypes.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end):
+        ms = self._ctypes.c_float()
+        if _hip_runtime().hipEventElapsedTime(self._ctypes.byref(ms), self.ev, end.ev) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if self.ev:
+            _hip_runtime().hipEventDestroy(self.ev)
+
+
+# ----------------------------------------------------------------------------
 # workload
 # ----------------------------------------------------------------------------
 
@@ -233,8 +285,8 @@ class Step:
         (start, end) event pairs recorded around that launch."""
         for name, fn, args, _, _ in self.sets[i % len(self.sets)]:
             if events is not None and name in events:
-                a = self.torch.cuda.Event(enable_timing=True)
-                b = self.torch.cuda.Event(enable_timing=True)
+                a = TimingEvent()
+                b = TimingEvent()
                 a.record(self.stream)
                 st = fn(*args)
                 b.record(self.stream)
@@ -250,8 +302,8 @@ def _event_times(step, fn, fargs, reps):
     torch = step.torch
     evs = []
     for _ in range(reps):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
+        a = TimingEvent()
+        b = TimingEvent()
         a.record(step.stream)
         if fn(*fargs) != 0:
             raise RuntimeError("launch failed")
@@ -285,8 +337,8 @@ def read_stream_ceiling(step, log):
             if launch(i) != 0:
                 raise RuntimeError("read-stream launch failed")
         torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
+        a = TimingEvent()
+        b = TimingEvent()
         reps = 8
         a.record(step.stream)
         for i in range(reps):
@@ -742,8 +794,8 @@ def main():
     for name, fn, fargs, wb, ob in step.extras:
         evs = []
         for _ in range(nb):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
+            a = TimingEvent()
+            b = TimingEvent()
             a.record(step.stream)
             if fn(*fargs) != 0:
                 raise RuntimeError("launch failed: " + name)
