@@ -43,63 +43,61 @@ hipError_t launch_pack(int type, const uint8_t* blocks, int64_t n, int64_t k, ui
 }
 
 // ---------------------------------------------------------------------------
-// Q8_0 activation quantiser, one thread per 32-element block:
-// amax (fp32) -> d = binary16(amax / 127) (fp32 divide, then round to
-// nearest even) -> q = clamp(round-half-away(x / d), -127, 127) with the
-// divide in fp32 by the rounded d; q = 0 when d == 0. The fp32 divides are
-// IEEE correctly rounded (no fast-math) so both the codes and the scale are
-// reproducible bit for bit. fp32 activation -> int8 codes + scale is the
-// activation quantiser of the jouleclaw-loader-gguf BENCHMARKS page
-// ("Matmul throughput -- Q8_0 scalar vs NEON"), taken per 32-element block.
+// Q8_0 activation quantiser: amax (fp32) -> d = binary16(amax / 127) (fp32
+// divide, then round to nearest even) -> q = clamp(round-half-away(x / d),
+// -127, 127) with the divide in fp32 by the rounded d; q = 0 when d == 0.
+// The fp32 divides are IEEE correctly rounded (no fast-math) so both the
+// codes and the scale are reproducible bit for bit. fp32 activation -> int8
+// codes + scale is the activation quantiser of the jouleclaw-loader-gguf
+// BENCHMARKS page ("Matmul throughput -- Q8_0 scalar vs NEON"), taken per
+// 32-element block.
+//
+// Eight lanes share a block, four elements each: one 16-byte load per lane,
+// the block's amax by a max over the eight lanes with DPP (max is exact, so
+// the order does not matter), four divides per lane, one 4-byte store per
+// lane (a wave writes 256 contiguous code bytes) and the scale from the
+// block's first lane. The blocks of all m rows are one flat sequence (x,
+// xq and xd are contiguous row after row).
 // ---------------------------------------------------------------------------
+constexpr int kQuantLanesPerBlock = 8;
+
 __global__ __launch_bounds__(kBlockThreads)
 void quantize_q8_0_kernel(const float* __restrict__ x, int64_t nblocks, int8_t* __restrict__ xq,
                           uint16_t* __restrict__ xd) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i >= nblocks) return;
-    const float4* src = reinterpret_cast<const float4*>(x + i * 32);
-    float v[32];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const float4 t = src[j];
-        v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-        const float a = fabsf(v[j]);
-        amax = a > amax ? a : amax;
-    }
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t blk = t / kQuantLanesPerBlock;
+    // the grid is whole waves and a block's eight lanes sit in one aligned
+    // group of a wave, so a group is either entirely in range or entirely out
+    if (blk >= nblocks) return;
+    const float4 v = reinterpret_cast<const float4*>(x)[t];
+    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    amax = fmaxf(amax, dpp_f32<kDppQuadSwap1>(amax));
+    amax = fmaxf(amax, dpp_f32<kDppQuadSwap2>(amax));
+    amax = fmaxf(amax, dpp_f32<kDppRowHalfMirror>(amax));
     const uint16_t hb = float_to_half_bits(amax / 127.0f);
     const float dh = half_bits_to_float(hb);
-    xd[i] = hb;
-    uint32_t packed[8];
+    if ((t & (kQuantLanesPerBlock - 1)) == 0) xd[blk] = hb;
+    const float e[4] = {v.x, v.y, v.z, v.w};
+    uint32_t w = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            int q = 0;
-            if (dh != 0.0f) {
-                float r = roundf(v[4 * j + b] / dh);
-                r = fminf(fmaxf(r, -127.0f), 127.0f);
-                q = static_cast<int>(r);
-            }
-            w |= (static_cast<uint32_t>(q) & 0xFFu) << (8 * b);
+    for (int b = 0; b < 4; ++b) {
+        int q = 0;
+        if (dh != 0.0f) {
+            float r = roundf(e[b] / dh);
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            q = static_cast<int>(r);
         }
-        packed[j] = w;
+        w |= (static_cast<uint32_t>(q) & 0xFFu) << (8 * b);
     }
-    uint4* dst = reinterpret_cast<uint4*>(xq + i * 32);
-    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    reinterpret_cast<uint32_t*>(xq)[t] = w;
 }
 
 hipError_t launch_quantize_q8_0(const float* x, int64_t m, int64_t k, int8_t* xq, uint16_t* xd,
                                 hipStream_t stream) {
-    const int64_t nblocks = m * (k / 32);
-    const int64_t grid = (nblocks + kBlockThreads - 1) / kBlockThreads;
+    const int64_t threads = m * (k / 32) * kQuantLanesPerBlock;
+    const int64_t grid = (threads + kBlockThreads - 1) / kBlockThreads;
     return launch_kernel(quantize_q8_0_kernel, dim3(static_cast<unsigned>(grid)), dim3(kBlockThreads), stream,
-                         x, nblocks, xq, xd);
+                         x, m * (k / 32), xq, xd);
 }
 
 }  // namespace gq

@@ -181,6 +181,17 @@ def test_quantize_bit_exact():
     assert np.array_equal(down(xq), rq.reshape(-1)) and np.array_equal(down(xd, np.uint16), rd.reshape(-1))
 
 
+@pytest.mark.parametrize("m,k", [(1, 32), (3, 96), (5, 1056), (33, 8192), (1, 32768), (257, 64)])
+def test_quantize_ragged_shapes(m, k):
+    """Block counts that leave part of the last workgroup (and wave) idle."""
+    rng = np.random.default_rng(m * 7 + k)
+    x = synth.activations(rng, (m, k)) * np.float32(rng.uniform(0.01, 100.0))
+    xq, xd = gq.quantize_q8_0(up(x))
+    rq, rd = oracle.quantize_q8_0(x)
+    assert np.array_equal(down(xq), rq)
+    assert np.array_equal(down(xd, np.uint16), rd)
+
+
 INT_SHAPES = [(Q4, 2048, 2048), (Q8, 64, 256), (Q4, 1, 32), (Q8, 1, 32), (Q4, 999, 96),
               (Q8, 777, 1056), (Q4, 300, 8192), (Q8, 300, 8192), (Q4, 33, 32768)]
 
