@@ -41,6 +41,9 @@
 #ifndef GQ_QMV_R_TALL
 #define GQ_QMV_R_TALL 4        // rows per wave step for tall (n >= 65536) un-split matrices
 #endif
+#ifndef GQ_QMV_R_SPLIT
+#define GQ_QMV_R_SPLIT 8         // rows per wave step when a row is split over 4 or 8 waves
+#endif
 #ifndef GQ_QMV_NT
 #define GQ_QMV_NT 1            // non-temporal loads for the quant stream (read once)
 #endif
@@ -560,7 +563,7 @@ hipError_t launch_cfg(QmvParams p, hipStream_t stream, int* grid_out) {
         // for the gate+up FFN) fit unspilled
         return launch_rows<TYPE, MODE, NI, WS, (MODE == kFFN ? 2 : 4)>(p, stream, grid_out);
     } else if constexpr (WS >= 4) {
-        return launch_rows<TYPE, MODE, NI, WS, 8>(p, stream, grid_out);
+        return launch_rows<TYPE, MODE, NI, WS, GQ_QMV_R_SPLIT>(p, stream, grid_out);
     } else {
         if (p.n >= 65536) return launch_rows<TYPE, MODE, NI, WS, GQ_QMV_R_TALL>(p, stream, grid_out);
         return launch_rows<TYPE, MODE, NI, WS, (MODE == kFFN ? GQ_QMV_R_FFN : 2)>(p, stream, grid_out);

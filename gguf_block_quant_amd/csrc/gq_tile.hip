@@ -20,9 +20,10 @@
 // k = 8s..8s+7 is bytes 8(s&1)..+7, low nibbles for s < 2, high for s >= 2.
 //
 // Work split: a workgroup owns 16 weight rows and walks k in chunks of
-// kChunk blocks. Each chunk's weight rows, activation codes and both scale
-// sets are staged in LDS with contiguous 16-byte global loads (the weight
-// rows stream from HBM one 512-byte run per row; the activations are
+// kChunk blocks (32 for one activation tile, 16 for two). Each chunk's
+// weight rows, activation codes and both scale sets are staged in LDS with
+// contiguous 16-byte global loads (the weight rows stream from HBM in
+// 512- or 256-byte runs per row; the activations are
 // shared by every workgroup and come from L2), while the registers already
 // hold the next chunk's loads. The four waves split the chunk's blocks; their
 // fp32 partials meet in LDS and are added in wave order (deterministic).
@@ -36,11 +37,22 @@ typedef int int32x4_t __attribute__((ext_vector_type(4)));
 
 namespace {
 
-constexpr int kChunk = 32;                         // blocks per chunk
-constexpr int kWPitch = kChunk * 16 + 16;          // weight row bytes in LDS (mod 256 = 16)
-constexpr int kXPitch = kChunk * 32 + 32;          // activation row bytes in LDS (mod 256 = 32)
+#ifndef GQ_TILE_CHUNK1
+#define GQ_TILE_CHUNK1 32
+#endif
+#ifndef GQ_TILE_CHUNK2
+#define GQ_TILE_CHUNK2 16        // two row tiles: shorter chunks keep the LDS and registers in budget (measured)
+#endif
 constexpr int kRows = 16;                          // weight rows per workgroup
-constexpr int kWavePart = kChunk / kWavesPerBlock; // blocks per wave per chunk
+// Blocks per k chunk, and the LDS pitches that follow from it: a weight row
+// takes CH * 16 + 16 bytes (mod 256 = 16), an activation row CH * 32 + 32
+// (mod 256 = 32), so the fragment reads of the 16 rows spread over the banks.
+template <int MT> struct Tiling {
+    static constexpr int kChunk = MT == 1 ? GQ_TILE_CHUNK1 : GQ_TILE_CHUNK2;
+    static constexpr int kWPitch = kChunk * 16 + 16;
+    static constexpr int kXPitch = kChunk * 32 + 32;
+    static constexpr int kWavePart = kChunk / kWavesPerBlock;   // blocks per wave per chunk
+};
 #ifndef GQ_TILE_BATCH
 #define GQ_TILE_BATCH 8
 #endif
@@ -64,6 +76,7 @@ __device__ __forceinline__ uint32_t nib_to_s8(uint32_t v) {
 template <int MT>
 struct Stage {                                      // one chunk's global loads, in registers
     static constexpr int MR = 16 * MT;
+    static constexpr int kChunk = Tiling<MT>::kChunk;
     static constexpr int WV = kRows * kChunk / kBlockThreads;           // 16-B weight pieces / thread
     static constexpr int XV = MR * kChunk * 2 / kBlockThreads;         // 16-B activation pieces / thread
     static constexpr int DXV = MR * kChunk / kBlockThreads;            // activation scales / thread
@@ -79,6 +92,7 @@ __device__ __forceinline__ void stage_load(Stage<MT>& st, int tid, int cb, int c
                                            int m, int64_t k, const uint8_t* qs, const uint16_t* d,
                                            const int8_t* xq, const uint16_t* xd) {
     constexpr int MR = Stage<MT>::MR;
+    constexpr int kChunk = Tiling<MT>::kChunk;
     const int row_bytes = nb * 16;
 #pragma unroll
     for (int i = 0; i < Stage<MT>::WV; ++i) {
@@ -121,6 +135,10 @@ void tile_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
                  int m, const int8_t* __restrict__ xq, const uint16_t* __restrict__ xd,
                  float* __restrict__ y, int32_t* __restrict__ blockdots) {
     constexpr int MR = 16 * MT;
+    constexpr int kChunk = Tiling<MT>::kChunk;
+    constexpr int kWPitch = Tiling<MT>::kWPitch;
+    constexpr int kXPitch = Tiling<MT>::kXPitch;
+    constexpr int kWavePart = Tiling<MT>::kWavePart;
     __shared__ __align__(16) uint8_t ws[kRows][kWPitch];
     __shared__ __align__(16) int8_t xs[MR][kXPitch];
     __shared__ __align__(16) float dxs[kChunk][MR];
@@ -180,6 +198,7 @@ void tile_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
         // both scales are zero, so they add exactly 0.
         const int b0 = wave * kWavePart;
         constexpr int kBatch = Batch<MT>::value;
+        static_assert(kWavePart % kBatch == 0, "a wave's blocks of a chunk must be whole batches");
 #pragma unroll GQ_TILE_JB_UNROLL
         for (int jb = 0; jb < kWavePart; jb += kBatch) {
             int32x4_t S[kBatch][MT];

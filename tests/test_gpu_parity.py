@@ -331,7 +331,8 @@ def test_tile_workload(m):
 
 @pytest.mark.parametrize("m,n,k", [(8, 1000, 96), (16, 17, 32), (32, 100, 1056), (32, 64, 8192),
                                    (1, 300, 2048), (2, 513, 512), (3, 64, 96), (5, 129, 1024),
-                                   (7, 2048, 2048), (12, 80, 256), (20, 48, 320), (31, 33, 4096)])
+                                   (7, 2048, 2048), (12, 80, 256), (20, 48, 320), (31, 33, 4096),
+                                   (24, 40, 544), (17, 16, 32768)])
 def test_tile_ragged(m, n, k):
     rng = np.random.default_rng(m * n + k)
     w = synth.q4_0_weights(rng, n, k)
