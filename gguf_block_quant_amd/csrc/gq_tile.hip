@@ -59,6 +59,12 @@ template <int MT> struct Tiling {
 #ifndef GQ_TILE_BATCH2
 #define GQ_TILE_BATCH2 4
 #endif
+#ifndef GQ_TILE_PAIR_BATCH
+#define GQ_TILE_PAIR_BATCH 4     // block pairs whose MFMAs issue before their epilogues (M <= 8)
+#endif
+#ifndef GQ_TILE_PAIRS
+#define GQ_TILE_PAIRS 1          // M <= 8 takes the paired-block MFMA
+#endif
 #ifndef GQ_TILE_JB_UNROLL
 #define GQ_TILE_JB_UNROLL 1
 #endif
@@ -73,31 +79,28 @@ __device__ __forceinline__ uint32_t nib_to_s8(uint32_t v) {
     return (v + 0x78787878u) ^ 0x80808080u;
 }
 
-template <int MT>
+template <int MR, int CH>
 struct Stage {                                      // one chunk's global loads, in registers
-    static constexpr int MR = 16 * MT;
-    static constexpr int kChunk = Tiling<MT>::kChunk;
-    static constexpr int WV = kRows * kChunk / kBlockThreads;           // 16-B weight pieces / thread
-    static constexpr int XV = MR * kChunk * 2 / kBlockThreads;         // 16-B activation pieces / thread
-    static constexpr int DXV = MR * kChunk / kBlockThreads;            // activation scales / thread
-    static constexpr int DWV = kRows * kChunk / kBlockThreads;         // weight scales / thread
+    static constexpr int WV = kRows * CH / kBlockThreads;           // 16-B weight pieces / thread
+    static constexpr int XV = MR * CH * 2 / kBlockThreads;          // 16-B activation pieces / thread
+    static constexpr int DXV = MR * CH / kBlockThreads;             // activation scales / thread
+    static constexpr int DWV = kRows * CH / kBlockThreads;          // weight scales / thread
+    static_assert(WV >= 1 && XV >= 1 && DXV >= 1 && DWV >= 1, "chunk too short for the workgroup");
     uint4 w[WV];
     uint4 x[XV];
     uint16_t dx[DXV];
     uint16_t dw[DWV];
 };
 
-template <int MT>
-__device__ __forceinline__ void stage_load(Stage<MT>& st, int tid, int cb, int cn, int n0, int n, int nb,
+template <int MR, int CH>
+__device__ __forceinline__ void stage_load(Stage<MR, CH>& st, int tid, int cb, int cn, int n0, int n, int nb,
                                            int m, int64_t k, const uint8_t* qs, const uint16_t* d,
                                            const int8_t* xq, const uint16_t* xd) {
-    constexpr int MR = Stage<MT>::MR;
-    constexpr int kChunk = Tiling<MT>::kChunk;
     const int row_bytes = nb * 16;
 #pragma unroll
-    for (int i = 0; i < Stage<MT>::WV; ++i) {
+    for (int i = 0; i < Stage<MR, CH>::WV; ++i) {
         const int e = tid + i * kBlockThreads;
-        const int row = e / kChunk, b = e % kChunk;          // a row's pieces are consecutive
+        const int row = e / CH, b = e % CH;                  // a row's pieces are consecutive
         const uint8_t* src = qs + static_cast<int64_t>(min(n0 + row, n - 1)) * row_bytes + (cb + b) * 16;
         if (b < cn) {
             typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -108,37 +111,46 @@ __device__ __forceinline__ void stage_load(Stage<MT>& st, int tid, int cb, int c
         }
     }
 #pragma unroll
-    for (int i = 0; i < Stage<MT>::XV; ++i) {
+    for (int i = 0; i < Stage<MR, CH>::XV; ++i) {
         const int e = tid + i * kBlockThreads;
-        const int row = e / (2 * kChunk), piece = e % (2 * kChunk);
+        const int row = e / (2 * CH), piece = e % (2 * CH);
         st.x[i] = (row < m && piece < 2 * cn)
                       ? *reinterpret_cast<const uint4*>(xq + row * k + cb * 32 + piece * 16)
                       : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
-    for (int i = 0; i < Stage<MT>::DXV; ++i) {
+    for (int i = 0; i < Stage<MR, CH>::DXV; ++i) {
         const int e = tid + i * kBlockThreads;
         const int b = e / MR, row = e % MR;
         st.dx[i] = (row < m && b < cn) ? xd[static_cast<int64_t>(row) * nb + cb + b] : uint16_t(0);
     }
 #pragma unroll
-    for (int i = 0; i < Stage<MT>::DWV; ++i) {
+    for (int i = 0; i < Stage<MR, CH>::DWV; ++i) {
         const int e = tid + i * kBlockThreads;
         const int b = e / kRows, row = e % kRows;
         st.dw[i] = (b < cn) ? d[static_cast<int64_t>(min(n0 + row, n - 1)) * nb + cb + b] : uint16_t(0);
     }
 }
 
-template <int MT>   // MT activation tiles of 16 rows (M = 8, 16 -> 1; M = 32 -> 2)
+// MT activation tiles of 16 rows (M <= 16 -> 1; M <= 32 -> 2). PAIR (M <= 8
+// only, MT = 1): one v_mfma_i32_16x16x64_i8 covers two consecutive blocks --
+// its 16 A rows are the <= 8 activation rows twice, the first copy holding
+// block b in the k positions where B holds block b's weights and zeros where
+// B holds block b+1's, the second copy the other way round -- so D rows 0..7
+// are S for block b and rows 8..15 S for block b+1, and no MFMA row or
+// epilogue lane is spent on padding.
+template <int MT, bool PAIR>
 __global__ __launch_bounds__(kBlockThreads)
 void tile_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d, int n, int nb,
                  int m, const int8_t* __restrict__ xq, const uint16_t* __restrict__ xd,
                  float* __restrict__ y, int32_t* __restrict__ blockdots) {
-    constexpr int MR = 16 * MT;
+    static_assert(!PAIR || MT == 1, "paired blocks are for M <= 8");
+    constexpr int MR = PAIR ? 8 : 16 * MT;
     constexpr int kChunk = Tiling<MT>::kChunk;
     constexpr int kWPitch = Tiling<MT>::kWPitch;
     constexpr int kXPitch = Tiling<MT>::kXPitch;
     constexpr int kWavePart = Tiling<MT>::kWavePart;
+    using St = Stage<MR, kChunk>;
     __shared__ __align__(16) uint8_t ws[kRows][kWPitch];
     __shared__ __align__(16) int8_t xs[MR][kXPitch];
     __shared__ __align__(16) float dxs[kChunk][MR];
@@ -160,36 +172,37 @@ void tile_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[t][v] = 0.f;
 
-    Stage<MT> st;
-    stage_load<MT>(st, tid, 0, min(kChunk, nb), n0, n, nb, m, k, qs, d, xq, xd);
+    St st;
+    stage_load<MR, kChunk>(st, tid, 0, min(kChunk, nb), n0, n, nb, m, k, qs, d, xq, xd);
 
     for (int cb = 0; cb < nb; cb += kChunk) {
         const int cn = min(kChunk, nb - cb);
         // registers -> LDS
 #pragma unroll
-        for (int i = 0; i < Stage<MT>::WV; ++i) {
+        for (int i = 0; i < St::WV; ++i) {
             const int e = tid + i * kBlockThreads;
             *reinterpret_cast<uint4*>(&ws[e / kChunk][(e % kChunk) * 16]) = st.w[i];
         }
 #pragma unroll
-        for (int i = 0; i < Stage<MT>::XV; ++i) {
+        for (int i = 0; i < St::XV; ++i) {
             const int e = tid + i * kBlockThreads;
             *reinterpret_cast<uint4*>(&xs[e / (2 * kChunk)][(e % (2 * kChunk)) * 16]) = st.x[i];
         }
 #pragma unroll
-        for (int i = 0; i < Stage<MT>::DXV; ++i) {
+        for (int i = 0; i < St::DXV; ++i) {
             const int e = tid + i * kBlockThreads;
             dxs[e / MR][e % MR] = half_bits_to_float(st.dx[i]);
         }
 #pragma unroll
-        for (int i = 0; i < Stage<MT>::DWV; ++i) {
+        for (int i = 0; i < St::DWV; ++i) {
             const int e = tid + i * kBlockThreads;
             dws[e / kRows][e % kRows] = half_bits_to_float(st.dw[i]);
         }
         __syncthreads();
         // the next chunk's global loads fly while this chunk computes
         if (cb + kChunk < nb)
-            stage_load<MT>(st, tid, cb + kChunk, min(kChunk, nb - cb - kChunk), n0, n, nb, m, k, qs, d, xq, xd);
+            stage_load<MR, kChunk>(st, tid, cb + kChunk, min(kChunk, nb - cb - kChunk), n0, n, nb, m, k, qs, d,
+                                   xq, xd);
 
         // this wave's blocks of the chunk, kBatch at a time: the batch's
         // scales are read from LDS first, then its MFMAs are issued, then
@@ -197,79 +210,153 @@ void tile_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
         // Blocks past the end of k need no branch: their staged weights and
         // both scales are zero, so they add exactly 0.
         const int b0 = wave * kWavePart;
-        constexpr int kBatch = Batch<MT>::value;
-        static_assert(kWavePart % kBatch == 0, "a wave's blocks of a chunk must be whole batches");
+        if constexpr (PAIR) {
+            // lane (s, c): block bl + (s >> 1) of weight row c, nibble half s & 1
+            // (elements 16 (s & 1) .. +15); activation row c & 7 of the same
+            // block where the copy matches (c < 8 with s < 2, c >= 8 with s >= 2),
+            // zeros elsewhere. D value v of lane (s, c): activation row
+            // 4 (s & 1) + v, weight row c, block bl + (s >> 1).
+            constexpr int kPairs = GQ_TILE_PAIR_BATCH;
+            static_assert(kWavePart % (2 * kPairs) == 0, "a wave's blocks of a chunk must be whole pair batches");
+            const int half = s >> 1;
+            const bool live = (c < 8) == (half == 0);
+            const int nshift = (s & 1) * 4;
 #pragma unroll GQ_TILE_JB_UNROLL
-        for (int jb = 0; jb < kWavePart; jb += kBatch) {
-            int32x4_t S[kBatch][MT];
-            float dwv[kBatch];
-            float4 dxv[kBatch][MT];
+            for (int jb = 0; jb < kWavePart; jb += 2 * kPairs) {
+                int32x4_t S[kPairs];
+                float dwv[kPairs];
+                float4 dxv[kPairs];
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                const int bl = b0 + jb + j;
-                dwv[j] = dws[bl][c];
+                for (int j = 0; j < kPairs; ++j) {
+                    const int bl = b0 + jb + 2 * j + half;
+                    dwv[j] = dws[bl][c];
+                    dxv[j] = *reinterpret_cast<const float4*>(&dxs[bl][4 * (s & 1)]);
+                }
 #pragma unroll
-                for (int t = 0; t < MT; ++t) dxv[j][t] = *reinterpret_cast<const float4*>(&dxs[bl][16 * t + 4 * s]);
-            }
-#pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                const int bl = b0 + jb + j;
-                const uint2 wq = *reinterpret_cast<const uint2*>(&ws[c][bl * 16 + 8 * (s & 1)]);
-                const uint32_t lo = nib_to_s8((wq.x >> ashift) & 0x0F0F0F0Fu);
-                const uint32_t hi = nib_to_s8((wq.y >> ashift) & 0x0F0F0F0Fu);
-                const long bop = static_cast<long>((static_cast<uint64_t>(hi) << 32) | lo);
-#pragma unroll
-                for (int t = 0; t < MT; ++t) {
-                    const long aop = *reinterpret_cast<const long*>(&xs[16 * t + c][bl * 32 + 8 * s]);
+                for (int j = 0; j < kPairs; ++j) {
+                    const int bl = b0 + jb + 2 * j + half;
+                    const uint4 wq = *reinterpret_cast<const uint4*>(&ws[c][bl * 16]);
+                    typedef int int32x4v __attribute__((ext_vector_type(4)));
+                    const int32x4v bop = {static_cast<int>(nib_to_s8((wq.x >> nshift) & 0x0F0F0F0Fu)),
+                                          static_cast<int>(nib_to_s8((wq.y >> nshift) & 0x0F0F0F0Fu)),
+                                          static_cast<int>(nib_to_s8((wq.z >> nshift) & 0x0F0F0F0Fu)),
+                                          static_cast<int>(nib_to_s8((wq.w >> nshift) & 0x0F0F0F0Fu))};
+                    const uint4 xa = *reinterpret_cast<const uint4*>(&xs[c & 7][bl * 32 + 16 * (s & 1)]);
+                    const int32x4v aop = {live ? static_cast<int>(xa.x) : 0, live ? static_cast<int>(xa.y) : 0,
+                                          live ? static_cast<int>(xa.z) : 0, live ? static_cast<int>(xa.w) : 0};
                     const int32x4_t zero = {0, 0, 0, 0};
-                    S[j][t] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop, zero, 0, 0, 0);
+                    S[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop, bop, zero, 0, 0, 0);
+                }
+#pragma unroll
+                for (int j = 0; j < kPairs; ++j) {
+                    const float dx[4] = {dxv[j].x, dxv[j].y, dxv[j].z, dxv[j].w};
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[0][v] = fmaf(dwv[j] * dx[v], static_cast<float>(S[j][v]), acc[0][v]);
+                }
+                if (blockdots != nullptr) {
+                    const int col = n0 + c;
+#pragma unroll
+                    for (int j = 0; j < kPairs; ++j) {
+                        const int bl = b0 + jb + 2 * j + half;
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int mrow = 4 * (s & 1) + v;
+                            if (bl < cn && mrow < m && col < n)
+                                blockdots[(static_cast<int64_t>(mrow) * n + col) * nb + cb + bl] = S[j][v];
+                        }
+                    }
                 }
             }
-#pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-#pragma unroll
-                for (int t = 0; t < MT; ++t) {
-                    const float dx[4] = {dxv[j][t].x, dxv[j][t].y, dxv[j][t].z, dxv[j][t].w};
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        acc[t][v] = fmaf(dwv[j] * dx[v], static_cast<float>(S[j][t][v]), acc[t][v]);
-                }
-            }
-            if (blockdots != nullptr) {
-                const int col = n0 + c;
+        } else {
+            constexpr int kBatch = Batch<MT>::value;
+            static_assert(kWavePart % kBatch == 0, "a wave's blocks of a chunk must be whole batches");
+#pragma unroll GQ_TILE_JB_UNROLL
+            for (int jb = 0; jb < kWavePart; jb += kBatch) {
+                int32x4_t S[kBatch][MT];
+                float dwv[kBatch];
+                float4 dxv[kBatch][MT];
 #pragma unroll
                 for (int j = 0; j < kBatch; ++j) {
                     const int bl = b0 + jb + j;
+                    dwv[j] = dws[bl][c];
 #pragma unroll
                     for (int t = 0; t < MT; ++t)
+                        dxv[j][t] = *reinterpret_cast<const float4*>(&dxs[bl][16 * t + 4 * s]);
+                }
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const int mrow = 16 * t + 4 * s + v;
-                            if (bl < cn && mrow < m && col < n)
-                                blockdots[(static_cast<int64_t>(mrow) * n + col) * nb + cb + bl] = S[j][t][v];
-                        }
+                for (int j = 0; j < kBatch; ++j) {
+                    const int bl = b0 + jb + j;
+                    const uint2 wq = *reinterpret_cast<const uint2*>(&ws[c][bl * 16 + 8 * (s & 1)]);
+                    const uint32_t lo = nib_to_s8((wq.x >> ashift) & 0x0F0F0F0Fu);
+                    const uint32_t hi = nib_to_s8((wq.y >> ashift) & 0x0F0F0F0Fu);
+                    const long bop = static_cast<long>((static_cast<uint64_t>(hi) << 32) | lo);
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) {
+                        const long aop = *reinterpret_cast<const long*>(&xs[16 * t + c][bl * 32 + 8 * s]);
+                        const int32x4_t zero = {0, 0, 0, 0};
+                        S[j][t] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop, zero, 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) {
+                        const float dx[4] = {dxv[j][t].x, dxv[j][t].y, dxv[j][t].z, dxv[j][t].w};
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            acc[t][v] = fmaf(dwv[j] * dx[v], static_cast<float>(S[j][t][v]), acc[t][v]);
+                    }
+                }
+                if (blockdots != nullptr) {
+                    const int col = n0 + c;
+#pragma unroll
+                    for (int j = 0; j < kBatch; ++j) {
+                        const int bl = b0 + jb + j;
+#pragma unroll
+                        for (int t = 0; t < MT; ++t)
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                const int mrow = 16 * t + 4 * s + v;
+                                if (bl < cn && mrow < m && col < n)
+                                    blockdots[(static_cast<int64_t>(mrow) * n + col) * nb + cb + bl] = S[j][t][v];
+                            }
+                    }
                 }
             }
         }
         __syncthreads();   // LDS is rewritten by the next chunk
     }
 
-    // add the four waves' partials in wave order and store
+    // add the four waves' partials in wave order (and, for paired blocks, the
+    // two lane halves holding even and odd blocks) and store
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
         for (int v = 0; v < 4; ++v) part[wave][t][v][lane] = acc[t][v];
     __syncthreads();
-    for (int e = tid; e < MT * 4 * kWave; e += kBlockThreads) {
-        const int l = e % kWave;
-        const int v = (e / kWave) % 4;
-        const int t = e / (kWave * 4);
-        float tot = part[0][t][v][l];
+    if constexpr (PAIR) {
+        if (tid < 2 * 4 * 16) {                      // 8 activation rows x 16 weight rows
+            const int l = tid % 32;                  // lane of the even-block half: s = l / 16 in {0, 1}
+            const int v = tid / 32;
+            float tot = part[0][0][v][l] + part[0][0][v][l + 32];
 #pragma unroll
-        for (int w = 1; w < kWavesPerBlock; ++w) tot += part[w][t][v][l];
-        const int mrow = 16 * t + 4 * (l >> 4) + v;
-        const int col = n0 + (l & 15);
-        if (mrow < m && col < n) y[static_cast<int64_t>(mrow) * n + col] = tot;
+            for (int w = 1; w < kWavesPerBlock; ++w) tot += part[w][0][v][l] + part[w][0][v][l + 32];
+            const int mrow = 4 * (l >> 4) + v;
+            const int col = n0 + (l & 15);
+            if (mrow < m && col < n) y[static_cast<int64_t>(mrow) * n + col] = tot;
+        }
+    } else {
+        for (int e = tid; e < MT * 4 * kWave; e += kBlockThreads) {
+            const int l = e % kWave;
+            const int v = (e / kWave) % 4;
+            const int t = e / (kWave * 4);
+            float tot = part[0][t][v][l];
+#pragma unroll
+            for (int w = 1; w < kWavesPerBlock; ++w) tot += part[w][t][v][l];
+            const int mrow = 16 * t + 4 * (l >> 4) + v;
+            const int col = n0 + (l & 15);
+            if (mrow < m && col < n) y[static_cast<int64_t>(mrow) * n + col] = tot;
+        }
     }
 }
 
@@ -280,10 +367,13 @@ hipError_t launch_tile_q4_0(const uint8_t* qs, const uint16_t* d, int64_t n, int
                             hipStream_t stream) {
     const int grid = static_cast<int>((n + kRows - 1) / kRows);
     const int nb = static_cast<int>(k / 32);
-    if (m <= 16)
-        return launch_kernel(tile_kernel<1>, dim3(grid), dim3(kBlockThreads), stream, qs, d,
+    if (GQ_TILE_PAIRS && m <= 8)
+        return launch_kernel(tile_kernel<1, true>, dim3(grid), dim3(kBlockThreads), stream, qs, d,
                              static_cast<int>(n), nb, m, xq, xd, y, blockdots);
-    return launch_kernel(tile_kernel<2>, dim3(grid), dim3(kBlockThreads), stream, qs, d,
+    if (m <= 16)
+        return launch_kernel(tile_kernel<1, false>, dim3(grid), dim3(kBlockThreads), stream, qs, d,
+                             static_cast<int>(n), nb, m, xq, xd, y, blockdots);
+    return launch_kernel(tile_kernel<2, false>, dim3(grid), dim3(kBlockThreads), stream, qs, d,
                          static_cast<int>(n), nb, m, xq, xd, y, blockdots);
 }
 
