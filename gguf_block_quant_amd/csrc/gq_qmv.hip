@@ -111,29 +111,37 @@ __device__ __forceinline__ float unit_dot_f32(const uint4 q, const float* xr) {
         // one packed fp16 add of -1032 leaves q - 8 exactly, and
         // v_fma_mix_f32 multiplies that half by the fp32 activation with a
         // single rounding -- the same value as an fp32 FMA on (float)(q - 8).
+        // The high nibbles are taken in place (bits 4..7 and 20..23), which
+        // gives 1024 + 16 q; adding -1152 leaves 16 (q - 8), still exact in
+        // binary16, accumulated separately and scaled by 1/16 (exact) at the
+        // end. Two masks share one shift per word instead of three shifts.
         typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-        const half2_t off = {static_cast<_Float16>(-1032.0f), static_cast<_Float16>(-1032.0f)};
+        const half2_t off_lo = {static_cast<_Float16>(-1032.0f), static_cast<_Float16>(-1032.0f)};
+        const half2_t off_hi = {static_cast<_Float16>(-1152.0f), static_cast<_Float16>(-1152.0f)};
         // keep the exponent pattern in a VGPR: gfx9 VOP3 takes no literal, and
         // with one register operand the mask-and-or is a single v_and_or_b32
         uint32_t magic = 0x64006400u;
         asm volatile("" : "+v"(magic));
+        float ph = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint32_t v = w[j];
-            const half2_t lo02 = __builtin_bit_cast(half2_t, (v & 0x000F000Fu) | magic) + off;
-            const half2_t lo13 = __builtin_bit_cast(half2_t, ((v >> 8) & 0x000F000Fu) | magic) + off;
-            const half2_t hi02 = __builtin_bit_cast(half2_t, ((v >> 4) & 0x000F000Fu) | magic) + off;
-            const half2_t hi13 = __builtin_bit_cast(half2_t, ((v >> 12) & 0x000F000Fu) | magic) + off;
+            const uint32_t v8 = v >> 8;
+            const half2_t lo02 = __builtin_bit_cast(half2_t, (v & 0x000F000Fu) | magic) + off_lo;
+            const half2_t lo13 = __builtin_bit_cast(half2_t, (v8 & 0x000F000Fu) | magic) + off_lo;
+            const half2_t hi02 = __builtin_bit_cast(half2_t, (v & 0x00F000F0u) | magic) + off_hi;
+            const half2_t hi13 = __builtin_bit_cast(half2_t, (v8 & 0x00F000F0u) | magic) + off_hi;
             // element order: 4j+b (low nibble of byte b), then 16+4j+b (its high nibble)
             p = fmaf(static_cast<float>(lo02.x), xr[4 * j + 0], p);
-            p = fmaf(static_cast<float>(hi02.x), xr[16 + 4 * j + 0], p);
+            ph = fmaf(static_cast<float>(hi02.x), xr[16 + 4 * j + 0], ph);
             p = fmaf(static_cast<float>(lo13.x), xr[4 * j + 1], p);
-            p = fmaf(static_cast<float>(hi13.x), xr[16 + 4 * j + 1], p);
+            ph = fmaf(static_cast<float>(hi13.x), xr[16 + 4 * j + 1], ph);
             p = fmaf(static_cast<float>(lo02.y), xr[4 * j + 2], p);
-            p = fmaf(static_cast<float>(hi02.y), xr[16 + 4 * j + 2], p);
+            ph = fmaf(static_cast<float>(hi02.y), xr[16 + 4 * j + 2], ph);
             p = fmaf(static_cast<float>(lo13.y), xr[4 * j + 3], p);
-            p = fmaf(static_cast<float>(hi13.y), xr[16 + 4 * j + 3], p);
+            ph = fmaf(static_cast<float>(hi13.y), xr[16 + 4 * j + 3], ph);
         }
+        p = fmaf(ph, 0.0625f, p);
     }
     return p;
 }
