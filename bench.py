@@ -5,13 +5,14 @@ One *step* is one pass of the whole hot path over one batch of synthetic
 inputs, shaped like one decode step that streams many different weights
 (the pages define effective bandwidth as bytes per token x tokens/s):
 
-  1. quantize_q8_0      x[2048] -> Q8_0 codes + scales
-  2. qmv_q4_0           Q4_0 2048 x 2048, fp32 x
-  3. qmv_q4_0_q8        Q4_0 2048 x 2048, Q8_0 x (int path, own weight copy)
-  4. qffn_gate_up_gelu  Q4_0 gate and up 8192 x 2048 -> h = G(gate x) * up x
-  5. qmv_q4_0           Q4_0 down 2048 x 8192 against h
-  6. qmv_q8_0           Q8_0 vocab 262144 x 2048 (0.57 GB of blocks), fp32 x
-  7. qmm_tile_m         Q4_0 8192 x 2048 against M = 8, 16, 32 Q8_0 rows
+  1. qmv_q4_0           Q4_0 2048 x 2048, fp32 x
+  2. qmv_q4_0_q8x       Q4_0 2048 x 2048, the same x quantised to Q8_0 in the
+                        kernel's prologue (int path, own weight copy; the
+                        codes and scales are written out too)
+  3. qffn_gate_up_gelu  Q4_0 gate and up 8192 x 2048 -> h = G(gate x) * up x
+  4. qmv_q4_0           Q4_0 down 2048 x 8192 against h
+  5. qmv_q8_0           Q8_0 vocab 262144 x 2048 (0.57 GB of blocks), fp32 x
+  6. qmm_tile_m         Q4_0 8192 x 2048 against M = 8, 16, 32 Q8_0 rows
 
 Every weight matrix is a distinct allocation, and ``--sets`` full copies of
 the step's weights are rotated so nothing is served from the 256 MB
@@ -207,11 +208,11 @@ class Step:
             self.keep.append((w2a, w2b, wg, wu, wd, wv, wt))
             self.vocab_qs = getattr(self, "vocab_qs", []) + [wv[0]]
             launches = [
-                ("quantize_q8_0 2048", L.gq_quantize_q8_0, (P(x2), 1, 2048, P(xq2), P(xd2), sp), 0, 2048 * 4 + 2048 + 128),
                 ("qmv_q4_0 2048x2048", L.gq_qmv_q4_0, (P(w2a[0]), P(w2a[1]), 2048, 2048, P(x2), P(y2a), sp),
                  2048 * 64 * 18, 8192 + 8192),
-                ("qmv_q4_0_q8 2048x2048", L.gq_qmv_q4_0_q8,
-                 (P(w2b[0]), P(w2b[1]), 2048, 2048, P(xq2), P(xd2), P(y2b), None, sp), 2048 * 64 * 18, 2176 + 8192),
+                ("qmv_q4_0_q8x 2048x2048 (quantise folded in)", L.gq_qmv_q4_0_q8x,
+                 (P(w2b[0]), P(w2b[1]), 2048, 2048, P(x2), P(xq2), P(xd2), P(y2b), None, sp), 2048 * 64 * 18,
+                 8192 + 2176 + 8192),
                 ("qffn_gate_up_gelu 8192x2048", L.gq_qffn_gate_up_gelu,
                  (P(wg[0]), P(wg[1]), P(wu[0]), P(wu[1]), 8192, 2048, P(x3), P(h3), sp), 2 * 8192 * 64 * 18,
                  8192 + 32768),
@@ -248,6 +249,11 @@ class Step:
                 self.hot = ("qmv_q4_0 2048x2048", L.gq_qmv_q4_0,
                             (P(w2a[0]), P(w2a[1]), 2048, 2048, P(x2), P(y2a), sp), 2048 * 64 * 18)
                 self.extras = [
+                    ("quantize_q8_0 2048 (standalone)", L.gq_quantize_q8_0, (P(x2), 1, 2048, P(xq2), P(xd2), sp), 0,
+                     2048 * 4 + 2048 + 128),
+                    ("qmv_q4_0_q8 2048x2048 (pre-quantised x)", L.gq_qmv_q4_0_q8,
+                     (P(w2b[0]), P(w2b[1]), 2048, 2048, P(xq2), P(xd2), P(y2b), None, sp), 2048 * 64 * 18,
+                     2176 + 8192),
                     ("qmv_q4_0_ex 2048x2048 (rmsnorm + residual)", L.gq_qmv_q4_0_ex,
                      (P(w2a[0]), P(w2a[1]), 2048, 2048, P(x2), P(g2), ctypes.c_float(1e-6), P(res2), P(y2c), sp),
                      2048 * 64 * 18, 8192 * 3 + 8192),
@@ -622,11 +628,12 @@ KERNEL_LABELS = [
     ("qmv_kernel<2, 0, 1, 4, 8, false>", "qmv Q4_0 fp32 x: down 2048x8192"),
     ("qmv_kernel<2, 0, 1, 1, 2, false>", "qmv Q4_0 fp32 x: 2048x2048 (step + MALL-hot runs)"),
     ("qmv_kernel<2, 0, 1, 1, 2, true>", "qmv Q4_0 + rmsnorm + residual: 2048x2048"),
-    ("qmv_kernel<2, 1, 1, 1, 2, false>", "qmv Q4_0 Q8_0 x: 2048x2048"),
+    ("qmv_kernel<2, 1, 1, 1, 2, false>", "qmv Q4_0 Q8_0 x: 2048x2048 (pre-quantised, extra)"),
+    ("qmv_kernel<2, 1, 1, 1, 2, true>", "qmv Q4_0 Q8_0 x quantised in the prologue: 2048x2048"),
     ("qmv_kernel<8, 0, 1, 1, 2, false>", "qmv Q8_0 fp32 x: 64x256 (latency point)"),
     ("tile_kernel<1>", "tile M <= 16: 8192x2048 at M = 8, 16 (and 4)"),
     ("tile_kernel<2>", "tile M = 32: 8192x2048"),
-    ("quantize_q8_0_kernel", "quantize_q8_0 1x2048"),
+    ("quantize_q8_0_kernel", "quantize_q8_0 1x2048 (standalone, extra)"),
     ("pack_kernel<8>", "pack Q8_0 (vocab + small)"),
     ("pack_kernel<2>", "pack Q4_0 (all Q4_0 weights)"),
     ("lane_stride_kernel", "read-stream ceiling, lane grid-stride (bench helper)"),
@@ -859,8 +866,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": "decode step over distinct weights: q4_0 2048x2048 (fp32 x; and q8_0 x incl. "
-                        "quantize), ffn q4_0 gate+up 8192x2048 + down 2048x8192, q8_0 vocab 262144x2048, "
+            "workload": "decode step over distinct weights: q4_0 2048x2048 (fp32 x; and q8_0 x quantised in "
+                        "the kernel), ffn q4_0 gate+up 8192x2048 + down 2048x8192, q8_0 vocab 262144x2048, "
                         "prefill tile q4_0 8192x2048 at M=8,16,32",
             "weight_bytes_per_step": step.step_weight_bytes,
             "weight_sets_rotated": args.sets,

@@ -47,6 +47,8 @@ _SIGS = {
     "gq_qmv_q4_0": ([_P, _P, _I64, _I64, _P, _P, _P], _I),
     "gq_qmv_q8_0_q8": ([_P, _P, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "gq_qmv_q4_0_q8": ([_P, _P, _I64, _I64, _P, _P, _P, _P, _P], _I),
+    "gq_qmv_q8_0_q8x": ([_P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P], _I),
+    "gq_qmv_q4_0_q8x": ([_P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P], _I),
     "gq_qffn_gate_up_gelu": ([_P, _P, _P, _P, _I64, _I64, _P, _P, _P], _I),
     "gq_qffn_gate_up_gelu_ex": ([_P, _P, _P, _P, _I64, _I64, _P, _P, _F, _P, _P], _I),
     "gq_qmv_q8_0_ex": ([_P, _P, _I64, _I64, _P, _P, _F, _P, _P, _P], _I),
@@ -213,6 +215,24 @@ def qmv_q8_0_q8(qs, d, n, k, xq, xd, y=None, blockdots=None, stream=None):
 
 def qmv_q4_0_q8(qs, d, n, k, xq, xd, y=None, blockdots=None, stream=None):
     return _qmv_q8("gq_qmv_q4_0_q8", qs, d, n, k, xq, xd, y, blockdots, stream)
+
+
+def _qmv_q8x(fn, qs, d, n, k, x, y, blockdots, xq_out, xd_out, stream):
+    torch = _torch()
+    if y is None:
+        y = _like(x, (n,), torch.float32)
+    _call(fn, _ptr(qs, "qs"), _ptr(d, "d"), n, k, _ptr(x, "x"), _ptr(xq_out, "xq_out"), _ptr(xd_out, "xd_out"),
+          _ptr(y, "y"), _ptr(blockdots, "blockdots"), _stream(stream))
+    return y
+
+
+def qmv_q8_0_q8x(qs, d, n, k, x, y=None, blockdots=None, xq_out=None, xd_out=None, stream=None):
+    """Integer path quantising the fp32 x itself (no separate quantise launch)."""
+    return _qmv_q8x("gq_qmv_q8_0_q8x", qs, d, n, k, x, y, blockdots, xq_out, xd_out, stream)
+
+
+def qmv_q4_0_q8x(qs, d, n, k, x, y=None, blockdots=None, xq_out=None, xd_out=None, stream=None):
+    return _qmv_q8x("gq_qmv_q4_0_q8x", qs, d, n, k, x, y, blockdots, xq_out, xd_out, stream)
 
 
 def qmv_q8_0_ex(qs, d, n, k, x, norm_weight=None, norm_eps=1e-6, residual=None, y=None, stream=None):

@@ -139,6 +139,23 @@ int qmv_q8(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k, co
     return status_of(gq::launch_qmv_q8(type, qs, d, n, k, xq, xd, y, blockdots, as_stream(stream)));
 }
 
+int qmv_q8x(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k, const float* x,
+            int8_t* xq_out, uint16_t* xd_out, float* y, int32_t* blockdots, void* stream) {
+    if (x == nullptr || y == nullptr || (xq_out == nullptr) != (xd_out == nullptr)) return GQ_ERR_NULL;
+    int st = check_weights(type, qs, d, n, k);
+    if (st != GQ_OK) return st;
+    if (!aligned(x, 16) || !aligned(y, 4) || !aligned(blockdots, 4) || !aligned(xq_out, 16) ||
+        !aligned(xd_out, 2))
+        return GQ_ERR_ALIGN;
+    const Range outs[] = {{y, static_cast<size_t>(n) * 4},
+                          {blockdots, blockdots ? static_cast<size_t>(n) * static_cast<size_t>(k / 32) * 4 : 0},
+                          {xq_out, xq_out ? static_cast<size_t>(k) : 0},
+                          {xd_out, xd_out ? static_cast<size_t>(k / 32) * 2 : 0}};
+    const Range ins[] = {{qs, qs_bytes(type, n, k)}, {d, d_bytes(n, k)}, {x, static_cast<size_t>(k) * 4}};
+    if (any_alias(outs, ins)) return GQ_ERR_ALIAS;
+    return status_of(gq::launch_qmv_q8x(type, qs, d, n, k, x, xq_out, xd_out, y, blockdots, as_stream(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -246,6 +263,16 @@ int gq_qmv_q8_0_q8(const int8_t* qs, const uint16_t* d, int64_t n, int64_t k, co
 int gq_qmv_q4_0_q8(const uint8_t* qs, const uint16_t* d, int64_t n, int64_t k, const int8_t* xq,
                    const uint16_t* xd, float* y, int32_t* blockdots, void* stream) {
     return qmv_q8(GQ_TYPE_Q4_0, qs, d, n, k, xq, xd, y, blockdots, stream);
+}
+
+int gq_qmv_q8_0_q8x(const int8_t* qs, const uint16_t* d, int64_t n, int64_t k, const float* x, int8_t* xq_out,
+                    uint16_t* xd_out, float* y, int32_t* blockdots, void* stream) {
+    return qmv_q8x(GQ_TYPE_Q8_0, qs, d, n, k, x, xq_out, xd_out, y, blockdots, stream);
+}
+
+int gq_qmv_q4_0_q8x(const uint8_t* qs, const uint16_t* d, int64_t n, int64_t k, const float* x, int8_t* xq_out,
+                    uint16_t* xd_out, float* y, int32_t* blockdots, void* stream) {
+    return qmv_q8x(GQ_TYPE_Q4_0, qs, d, n, k, x, xq_out, xd_out, y, blockdots, stream);
 }
 
 }  // extern "C"

@@ -72,4 +72,38 @@ __device__ __forceinline__ float gelu_tanh(float t) {
     return t / (1.0f + expf(-2.0f * z));
 }
 
+// ---- Q8_0 activation quantiser, eight lanes per 32-element block ---------
+// Each lane holds four consecutive elements of one block and the block's
+// eight lanes are an aligned group of a wave (all active). Returns the
+// lane's four codes packed little-endian and sets the block's binary16
+// scale bits: amax (fp32, exact) -> d = binary16(amax / 127) (fp32 divide,
+// round to nearest even) -> q = clamp(round half away(x / d), -127, 127)
+// with the divide in fp32 by the rounded d; q = 0 when d == 0 (the
+// activation quantiser of the jouleclaw-loader-gguf BENCHMARKS page, "Matmul
+// throughput -- Q8_0 scalar vs NEON", taken per GGUF 32-element block). The
+// same code serves the standalone quantiser and the prologue of the fused
+// integer-path matvec, so both give identical codes.
+__device__ __forceinline__ uint32_t quantize_q8_0_lane4(const float4 v, uint16_t& scale_bits) {
+    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    amax = fmaxf(amax, dpp_f32<kDppQuadSwap1>(amax));
+    amax = fmaxf(amax, dpp_f32<kDppQuadSwap2>(amax));
+    amax = fmaxf(amax, dpp_f32<kDppRowHalfMirror>(amax));
+    const uint16_t hb = float_to_half_bits(amax / 127.0f);
+    const float dh = half_bits_to_float(hb);
+    scale_bits = hb;
+    const float e[4] = {v.x, v.y, v.z, v.w};
+    uint32_t w = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        int q = 0;
+        if (dh != 0.0f) {
+            float r = roundf(e[b] / dh);
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            q = static_cast<int>(r);
+        }
+        w |= (static_cast<uint32_t>(q) & 0xFFu) << (8 * b);
+    }
+    return w;
+}
+
 }  // namespace gq

@@ -50,6 +50,9 @@ hipError_t launch_qmv_q8(int type, const void* qs, const uint16_t* d, int64_t n,
                          const int8_t* xq, const uint16_t* xd, float* y, int32_t* blockdots,
                          hipStream_t stream);
 
+hipError_t launch_qmv_q8x(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k, const float* x,
+                          int8_t* xq_out, uint16_t* xd_out, float* y, int32_t* blockdots, hipStream_t stream);
+
 hipError_t launch_ffn_gate_up(const uint8_t* g_qs, const uint16_t* g_d, const uint8_t* u_qs,
                               const uint16_t* u_d, int64_t n_ff, int64_t k, const float* x,
                               const float* norm_w, float norm_eps, float* h, hipStream_t stream);

@@ -43,21 +43,13 @@ hipError_t launch_pack(int type, const uint8_t* blocks, int64_t n, int64_t k, ui
 }
 
 // ---------------------------------------------------------------------------
-// Q8_0 activation quantiser: amax (fp32) -> d = binary16(amax / 127) (fp32
-// divide, then round to nearest even) -> q = clamp(round-half-away(x / d),
-// -127, 127) with the divide in fp32 by the rounded d; q = 0 when d == 0.
-// The fp32 divides are IEEE correctly rounded (no fast-math) so both the
-// codes and the scale are reproducible bit for bit. fp32 activation -> int8
-// codes + scale is the activation quantiser of the jouleclaw-loader-gguf
-// BENCHMARKS page ("Matmul throughput -- Q8_0 scalar vs NEON"), taken per
-// 32-element block.
-//
-// Eight lanes share a block, four elements each: one 16-byte load per lane,
-// the block's amax by a max over the eight lanes with DPP (max is exact, so
-// the order does not matter), four divides per lane, one 4-byte store per
-// lane (a wave writes 256 contiguous code bytes) and the scale from the
-// block's first lane. The blocks of all m rows are one flat sequence (x,
-// xq and xd are contiguous row after row).
+// Q8_0 activation quantiser (quantize_q8_0_lane4 in gq_device.hpp holds the
+// arithmetic). Eight lanes share a block, four elements each: one 16-byte
+// load per lane, the block's amax by a max over the eight lanes with DPP
+// (max is exact, so the order does not matter), four divides per lane, one
+// 4-byte store per lane (a wave writes 256 contiguous code bytes) and the
+// scale from the block's first lane. The blocks of all m rows are one flat
+// sequence (x, xq and xd are contiguous row after row).
 // ---------------------------------------------------------------------------
 constexpr int kQuantLanesPerBlock = 8;
 
@@ -70,25 +62,9 @@ void quantize_q8_0_kernel(const float* __restrict__ x, int64_t nblocks, int8_t* 
     // group of a wave, so a group is either entirely in range or entirely out
     if (blk >= nblocks) return;
     const float4 v = reinterpret_cast<const float4*>(x)[t];
-    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    amax = fmaxf(amax, dpp_f32<kDppQuadSwap1>(amax));
-    amax = fmaxf(amax, dpp_f32<kDppQuadSwap2>(amax));
-    amax = fmaxf(amax, dpp_f32<kDppRowHalfMirror>(amax));
-    const uint16_t hb = float_to_half_bits(amax / 127.0f);
-    const float dh = half_bits_to_float(hb);
+    uint16_t hb;
+    const uint32_t w = quantize_q8_0_lane4(v, hb);
     if ((t & (kQuantLanesPerBlock - 1)) == 0) xd[blk] = hb;
-    const float e[4] = {v.x, v.y, v.z, v.w};
-    uint32_t w = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        int q = 0;
-        if (dh != 0.0f) {
-            float r = roundf(e[b] / dh);
-            r = fminf(fmaxf(r, -127.0f), 127.0f);
-            q = static_cast<int>(r);
-        }
-        w |= (static_cast<uint32_t>(q) & 0xFFu) << (8 * b);
-    }
     reinterpret_cast<uint32_t*>(xq)[t] = w;
 }
 

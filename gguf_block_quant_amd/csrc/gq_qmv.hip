@@ -75,6 +75,8 @@ struct QmvParams {
     const float* norm_w;    // optional RMSNorm weight [k] (prologue on x)
     const float* residual;  // optional residual [n] added to the output
     unsigned long long* part;  // optional argmax partials [gridDim.x]
+    int8_t* xq_out;         // integer path quantising x itself: optional codes out [k]
+    uint16_t* xd_out;       // ... and scales out [k/32] (written by workgroup 0)
     float norm_eps;
     float softcap;          // > 0: output = softcap * tanh(output / softcap)
     int n;
@@ -192,6 +194,12 @@ void qmv_kernel(const QmvParams p) {
     constexpr bool kStage = (MODE != kQ8X) && (WS == 1);
     constexpr int kPitch = EPU + 4;
     __shared__ float xstage[kStage ? NI * kWave * kPitch : 1];
+    // integer path with the quantiser folded in: the workgroup's Q8_0 codes
+    // (4 per word) and binary16 scales of all of x
+    constexpr bool kQuantX = (MODE == kQ8X) && FOLD;
+    constexpr int kQxWords = kQuantX ? WS * NI * kWave * EPU / 4 : 1;
+    __shared__ uint32_t qx_s[kQxWords];
+    __shared__ uint16_t qd_s[kQuantX ? kQxWords / 8 : 1];
     __shared__ float nss[WAVES];
 
     // ---- this lane's units ------------------------------------------------
@@ -304,6 +312,24 @@ void qmv_kernel(const QmvParams p) {
             dxr[i] = 0.f; sxr[i] = 0;
         }
     } else {
+        if constexpr (kQuantX) {
+            // The quantiser as a prologue: every workgroup quantises all of x
+            // (k floats, eight lanes per 32-block, the same arithmetic as the
+            // standalone quantiser) into LDS, so no separate launch is needed;
+            // workgroup 0 also writes the codes and scales out if asked.
+            const int nf4 = p.k >> 2;
+            for (int j = threadIdx.x; j < nf4; j += WAVES * kWave) {
+                uint16_t hb;
+                const uint32_t w = quantize_q8_0_lane4(reinterpret_cast<const float4*>(p.x)[j], hb);
+                qx_s[j] = w;
+                if ((j & 7) == 0) qd_s[j >> 3] = hb;
+                if (blockIdx.x == 0 && p.xq_out != nullptr) {
+                    reinterpret_cast<uint32_t*>(p.xq_out)[j] = w;
+                    if ((j & 7) == 0) p.xd_out[j >> 3] = hb;
+                }
+            }
+            __syncthreads();
+        }
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int e0 = unit[i] * EPU;
@@ -317,14 +343,25 @@ void qmv_kernel(const QmvParams p) {
                 }
                 dxr[i] = 0.f; sxr[i] = 0;
             } else {
-                const uint4* xs = reinterpret_cast<const uint4*>(p.xq + e0);
+                if constexpr (kQuantX) {
+                    const uint4* xs = reinterpret_cast<const uint4*>(&qx_s[uload[i] * (EPU / 4)]);
 #pragma unroll
-                for (int v = 0; v < EPU / 16; ++v) {
-                    const uint4 t = uvalid[i] ? xs[v] : make_uint4(0u, 0u, 0u, 0u);
-                    xqr[i][4 * v + 0] = t.x; xqr[i][4 * v + 1] = t.y;
-                    xqr[i][4 * v + 2] = t.z; xqr[i][4 * v + 3] = t.w;
+                    for (int v = 0; v < EPU / 16; ++v) {
+                        const uint4 t = uvalid[i] ? xs[v] : make_uint4(0u, 0u, 0u, 0u);
+                        xqr[i][4 * v + 0] = t.x; xqr[i][4 * v + 1] = t.y;
+                        xqr[i][4 * v + 2] = t.z; xqr[i][4 * v + 3] = t.w;
+                    }
+                    dxr[i] = uvalid[i] ? half_bits_to_float(qd_s[uload[i] >> SH]) : 0.f;
+                } else {
+                    const uint4* xs = reinterpret_cast<const uint4*>(p.xq + e0);
+#pragma unroll
+                    for (int v = 0; v < EPU / 16; ++v) {
+                        const uint4 t = uvalid[i] ? xs[v] : make_uint4(0u, 0u, 0u, 0u);
+                        xqr[i][4 * v + 0] = t.x; xqr[i][4 * v + 1] = t.y;
+                        xqr[i][4 * v + 2] = t.z; xqr[i][4 * v + 3] = t.w;
+                    }
+                    dxr[i] = uvalid[i] ? half_bits_to_float(p.xd[unit[i] >> SH]) : 0.f;
                 }
-                dxr[i] = uvalid[i] ? half_bits_to_float(p.xd[unit[i] >> SH]) : 0.f;
                 int sx = 0;
                 if constexpr (TYPE == kTypeQ4_0) {
 #pragma unroll
@@ -555,7 +592,10 @@ hipError_t launch_variant(QmvParams p, hipStream_t stream, int* grid_out) {
 
 template <int TYPE, int MODE, int NI, int WS, int R>
 hipError_t launch_rows(QmvParams p, hipStream_t stream, int* grid_out) {
-    const bool fold = p.norm_w != nullptr || p.residual != nullptr || p.softcap > 0.0f || p.part != nullptr;
+    // the folded variant: the fp32 prologue/epilogue folds, or (integer path)
+    // the activation quantiser as a prologue
+    const bool fold = p.norm_w != nullptr || p.residual != nullptr || p.softcap > 0.0f || p.part != nullptr ||
+                      (MODE == kQ8X && p.x != nullptr);
     if (fold) return launch_variant<TYPE, MODE, NI, WS, R, true>(p, stream, grid_out);
     return launch_variant<TYPE, MODE, NI, WS, R, false>(p, stream, grid_out);
 }
@@ -644,6 +684,13 @@ hipError_t launch_qmv_q8(int type, const void* qs, const uint16_t* d, int64_t n,
     QmvParams p = base_params(qs, d, n, k, 16);
     p.xq = xq; p.xd = xd; p.y = y; p.blockdots = blockdots;
     return dispatch<kTypeQ4_0, kQ8X>(p, stream);
+}
+
+hipError_t launch_qmv_q8x(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k, const float* x,
+                          int8_t* xq_out, uint16_t* xd_out, float* y, int32_t* blockdots, hipStream_t stream) {
+    QmvParams p = base_params(qs, d, n, k, type == kTypeQ8_0 ? 32 : 16);
+    p.x = x; p.xq_out = xq_out; p.xd_out = xd_out; p.y = y; p.blockdots = blockdots;
+    return type == kTypeQ8_0 ? dispatch<kTypeQ8_0, kQ8X>(p, stream) : dispatch<kTypeQ4_0, kQ8X>(p, stream);
 }
 
 hipError_t launch_ffn_gate_up(const uint8_t* g_qs, const uint16_t* g_d, const uint8_t* u_qs,

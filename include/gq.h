@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define GQ_ABI_VERSION 3
+#define GQ_ABI_VERSION 4
 
 enum {
     GQ_OK = 0,
@@ -204,6 +204,27 @@ int gq_qmv_q8_0_q8(const int8_t *qs, const uint16_t *d, int64_t n, int64_t k,
 int gq_qmv_q4_0_q8(const uint8_t *qs, const uint16_t *d, int64_t n, int64_t k,
                    const int8_t *xq, const uint16_t *xd, float *y,
                    int32_t *blockdots, void *stream);
+
+/*
+ * gq_qmv_q8_0_q8x / gq_qmv_q4_0_q8x -- the same integer path with the
+ * activation quantiser folded in as a prologue: x fp32 [k] is quantised to
+ * Q8_0 exactly as gq_quantize_q8_0 does (every workgroup quantises the
+ * vector itself, so there is no separate launch and the codes never leave
+ * the chip), then S, y and blockdots are as in gq_qmv_*_q8 on those codes,
+ * bit for bit. If xq_out and xd_out are given (both or neither, else
+ * GQ_ERR_NULL), the codes (int8 [k], 16-byte aligned) and scales (binary16
+ * bits [k/32]) are also written there, for later calls on the same
+ * activations. Inputs must be finite. Folding the quantiser into its
+ * consumer follows the jouleclaw-loader-gguf BENCHMARKS page, where the
+ * direct Q8_0 kernel takes fp32 activations and quantises them per call
+ * ("Matmul throughput -- Q8_0 scalar vs NEON"). Maximum k: 32768.
+ */
+int gq_qmv_q8_0_q8x(const int8_t *qs, const uint16_t *d, int64_t n, int64_t k,
+                    const float *x, int8_t *xq_out, uint16_t *xd_out, float *y,
+                    int32_t *blockdots, void *stream);
+int gq_qmv_q4_0_q8x(const uint8_t *qs, const uint16_t *d, int64_t n, int64_t k,
+                    const float *x, int8_t *xq_out, uint16_t *xd_out, float *y,
+                    int32_t *blockdots, void *stream);
 
 /*
  * gq_qffn_gate_up_gelu -- first half of the gated FFN, one pass over both

@@ -40,7 +40,7 @@ def test_header_symbols_all_exported():
 
 
 def test_version_and_status_strings():
-    assert gq.abi_version() == 3
+    assert gq.abi_version() == 4
     for s in range(8):
         assert gq.status_str(s)
     assert gq.status_str(99) == "unknown status"
@@ -94,6 +94,25 @@ def test_qmv_q8_validation(fn):
     assert f(A, B, 64, 256, C, E, D, D + 2, None) == ALIGN
     assert f(A, B, 64, 256, C, E, D, D + 128, None) == ALIAS      # blockdots over y
     assert f(A, B, 64, 256, C, E, D, A + 1024, None) == ALIAS     # blockdots over qs
+
+
+@pytest.mark.parametrize("fn", ["gq_qmv_q8_0_q8x", "gq_qmv_q4_0_q8x"])
+def test_qmv_q8x_validation(fn):
+    """(qs, d, n, k, x, xq_out, xd_out, y, blockdots, stream)"""
+    f = getattr(L, fn)
+    assert f(A, B, 64, 256, None, None, None, D, None, None) == NULL
+    assert f(A, B, 64, 256, C, None, None, None, None, None) == NULL
+    assert f(A, B, 64, 256, C, E, None, D, None, None) == NULL             # codes out without scales out
+    assert f(A, B, 64, 256, C, None, E, D, None, None) == NULL
+    assert f(A, B, 64, 250, C, None, None, D, None, None) == SHAPE
+    assert f(A, B, 64, 65536, C, None, None, D, None, None) == UNSUP
+    assert f(A, B, 64, 256, C + 4, None, None, D, None, None) == ALIGN     # x 16 B
+    assert f(A, B, 64, 256, C, E + 8, E + 4096, D, None, None) == ALIGN    # codes out 16 B
+    assert f(A, B, 64, 256, C, E, E + 4097, D, None, None) == ALIGN        # scales out 2 B
+    assert f(A, B, 64, 256, C, None, None, C + 512, None, None) == ALIAS   # y over x
+    assert f(A, B, 64, 256, C, C, E, D, None, None) == ALIAS               # codes out over x
+    assert f(A, B, 64, 256, C, E, D, D, None, None) == ALIAS               # scales out over y
+    assert f(A, B, 64, 256, C, None, None, D, D + 64, None) == ALIAS       # blockdots over y
 
 
 def test_ffn_validation():

@@ -196,6 +196,38 @@ INT_SHAPES = [(Q4, 2048, 2048), (Q8, 64, 256), (Q4, 1, 32), (Q8, 1, 32), (Q4, 99
               (Q8, 777, 1056), (Q4, 300, 8192), (Q8, 300, 8192), (Q4, 33, 32768)]
 
 
+def _qmv8x(qtype):
+    return gq.qmv_q8_0_q8x if qtype == Q8 else gq.qmv_q4_0_q8x
+
+
+@pytest.mark.parametrize("qtype,n,k", INT_SHAPES)
+def test_qmv_q8x_equals_quantise_then_q8(qtype, n, k):
+    """The fused quantiser prologue gives the standalone quantiser's codes and
+    the same block dots and outputs bit for bit, and matches the oracle."""
+    rng = np.random.default_rng(3 * n + k)
+    w = synth.weights(rng, qtype, n, k)
+    x = synth.activations(rng, k) * np.float32(rng.uniform(0.1, 10.0))
+    qs, d = packed(gq, qtype, w, n, k)
+    xg = up(x)
+    xq, xd = gq.quantize_q8_0(xg)
+    bd_ref = torch.empty((n, k // 32), dtype=torch.int32, device="cuda")
+    y_ref = down(_qmv8(qtype)(qs, d, n, k, xq, xd, blockdots=bd_ref))
+    bd = torch.full((n, k // 32), 7, dtype=torch.int32, device="cuda")
+    xq_out = torch.full((k,), 99, dtype=torch.int8, device="cuda")
+    xd_out = torch.zeros((k // 32,), dtype=torch.int16, device="cuda")
+    y = down(_qmv8x(qtype)(qs, d, n, k, xg, blockdots=bd, xq_out=xq_out, xd_out=xd_out))
+    assert np.array_equal(down(xq_out), down(xq)) and np.array_equal(down(xd_out), down(xd))
+    assert np.array_equal(down(bd), down(bd_ref))
+    assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32))
+    # without the optional outputs
+    y2 = down(_qmv8x(qtype)(qs, d, n, k, xg))
+    assert np.array_equal(y2.view(np.uint32), y_ref.view(np.uint32))
+    rq, rd = oracle.quantize_q8_0(x)
+    S, yr, ar = oracle.blockdots(qtype, w, n, k, rq, rd)
+    assert np.array_equal(down(bd), S[0])
+    check_within(y, yr[0], oracle.fp32_path_bound(ar[0]), "fused int path")
+
+
 @pytest.mark.parametrize("qtype,n,k", INT_SHAPES)
 def test_qmv_q8_block_dots_exact(qtype, n, k):
     rng = np.random.default_rng(n + k)
