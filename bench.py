@@ -631,8 +631,9 @@ KERNEL_LABELS = [
     ("qmv_kernel<2, 1, 1, 1, 2, false>", "qmv Q4_0 Q8_0 x: 2048x2048 (pre-quantised, extra)"),
     ("qmv_kernel<2, 1, 1, 1, 2, true>", "qmv Q4_0 Q8_0 x quantised in the prologue: 2048x2048"),
     ("qmv_kernel<8, 0, 1, 1, 2, false>", "qmv Q8_0 fp32 x: 64x256 (latency point)"),
-    ("tile_kernel<1>", "tile M <= 16: 8192x2048 at M = 8, 16 (and 4)"),
-    ("tile_kernel<2>", "tile M = 32: 8192x2048"),
+    ("tile_kernel<1, true>", "tile M <= 8, paired blocks: 8192x2048 at M = 8 (and 4)"),
+    ("tile_kernel<1, false>", "tile M <= 16: 8192x2048 at M = 16"),
+    ("tile_kernel<2, false>", "tile M <= 32: 8192x2048 at M = 32"),
     ("quantize_q8_0_kernel", "quantize_q8_0 1x2048 (standalone, extra)"),
     ("pack_kernel<8>", "pack Q8_0 (vocab + small)"),
     ("pack_kernel<2>", "pack Q4_0 (all Q4_0 weights)"),
