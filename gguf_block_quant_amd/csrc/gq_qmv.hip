@@ -20,6 +20,8 @@
 // an M == 1 product wants its own kernel rather than a tiled GEMM, follow the
 // SafeC Gemma 4 DESIGN_NOTES page ("A dedicated GEMV kernel for the M==1
 // decode step") and the Gemma-4-E2B raw-Metal port page ("Why this exists").
+#include <atomic>
+
 #include "gq_device.hpp"
 #include "gq_launch.hpp"
 
@@ -561,6 +563,22 @@ constexpr int kMaxGrid = GQ_QMV_MAX_GRID;
 // Workgroups of a kernel that can be resident at once on the device: the
 // persistent grid is never larger, so no workgroup waits for a second round.
 // The per-kernel occupancy is a property of the code object, queried once.
+// Compute units of the current device, queried once per device.
+inline int device_cus() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    if (dev >= 0 && dev < kMaxDevices) cached[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
 template <typename K>
 int resident_workgroups(K kernel, int threads) {
     static const int per_cu = [&] {
@@ -568,11 +586,7 @@ int resident_workgroups(K kernel, int threads) {
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kernel, threads, 0) != hipSuccess || b < 1) b = 1;
         return b;
     }();
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-        cus = 256;
-    return per_cu * cus;
+    return per_cu * device_cus();
 }
 
 template <int TYPE, int MODE, int NI, int WS, int R, bool FOLD>

@@ -344,11 +344,13 @@ def test_ffn_large_gate_no_nan():
 # small-M prefill tile
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("m", [8, 16, 32])
+@pytest.mark.parametrize("m", [8, 16, 32, 4])
 def test_tile_workload(m):
+    """The prefill workload at full size (M = 4 is the batched-decode launch:
+    the first four rows of the M = 8 activations)."""
     wl = synth.workload_tile()
     n, k, w = wl["n"], wl["k"], wl["w"]
-    xq, xd = wl["acts"][m]
+    xq, xd = wl["acts"][m] if m in wl["acts"] else (wl["acts"][8][0][:m].copy(), wl["acts"][8][1][:m].copy())
     qs, d = packed(gq, Q4, w, n, k)
     bd = torch.full((m, n, k // 32), -7, dtype=torch.int32, device="cuda")
     y = down(gq.qmm_tile_m(qs, d, n, k, m, up(xq), up(xd), blockdots=bd))
