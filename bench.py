@@ -31,12 +31,15 @@ Also reported beside ``value`` (none of them replaces it):
   read_stream_ceiling  best bandwidth of a plain 16-byte read-and-XOR kernel
                        (libgq_bench.so) over the 512 MiB vocab buffers;
                        breakdown rows give their % of it
-  hot                  a 2048x2048 Q4_0 matvec re-launched on one copy
-                       (last-level-cache resident: a MALL figure, not HBM)
-  latency              the 64x256 Q8_0 matvec: a launch-latency point
   cpu_baseline[_threads]  the fp64 oracle on one thread / on T threads with
                        every matrix split by rows
   breakdown, extras    per-launch medians from HIP events
+  per_config           each workload alone: launches over >= 2 GiB of rotated
+                       weight copies, 7 timed repeats (median, min-max), the
+                       host's issue time per launch, and 64-launch graph
+                       figures over distinct copies and over one copy
+                       (MALL-hot); the 64x256 Q8_0 config is a launch-latency
+                       point, not a roofline point
 
 Modes:
   python bench.py [--steps K --warmup W]    the benchmark (one JSON line)
@@ -207,6 +210,7 @@ class Step:
             wt = {m: pack(Q4, c5["w"], 8192, 2048) for m in (8, 16, 32)}
             self.keep.append((w2a, w2b, wg, wu, wd, wv, wt))
             self.vocab_qs = getattr(self, "vocab_qs", []) + [wv[0]]
+            self.vocab_sets = getattr(self, "vocab_sets", []) + [wv]
             launches = [
                 ("qmv_q4_0 2048x2048", L.gq_qmv_q4_0, (P(w2a[0]), P(w2a[1]), 2048, 2048, P(x2), P(y2a), sp),
                  2048 * 64 * 18, 8192 + 8192),
@@ -240,14 +244,6 @@ class Step:
                 xq4, xd4 = (up(c5["acts"][8][0][:4].copy()), up(c5["acts"][8][1][:4].copy()))
                 y4t = torch.empty((4, 8192), dtype=torch.float32, device=dev)
                 self.keep += [g2, res2, y2c, logits, ws, idx, val, xq4, xd4, y4t]
-                # the smallest config (Q8_0 64 x 256): a launch-latency point
-                c1 = synth.workload_q8_0_small()
-                w1 = pack(Q8, c1["w"], 64, 256)
-                x1, y1 = up(c1["x"]), torch.empty(64, dtype=torch.float32, device=dev)
-                self.keep += [w1, x1, y1]
-                self.latency = ("qmv_q8_0 64x256", L.gq_qmv_q8_0, (P(w1[0]), P(w1[1]), 64, 256, P(x1), P(y1), sp))
-                self.hot = ("qmv_q4_0 2048x2048", L.gq_qmv_q4_0,
-                            (P(w2a[0]), P(w2a[1]), 2048, 2048, P(x2), P(y2a), sp), 2048 * 64 * 18)
                 self.extras = [
                     ("quantize_q8_0 2048 (standalone)", L.gq_quantize_q8_0, (P(x2), 1, 2048, P(xq2), P(xd2), sp), 0,
                      2048 * 4 + 2048 + 128),
@@ -301,6 +297,161 @@ class Step:
                 st = fn(*args)
             if st != 0:
                 raise self.gq.GQError(st, name)
+
+
+def per_config(step, ceiling_gbps, log, rotate_bytes=2 << 30):
+    """Each workload on its own, as a throughput measurement: enough packed
+    copies of its weights to cover >= 2 GiB (so consecutive launches never
+    find their weights in the 256 MB last-level cache), 10 warm-up launches,
+    then 7 repeats of [event, L launches cycling through the copies, event]
+    with L chosen so a repeat takes >= 20 ms; median and min-max per launch.
+    Beside it: a graph figure (64 launches over distinct copies recorded as
+    one chain and replayed, free of the host's per-call cost) and the same
+    over one copy (MALL-hot, not an HBM figure)."""
+    import ctypes
+    import math
+
+    import numpy as np
+    import torch
+
+    import synth
+
+    gq = step.gq
+    L = gq.raw()
+    sp = step.sp
+    dev = torch.device("cuda:0")
+    P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    def copies(qtype, blocks, n, k, count):
+        raw = up(synth.as_bytes(blocks).reshape(-1))
+        out = [gq.pack(qtype, raw, n, k) for _ in range(count)]
+        torch.cuda.synchronize()
+        return out
+
+    Q4, Q8 = gq.TYPE_Q4_0, gq.TYPE_Q8_0
+    host = step.host
+    c1 = synth.workload_q8_0_small()
+    x1, y1 = up(c1["x"]), torch.empty(64, dtype=torch.float32, device=dev)
+    x2, y2 = up(host["c2"]["x"]), torch.empty(2048, dtype=torch.float32, device=dev)
+    xq2 = torch.empty(2048, dtype=torch.int8, device=dev)
+    xd2 = torch.empty(64, dtype=torch.int16, device=dev)
+    x3, h3 = up(host["c3"]["x"]), torch.empty(8192, dtype=torch.float32, device=dev)
+    y3 = torch.empty(2048, dtype=torch.float32, device=dev)
+    x4, y4 = up(host["c4"]["x"]), torch.empty(262144, dtype=torch.float32, device=dev)
+    acts = {m: (up(host["c5"]["acts"][m][0]), up(host["c5"]["acts"][m][1])) for m in (8, 16, 32)}
+    yt = {m: torch.empty((m, 8192), dtype=torch.float32, device=dev) for m in (8, 16, 32)}
+
+    def ncopies(nbytes):
+        return max(2, math.ceil(rotate_bytes / nbytes))
+
+    rows = []
+    w1 = copies(Q8, c1["w"], 64, 256, 64)
+    rows.append(("C1 qmv_q8_0 64x256", 64 * 8 * 34, 1024 + 256,
+                 [(L.gq_qmv_q8_0, (P(q), P(d), 64, 256, P(x1), P(y1), sp)) for q, d in w1]))
+    w2 = copies(Q4, host["c2"]["w"], 2048, 2048, ncopies(2359296))
+    rows.append(("C2 qmv_q4_0 2048x2048 fp32 x", 2359296, 8192 + 8192,
+                 [(L.gq_qmv_q4_0, (P(q), P(d), 2048, 2048, P(x2), P(y2), sp)) for q, d in w2]))
+    rows.append(("C2 qmv_q4_0_q8x 2048x2048 (Q8_0 x, quantised in the kernel)", 2359296, 8192 + 2176 + 8192,
+                 [(L.gq_qmv_q4_0_q8x, (P(q), P(d), 2048, 2048, P(x2), P(xq2), P(xd2), P(y2), None, sp))
+                  for q, d in w2]))
+    nf = ncopies(3 * 9437184)
+    wg = copies(Q4, host["c3"]["wg"], 8192, 2048, nf)
+    wu = copies(Q4, host["c3"]["wu"], 8192, 2048, nf)
+    wd = copies(Q4, host["c3"]["wd"], 2048, 8192, nf)
+    gate_up = [(L.gq_qffn_gate_up_gelu, (P(g[0]), P(g[1]), P(u[0]), P(u[1]), 8192, 2048, P(x3), P(h3), sp))
+               for g, u in zip(wg, wu)]
+    down = [(L.gq_qmv_q4_0, (P(q), P(d), 2048, 8192, P(h3), P(y3), sp)) for q, d in wd]
+    rows.append(("C3 qffn_gate_up_gelu 2x8192x2048", 2 * 9437184, 8192 + 32768, gate_up))
+    rows.append(("C3 down qmv_q4_0 2048x8192", 9437184, 32768 + 8192, down))
+    rows.append(("C3 FFN gate+up then down (pairs)", 3 * 9437184, 8192 + 2 * 32768 + 8192,
+                 [pair for pair in zip(gate_up, down)]))
+    rows.append(("C4 qmv_q8_0 262144x2048", 570425344, 8192 + 1048576,
+                 [(L.gq_qmv_q8_0, (P(q), P(d), 262144, 2048, P(x4), P(y4), sp)) for q, d in step.vocab_sets]))
+    w5 = copies(Q4, host["c5"]["w"], 8192, 2048, ncopies(9437184))
+    for m in (8, 16, 32):
+        rows.append(("C5 qmm_tile_m 8192x2048 M=%d" % m, 9437184, m * 2176 + m * 8192 * 4,
+                     [(L.gq_qmm_tile_m, (P(q), P(d), 8192, 2048, m, P(acts[m][0]), P(acts[m][1]), P(yt[m]), None,
+                                         sp)) for q, d in w5]))
+    keep = [w1, w2, wg, wu, wd, w5, x1, y1, x2, y2, xq2, xd2, x3, h3, y3, x4, y4, acts, yt]
+
+    def issue(launch):
+        for fn, fargs in (launch if isinstance(launch[0], tuple) else (launch,)):
+            if fn(*fargs) != 0:
+                raise RuntimeError("launch failed in the per-config pass")
+
+    out = {}
+    for name, wbytes, obytes, launches in rows:
+        nl = len(launches)
+        for i in range(10):
+            issue(launches[i % nl])
+        torch.cuda.synchronize()
+        # launches per repeat: >= 20 ms, from a first estimate
+        a, b = TimingEvent(), TimingEvent()
+        a.record(step.stream)
+        for i in range(min(nl, 64)):
+            issue(launches[i % nl])
+        b.record(step.stream)
+        torch.cuda.synchronize()
+        est_us = a.elapsed_time(b) * 1e3 / min(nl, 64)
+        per = max(nl, int(math.ceil(20000.0 / max(est_us, 0.5))))
+        reps, host = [], []
+        for _ in range(7):
+            a, b = TimingEvent(), TimingEvent()
+            a.record(step.stream)
+            t0 = time.perf_counter()
+            for i in range(per):
+                issue(launches[i % nl])
+            host.append((time.perf_counter() - t0) * 1e6 / per)
+            b.record(step.stream)
+            torch.cuda.synchronize()
+            reps.append(a.elapsed_time(b) * 1e3 / per)
+        reps.sort()
+        med = reps[3]
+        host_us = sorted(host)[3]
+        def graph_us(pick):
+            """64 launches recorded as one chain, replayed 7 times: per-launch
+            device time without the host's per-call cost."""
+            chain = gq.Chain(step.stream)
+            with chain:
+                for i in range(64):
+                    issue(launches[pick(i)])
+            chain.launch(step.stream)
+            torch.cuda.synchronize()
+            a, b = TimingEvent(), TimingEvent()
+            a.record(step.stream)
+            for _ in range(7):
+                chain.launch(step.stream)
+            b.record(step.stream)
+            torch.cuda.synchronize()
+            chain.close()
+            return a.elapsed_time(b) * 1e3 / (7 * 64)
+
+        graph_cold = graph_us(lambda i: i % nl)      # distinct copies
+        graph_hot = graph_us(lambda i: 0)            # one copy: MALL-resident after the first
+        out[name] = {
+            "median_us": round(med, 3), "min_us": round(reps[0], 3), "max_us": round(reps[-1], 3),
+            "launches_per_repeat": per, "copies_rotated": nl,
+            "weight_GBps": round(wbytes / med / 1e3, 1), "total_GBps": round((wbytes + obytes) / med / 1e3, 1),
+            "pct_of_8TBps": round(100.0 * wbytes / med / 1e3 / HBM_PEAK_GBPS, 1),
+            "pct_of_read_ceiling": round(100.0 * (wbytes + obytes) / med / 1e3 / ceiling_gbps, 1),
+            "calls_per_s": round(1e6 / med, 1),
+            "tokens_per_s_at_0.783GB": round(wbytes / med / 1e3 / 0.783, 1),
+            "graph_us_per_launch": round(graph_cold, 3), "graph_hot_MALL_us_per_launch": round(graph_hot, 3),
+            # the host's own time to issue one launch through the C ABI; where
+            # it reaches median_us the eager figure is host-bound and the graph
+            # figure is the device's
+            "host_issue_us": round(host_us, 3),
+        }
+        log("per-config %s: %.2f us (%.0f GB/s)" % (name, med, wbytes / med / 1e3))
+    del keep
+    torch.cuda.synchronize()
+    return out
 
 
 def _event_times(step, fn, fargs, reps):
@@ -721,6 +872,7 @@ def main():
     ap.add_argument("--sets", type=int, default=2, help="rotated copies of the step's weights")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true", help="skip the per-workload throughput pass")
     ap.add_argument("--mode", choices=["bench", "pmc", "pmc-step"], default="bench")
     ap.add_argument("--pmc-summary", default=None)
     ap.add_argument("--counters-summary", default=None,
@@ -835,17 +987,7 @@ def main():
     for n, b in breakdown.items():
         if b["weight_GBps"]:
             b["pct_of_read_ceiling"] = round(100.0 * b["total_GBps"] / ceiling["GBps"], 1)
-
-    # MALL-hot: one small matrix launched back to back (served from the
-    # 256 MB last-level cache after the first launch; never an HBM figure)
-    name, fn, fargs, wb = step.hot
-    us = _event_times(step, fn, fargs, 100)
-    hot = {"kernel": name, "median_us": round(us[len(us) // 2], 2),
-           "MALL_GBps": round(wb / us[len(us) // 2] / 1e3, 1)}
-    name, fn, fargs = step.latency
-    us = _event_times(step, fn, fargs, 100)
-    latency = {"kernel": name, "median_us": round(us[len(us) // 2], 2), "min_us": round(us[0], 2),
-               "note": "launch-latency point (17,408 weight bytes), not a roofline point"}
+    configs = None if args.no_per_config else per_config(step, ceiling["GBps"], log)
 
     traffic = load_traffic()
     cpu = cpu_threads = None
@@ -892,14 +1034,13 @@ def main():
         "cpu_baseline_threads": cpu_threads,
         "chained": chained,
         "read_stream_ceiling": ceiling,
-        "hot": hot,
-        "latency": latency,
         "tokens_per_s_projection": {
             "value": round(value / 0.783, 1),
             "note": "effective GB/s / 0.783 GB per token (the byte budget per decoded token quoted "
                     "for the int2/int4/int8 Gemma-4-E2B port); context only"},
         "breakdown": breakdown,
         "extras": extras,
+        "per_config": configs,
     }
     print(json.dumps(out), flush=True)
 

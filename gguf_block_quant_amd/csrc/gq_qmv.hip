@@ -28,6 +28,9 @@
 #ifndef GQ_QMV_MAX_GRID
 #define GQ_QMV_MAX_GRID 1024   // workgroups of 4 waves (4 per CU on 256 CUs)
 #endif
+#ifndef GQ_QMV_R_SHORT
+#define GQ_QMV_R_SHORT 2         // rows per wave step for shorter (n < 65536) un-split matrices
+#endif
 #ifndef GQ_QMV_R_FFN
 #define GQ_QMV_R_FFN 2           // rows per wave step of the gate+up pass (each a gate and an up row)
 #endif
@@ -628,7 +631,7 @@ hipError_t launch_cfg(QmvParams p, hipStream_t stream, int* grid_out) {
         return launch_rows<TYPE, MODE, NI, WS, GQ_QMV_R_SPLIT>(p, stream, grid_out);
     } else {
         if (p.n >= 65536) return launch_rows<TYPE, MODE, NI, WS, GQ_QMV_R_TALL>(p, stream, grid_out);
-        return launch_rows<TYPE, MODE, NI, WS, (MODE == kFFN ? GQ_QMV_R_FFN : 2)>(p, stream, grid_out);
+        return launch_rows<TYPE, MODE, NI, WS, (MODE == kFFN ? GQ_QMV_R_FFN : GQ_QMV_R_SHORT)>(p, stream, grid_out);
     }
 }
 
