@@ -198,11 +198,17 @@ void qmv_kernel(const QmvParams p) {
     // fp32 activations of un-split rows are staged through LDS (below)
     constexpr bool kStage = (MODE != kQ8X) && (WS == 1);
     constexpr int kPitch = EPU + 4;
-    __shared__ float xstage[kStage ? NI * kWave * kPitch : 1];
+    constexpr int kThreads = WAVES * kWave;
+    // float4s of x per thread when staging; the LDS copy is padded to whole
+    // rounds of the workgroup so every thread writes its slots unconditionally
+    constexpr int kStageF4 = kStage ? (NI * kWave * EPU / 4 + kThreads - 1) / kThreads : 0;
+    constexpr int kStageUnits = kStage ? (kStageF4 * kThreads * 4 + EPU - 1) / EPU : 1;
+    __shared__ float xstage[kStage ? kStageUnits * kPitch : 1];
     // integer path with the quantiser folded in: the workgroup's Q8_0 codes
     // (4 per word) and binary16 scales of all of x
     constexpr bool kQuantX = (MODE == kQ8X) && FOLD;
-    constexpr int kQxWords = kQuantX ? WS * NI * kWave * EPU / 4 : 1;
+    constexpr int kQuantF4 = kQuantX ? (WS * NI * kWave * EPU / 4 + kThreads - 1) / kThreads : 0;
+    constexpr int kQxWords = kQuantX ? kQuantF4 * kThreads : 1;       // whole rounds, as above
     __shared__ uint32_t qx_s[kQxWords];
     __shared__ uint16_t qd_s[kQuantX ? kQxWords / 8 : 1];
     __shared__ float nss[WAVES];
@@ -249,11 +255,44 @@ void qmv_kernel(const QmvParams p) {
             }
     };
 
-    // The first row group's loads go out before the activations are read:
-    // they do not depend on them and are the long-latency (HBM) part.
+    // Loads of the activations that the workgroup stages (fp32 x, and the
+    // RMSNorm weight; or x for the folded quantiser) go out first, then the
+    // first row group's weights: loads complete in issue order, so waiting
+    // for the activations (an L2 hit) does not wait for the weights (HBM),
+    // and the staging overlaps the weights' flight.
+    bool norm = false;
+    if constexpr (MODE != kQ8X && FOLD) norm = p.norm_w != nullptr;
+    const int nf4 = p.k >> 2;
+    constexpr int kPreF4 = kStageF4 > kQuantF4 ? kStageF4 : kQuantF4;    // at most one is nonzero
+    float4 xpre[kPreF4 > 0 ? kPreF4 : 1];
+    float4 gpre[(kStage && FOLD) ? kStageF4 : 1];
+    if constexpr (kPreF4 > 0) {
+        // unconditional (clamped) loads: straight-line code lets the wait
+        // before the LDS writes count only these loads
+#pragma unroll
+        for (int u = 0; u < kPreF4; ++u) {
+            const int j = min(static_cast<int>(threadIdx.x) + u * kThreads, nf4 - 1);
+            xpre[u] = reinterpret_cast<const float4*>(p.x)[j];
+        }
+        if constexpr (kStage && FOLD) {
+            const float4* g4 = reinterpret_cast<const float4*>(norm ? p.norm_w : p.x);
+#pragma unroll
+            for (int u = 0; u < kStageF4; ++u) {
+                const int j = min(static_cast<int>(threadIdx.x) + u * kThreads, nf4 - 1);
+                gpre[u] = g4[j];
+            }
+        }
+    }
+
+    // (the grid never exceeds the row-group iterations, so every workgroup's
+    // first group exists; the load is unconditional, which also keeps the
+    // activation waits above exact)
+    // keep the scheduler from hoisting the weight loads above the activation
+    // loads (the point of the order above)
+    if constexpr (kPreF4 > 0) __builtin_amdgcn_sched_barrier(0);
     int it = blockIdx.x;
 #if GQ_QMV_CARRY
-    if (it * SUBS < p.row_groups) load_group((it * SUBS + sub) * R);
+    load_group((it * SUBS + sub) * R);
 #endif
 
     // ---- activation registers for this lane's units ----------------------
@@ -267,8 +306,6 @@ void qmv_kernel(const QmvParams p) {
     float dxr[NI];
     int sxr[NI];
     float ss = 0.f;
-    bool norm = false;
-    if constexpr (MODE != kQ8X && FOLD) norm = p.norm_w != nullptr;
     if constexpr (kStage) {
         // Un-split rows: every wave of the workgroup needs all of x, so the
         // workgroup reads it (and w) from memory once into LDS, padded to a
@@ -276,12 +313,14 @@ void qmv_kernel(const QmvParams p) {
         // consecutive units do not collide in a bank, and the waves copy
         // their slices from there. Without this each wave re-reads the same
         // few KiB, which for short matrices is more traffic than the weights.
-        const int nf4 = p.k >> 2;
-        for (int j = threadIdx.x; j < nf4; j += WAVES * kWave) {
-            float4 t = reinterpret_cast<const float4*>(p.x)[j];
+        // slots past k get zeros (never read: lanes read units < p.units)
+#pragma unroll
+        for (int u = 0; u < kStageF4; ++u) {
+            const int j = threadIdx.x + u * kThreads;
+            float4 t = j < nf4 ? xpre[u] : make_float4(0.f, 0.f, 0.f, 0.f);
             if constexpr (FOLD) {
                 if (norm) {
-                    const float4 g = reinterpret_cast<const float4*>(p.norm_w)[j];
+                    const float4 g = gpre[u];
                     ss = fmaf(t.x, t.x, ss); ss = fmaf(t.y, t.y, ss);
                     ss = fmaf(t.z, t.z, ss); ss = fmaf(t.w, t.w, ss);
                     t.x *= g.x; t.y *= g.y; t.z *= g.z; t.w *= g.w;
@@ -322,13 +361,17 @@ void qmv_kernel(const QmvParams p) {
             // (k floats, eight lanes per 32-block, the same arithmetic as the
             // standalone quantiser) into LDS, so no separate launch is needed;
             // workgroup 0 also writes the codes and scales out if asked.
-            const int nf4 = p.k >> 2;
-            for (int j = threadIdx.x; j < nf4; j += WAVES * kWave) {
+            // every lane quantises (zeros past k, into padding slots that are
+            // never read); only the codes of x itself are written out
+#pragma unroll
+            for (int u = 0; u < kQuantF4; ++u) {
+                const int j = threadIdx.x + u * kThreads;
                 uint16_t hb;
-                const uint32_t w = quantize_q8_0_lane4(reinterpret_cast<const float4*>(p.x)[j], hb);
+                const uint32_t w =
+                    quantize_q8_0_lane4(j < nf4 ? xpre[u] : make_float4(0.f, 0.f, 0.f, 0.f), hb);
                 qx_s[j] = w;
                 if ((j & 7) == 0) qd_s[j >> 3] = hb;
-                if (blockIdx.x == 0 && p.xq_out != nullptr) {
+                if (blockIdx.x == 0 && p.xq_out != nullptr && j < nf4) {
                     reinterpret_cast<uint32_t*>(p.xq_out)[j] = w;
                     if ((j & 7) == 0) p.xd_out[j >> 3] = hb;
                 }
