@@ -777,7 +777,7 @@ KERNEL_LABELS = [
     ("qmv_kernel<2, 2, 1, 1, 2, false>", "FFN gate+up GELU: 2 x 8192x2048 Q4_0"),
     ("qmv_kernel<2, 2, 1, 1, 2, true>", "FFN gate+up GELU + rmsnorm"),
     ("qmv_kernel<2, 0, 1, 4, 8, false>", "qmv Q4_0 fp32 x: down 2048x8192"),
-    ("qmv_kernel<2, 0, 1, 1, 2, false>", "qmv Q4_0 fp32 x: 2048x2048 (step + MALL-hot runs)"),
+    ("qmv_kernel<2, 0, 1, 1, 2, false>", "qmv Q4_0 fp32 x: 2048x2048"),
     ("qmv_kernel<2, 0, 1, 1, 2, true>", "qmv Q4_0 + rmsnorm + residual: 2048x2048"),
     ("qmv_kernel<2, 1, 1, 1, 2, false>", "qmv Q4_0 Q8_0 x: 2048x2048 (pre-quantised, extra)"),
     ("qmv_kernel<2, 1, 1, 1, 2, true>", "qmv Q4_0 Q8_0 x quantised in the prologue: 2048x2048"),
@@ -810,6 +810,8 @@ def stats_summary(args):
         "#       --output-format csv -- python3 $R/bench.py > $R/%s.log" % run_dir.rstrip("/"),
         "#   python3 bench.py --stats-summary %s --write-profile" % run_dir,
         "# durations in microseconds; kernel_source_hash = %s" % kernel_source_hash(),
+        "# calls cover the whole run: warm-up, the timed steps, the breakdown, the extras and the",
+        "# per-config pass (eager and graph launches, MALL-hot), so an average mixes those contexts",
         "%-58s %6s %9s %9s %9s" % ("kernel", "calls", "avg_us", "min_us", "max_us"),
     ]
     dom = None
