@@ -284,12 +284,46 @@ void qmv_kernel(const QmvParams p) {
         }
     }
 
+    // The other paths read their lane's activation slice straight into
+    // registers; those loads go out before the weights as well (clamped
+    // units, masked below), so the first row's dot waits for its own loads
+    // rather than for the whole group.
+    constexpr bool kDirect = !kStage && !kQuantX;
+    constexpr bool kDirectF = kDirect && MODE != kQ8X;
+    constexpr bool kDirectQ = kDirect && MODE == kQ8X;
+    float4 xd4[kDirectF ? NI : 1][kDirectF ? EPU / 4 : 1];
+    float4 gd4[(kDirectF && FOLD) ? NI : 1][(kDirectF && FOLD) ? EPU / 4 : 1];
+    uint4 xq4[kDirectQ ? NI : 1][kDirectQ ? EPU / 16 : 1];
+    uint16_t xdb[NI];
+    if constexpr (kDirectF) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int v = 0; v < EPU / 4; ++v) xd4[i][v] = reinterpret_cast<const float4*>(p.x + uload[i] * EPU)[v];
+        if constexpr (FOLD) {
+            const float* gsrc = norm ? p.norm_w : p.x;
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+#pragma unroll
+                for (int v = 0; v < EPU / 4; ++v)
+                    gd4[i][v] = reinterpret_cast<const float4*>(gsrc + uload[i] * EPU)[v];
+        }
+    }
+    if constexpr (kDirectQ) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+#pragma unroll
+            for (int v = 0; v < EPU / 16; ++v) xq4[i][v] = reinterpret_cast<const uint4*>(p.xq + uload[i] * EPU)[v];
+            xdb[i] = p.xd[uload[i] >> SH];
+        }
+    }
+
     // (the grid never exceeds the row-group iterations, so every workgroup's
     // first group exists; the load is unconditional, which also keeps the
     // activation waits above exact)
     // keep the scheduler from hoisting the weight loads above the activation
     // loads (the point of the order above)
-    if constexpr (kPreF4 > 0) __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_sched_barrier(0);
     int it = blockIdx.x;
 #if GQ_QMV_CARRY
     load_group((it * SUBS + sub) * R);
@@ -380,12 +414,10 @@ void qmv_kernel(const QmvParams p) {
         }
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int e0 = unit[i] * EPU;
             if constexpr (MODE != kQ8X) {
-                const float4* xs = reinterpret_cast<const float4*>(p.x + e0);
 #pragma unroll
                 for (int v = 0; v < EPU / 4; ++v) {
-                    const float4 t = uvalid[i] ? xs[v] : make_float4(0.f, 0.f, 0.f, 0.f);
+                    const float4 t = uvalid[i] ? xd4[i][v] : make_float4(0.f, 0.f, 0.f, 0.f);
                     xr[i][4 * v + 0] = t.x; xr[i][4 * v + 1] = t.y;
                     xr[i][4 * v + 2] = t.z; xr[i][4 * v + 3] = t.w;
                 }
@@ -401,14 +433,13 @@ void qmv_kernel(const QmvParams p) {
                     }
                     dxr[i] = uvalid[i] ? half_bits_to_float(qd_s[uload[i] >> SH]) : 0.f;
                 } else {
-                    const uint4* xs = reinterpret_cast<const uint4*>(p.xq + e0);
 #pragma unroll
                     for (int v = 0; v < EPU / 16; ++v) {
-                        const uint4 t = uvalid[i] ? xs[v] : make_uint4(0u, 0u, 0u, 0u);
+                        const uint4 t = uvalid[i] ? xq4[i][v] : make_uint4(0u, 0u, 0u, 0u);
                         xqr[i][4 * v + 0] = t.x; xqr[i][4 * v + 1] = t.y;
                         xqr[i][4 * v + 2] = t.z; xqr[i][4 * v + 3] = t.w;
                     }
-                    dxr[i] = uvalid[i] ? half_bits_to_float(p.xd[unit[i] >> SH]) : 0.f;
+                    dxr[i] = uvalid[i] ? half_bits_to_float(xdb[i]) : 0.f;
                 }
                 int sx = 0;
                 if constexpr (TYPE == kTypeQ4_0) {
@@ -425,10 +456,9 @@ void qmv_kernel(const QmvParams p) {
             if (norm) {
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
-                    const float4* ws4 = reinterpret_cast<const float4*>(p.norm_w + uload[i] * EPU);
 #pragma unroll
                     for (int v = 0; v < EPU / 4; ++v) {
-                        const float4 g = ws4[v];
+                        const float4 g = gd4[i][v];
                         ss = fmaf(xr[i][4 * v + 0], xr[i][4 * v + 0], ss);
                         ss = fmaf(xr[i][4 * v + 1], xr[i][4 * v + 1], ss);
                         ss = fmaf(xr[i][4 * v + 2], xr[i][4 * v + 2], ss);
