@@ -34,9 +34,6 @@
 #ifndef GQ_QMV_R_FFN
 #define GQ_QMV_R_FFN 2           // rows per wave step of the gate+up pass (each a gate and an up row)
 #endif
-#ifndef GQ_QMV_MAX_GRID_FFN
-#define GQ_QMV_MAX_GRID_FFN 512  // the gate+up pass: fewer, longer-lived workgroups (measured)
-#endif
 #ifndef GQ_QMV_CARRY
 #define GQ_QMV_CARRY 1         // issue the next row group's loads before this one's reduction
 #endif
@@ -673,7 +670,7 @@ hipError_t launch_variant(QmvParams p, hipStream_t stream, int* grid_out) {
     const int64_t iters = (static_cast<int64_t>(p.row_groups) + SUBS - 1) / SUBS;
     const auto kernel = qmv_kernel<TYPE, MODE, NI, WS, R, FOLD>;
     int64_t cap = resident_workgroups(kernel, WAVES * kWave);
-    const int64_t max_grid = (MODE == kFFN ? GQ_QMV_MAX_GRID_FFN : kMaxGrid) * 4 / WAVES;
+    const int64_t max_grid = kMaxGrid * 4 / WAVES;
     cap = cap < max_grid ? cap : max_grid;
     const int grid = static_cast<int>(iters < cap ? iters : cap);
     if (grid_out != nullptr) *grid_out = grid;
