@@ -25,8 +25,8 @@
 // contiguous 16-byte global loads (the weight rows stream from HBM in
 // 512- or 256-byte runs per row; the activations are
 // shared by every workgroup and come from L2), while the registers already
-// hold the next chunk's loads. The four waves split the chunk's blocks; their
-// fp32 partials meet in LDS and are added in wave order (deterministic).
+// hold the next chunk's loads. The eight waves split the chunk's blocks;
+// their fp32 partials meet in LDS and are added in wave order (deterministic).
 // LDS rows are padded so the MFMA fragment reads are bank-conflict free.
 #include "gq_device.hpp"
 #include "gq_launch.hpp"
@@ -40,6 +40,12 @@ namespace {
 #ifndef GQ_TILE_CHUNK1
 #define GQ_TILE_CHUNK1 32
 #endif
+#ifndef GQ_TILE_THREADS1
+#define GQ_TILE_THREADS1 512     // workgroup size for one activation tile (8 waves, measured)
+#endif
+#ifndef GQ_TILE_THREADS2
+#define GQ_TILE_THREADS2 512     // ... and for two (measured)
+#endif
 #ifndef GQ_TILE_CHUNK2
 #define GQ_TILE_CHUNK2 16        // two row tiles: shorter chunks keep the LDS and registers in budget (measured)
 #endif
@@ -49,9 +55,11 @@ constexpr int kRows = 16;                          // weight rows per workgroup
 // (mod 256 = 32), so the fragment reads of the 16 rows spread over the banks.
 template <int MT> struct Tiling {
     static constexpr int kChunk = MT == 1 ? GQ_TILE_CHUNK1 : GQ_TILE_CHUNK2;
+    static constexpr int kThreads = MT == 1 ? GQ_TILE_THREADS1 : GQ_TILE_THREADS2;
+    static constexpr int kWaves = kThreads / kWave;
     static constexpr int kWPitch = kChunk * 16 + 16;
     static constexpr int kXPitch = kChunk * 32 + 32;
-    static constexpr int kWavePart = kChunk / kWavesPerBlock;   // blocks per wave per chunk
+    static constexpr int kWavePart = kChunk / kWaves;            // blocks per wave per chunk
 };
 #ifndef GQ_TILE_BATCH
 #define GQ_TILE_BATCH 8
@@ -71,6 +79,7 @@ template <int MT> struct Tiling {
 // blocks whose MFMAs issue before their epilogues (smaller for two row tiles,
 // whose batches carry twice the scales and results)
 template <int MT> struct Batch { static constexpr int value = MT == 1 ? GQ_TILE_BATCH : GQ_TILE_BATCH2; };
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
 
 // 8 unsigned nibbles (4 bytes) -> 8 signed bytes q - 8:
 // (q + 120) ^ 0x80 per byte is q - 8 in two's complement; q + 120 <= 135
@@ -79,27 +88,30 @@ __device__ __forceinline__ uint32_t nib_to_s8(uint32_t v) {
     return (v + 0x78787878u) ^ 0x80808080u;
 }
 
-template <int MR, int CH>
+template <int MR, int CH, int T>
 struct Stage {                                      // one chunk's global loads, in registers
-    static constexpr int WV = kRows * CH / kBlockThreads;           // 16-B weight pieces / thread
-    static constexpr int XV = MR * CH * 2 / kBlockThreads;          // 16-B activation pieces / thread
-    static constexpr int DXV = MR * CH / kBlockThreads;             // activation scales / thread
-    static constexpr int DWV = kRows * CH / kBlockThreads;          // weight scales / thread
-    static_assert(WV >= 1 && XV >= 1 && DXV >= 1 && DWV >= 1, "chunk too short for the workgroup");
+    // pieces of the chunk, and per thread (rounded up; threads past the
+    // total skip the last round)
+    static constexpr int kW = kRows * CH, kX = MR * CH * 2, kDX = MR * CH, kDW = kRows * CH;
+    static constexpr int WV = (kW + T - 1) / T;     // 16-B weight pieces / thread
+    static constexpr int XV = (kX + T - 1) / T;     // 16-B activation pieces / thread
+    static constexpr int DXV = (kDX + T - 1) / T;   // activation scales / thread
+    static constexpr int DWV = (kDW + T - 1) / T;   // weight scales / thread
     uint4 w[WV];
     uint4 x[XV];
     uint16_t dx[DXV];
     uint16_t dw[DWV];
 };
 
-template <int MR, int CH>
-__device__ __forceinline__ void stage_load(Stage<MR, CH>& st, int tid, int cb, int cn, int n0, int n, int nb,
+template <int MR, int CH, int T>
+__device__ __forceinline__ void stage_load(Stage<MR, CH, T>& st, int tid, int cb, int cn, int n0, int n, int nb,
                                            int m, int64_t k, const uint8_t* qs, const uint16_t* d,
                                            const int8_t* xq, const uint16_t* xd) {
     const int row_bytes = nb * 16;
 #pragma unroll
-    for (int i = 0; i < Stage<MR, CH>::WV; ++i) {
-        const int e = tid + i * kBlockThreads;
+    for (int i = 0; i < Stage<MR, CH, T>::WV; ++i) {
+        const int e = tid + i * T;
+        if (Stage<MR, CH, T>::kW % T != 0 && e >= Stage<MR, CH, T>::kW) break;
         const int row = e / CH, b = e % CH;                  // a row's pieces are consecutive
         const uint8_t* src = qs + static_cast<int64_t>(min(n0 + row, n - 1)) * row_bytes + (cb + b) * 16;
         if (b < cn) {
@@ -111,22 +123,25 @@ __device__ __forceinline__ void stage_load(Stage<MR, CH>& st, int tid, int cb, i
         }
     }
 #pragma unroll
-    for (int i = 0; i < Stage<MR, CH>::XV; ++i) {
-        const int e = tid + i * kBlockThreads;
+    for (int i = 0; i < Stage<MR, CH, T>::XV; ++i) {
+        const int e = tid + i * T;
+        if (Stage<MR, CH, T>::kX % T != 0 && e >= Stage<MR, CH, T>::kX) break;
         const int row = e / (2 * CH), piece = e % (2 * CH);
         st.x[i] = (row < m && piece < 2 * cn)
                       ? *reinterpret_cast<const uint4*>(xq + row * k + cb * 32 + piece * 16)
                       : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
-    for (int i = 0; i < Stage<MR, CH>::DXV; ++i) {
-        const int e = tid + i * kBlockThreads;
+    for (int i = 0; i < Stage<MR, CH, T>::DXV; ++i) {
+        const int e = tid + i * T;
+        if (Stage<MR, CH, T>::kDX % T != 0 && e >= Stage<MR, CH, T>::kDX) break;
         const int b = e / MR, row = e % MR;
         st.dx[i] = (row < m && b < cn) ? xd[static_cast<int64_t>(row) * nb + cb + b] : uint16_t(0);
     }
 #pragma unroll
-    for (int i = 0; i < Stage<MR, CH>::DWV; ++i) {
-        const int e = tid + i * kBlockThreads;
+    for (int i = 0; i < Stage<MR, CH, T>::DWV; ++i) {
+        const int e = tid + i * T;
+        if (Stage<MR, CH, T>::kDW % T != 0 && e >= Stage<MR, CH, T>::kDW) break;
         const int b = e / kRows, row = e % kRows;
         st.dw[i] = (b < cn) ? d[static_cast<int64_t>(min(n0 + row, n - 1)) * nb + cb + b] : uint16_t(0);
     }
@@ -140,7 +155,7 @@ __device__ __forceinline__ void stage_load(Stage<MR, CH>& st, int tid, int cb, i
 // are S for block b and rows 8..15 S for block b+1, and no MFMA row or
 // epilogue lane is spent on padding.
 template <int MT, bool PAIR>
-__global__ __launch_bounds__(kBlockThreads)
+__global__ __launch_bounds__(Tiling<MT>::kThreads)
 void tile_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d, int n, int nb,
                  int m, const int8_t* __restrict__ xq, const uint16_t* __restrict__ xd,
                  float* __restrict__ y, int32_t* __restrict__ blockdots) {
@@ -150,12 +165,14 @@ void tile_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
     constexpr int kWPitch = Tiling<MT>::kWPitch;
     constexpr int kXPitch = Tiling<MT>::kXPitch;
     constexpr int kWavePart = Tiling<MT>::kWavePart;
-    using St = Stage<MR, kChunk>;
+    constexpr int kThreads = Tiling<MT>::kThreads;
+    constexpr int kWaves = Tiling<MT>::kWaves;
+    using St = Stage<MR, kChunk, kThreads>;
     __shared__ __align__(16) uint8_t ws[kRows][kWPitch];
     __shared__ __align__(16) int8_t xs[MR][kXPitch];
     __shared__ __align__(16) float dxs[kChunk][MR];
     __shared__ __align__(16) float dws[kChunk][kRows];
-    __shared__ __align__(16) float part[kWavesPerBlock][MT][4][kWave];
+    __shared__ __align__(16) float part[kWaves][MT][4][kWave];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -173,35 +190,39 @@ void tile_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
         for (int v = 0; v < 4; ++v) acc[t][v] = 0.f;
 
     St st;
-    stage_load<MR, kChunk>(st, tid, 0, min(kChunk, nb), n0, n, nb, m, k, qs, d, xq, xd);
+    stage_load<MR, kChunk, kThreads>(st, tid, 0, min(kChunk, nb), n0, n, nb, m, k, qs, d, xq, xd);
 
     for (int cb = 0; cb < nb; cb += kChunk) {
         const int cn = min(kChunk, nb - cb);
         // registers -> LDS
 #pragma unroll
         for (int i = 0; i < St::WV; ++i) {
-            const int e = tid + i * kBlockThreads;
+            const int e = tid + i * kThreads;
+            if (St::kW % kThreads != 0 && e >= St::kW) break;
             *reinterpret_cast<uint4*>(&ws[e / kChunk][(e % kChunk) * 16]) = st.w[i];
         }
 #pragma unroll
         for (int i = 0; i < St::XV; ++i) {
-            const int e = tid + i * kBlockThreads;
+            const int e = tid + i * kThreads;
+            if (St::kX % kThreads != 0 && e >= St::kX) break;
             *reinterpret_cast<uint4*>(&xs[e / (2 * kChunk)][(e % (2 * kChunk)) * 16]) = st.x[i];
         }
 #pragma unroll
         for (int i = 0; i < St::DXV; ++i) {
-            const int e = tid + i * kBlockThreads;
+            const int e = tid + i * kThreads;
+            if (St::kDX % kThreads != 0 && e >= St::kDX) break;
             dxs[e / MR][e % MR] = half_bits_to_float(st.dx[i]);
         }
 #pragma unroll
         for (int i = 0; i < St::DWV; ++i) {
-            const int e = tid + i * kBlockThreads;
+            const int e = tid + i * kThreads;
+            if (St::kDW % kThreads != 0 && e >= St::kDW) break;
             dws[e / kRows][e % kRows] = half_bits_to_float(st.dw[i]);
         }
         __syncthreads();
         // the next chunk's global loads fly while this chunk computes
         if (cb + kChunk < nb)
-            stage_load<MR, kChunk>(st, tid, cb + kChunk, min(kChunk, nb - cb - kChunk), n0, n, nb, m, k, qs, d,
+            stage_load<MR, kChunk, kThreads>(st, tid, cb + kChunk, min(kChunk, nb - cb - kChunk), n0, n, nb, m, k, qs, d,
                                    xq, xd);
 
         // this wave's blocks of the chunk, kBatch at a time: the batch's
@@ -216,7 +237,7 @@ void tile_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
             // block where the copy matches (c < 8 with s < 2, c >= 8 with s >= 2),
             // zeros elsewhere. D value v of lane (s, c): activation row
             // 4 (s & 1) + v, weight row c, block bl + (s >> 1).
-            constexpr int kPairs = GQ_TILE_PAIR_BATCH;
+            constexpr int kPairs = cmin(GQ_TILE_PAIR_BATCH, kWavePart / 2);
             static_assert(kWavePart % (2 * kPairs) == 0, "a wave's blocks of a chunk must be whole pair batches");
             const int half = s >> 1;
             const bool live = (c < 8) == (half == 0);
@@ -268,7 +289,7 @@ void tile_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
                 }
             }
         } else {
-            constexpr int kBatch = Batch<MT>::value;
+            constexpr int kBatch = cmin(Batch<MT>::value, kWavePart);
             static_assert(kWavePart % kBatch == 0, "a wave's blocks of a chunk must be whole batches");
 #pragma unroll GQ_TILE_JB_UNROLL
             for (int jb = 0; jb < kWavePart; jb += kBatch) {
@@ -327,7 +348,7 @@ void tile_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
         __syncthreads();   // LDS is rewritten by the next chunk
     }
 
-    // add the four waves' partials in wave order (and, for paired blocks, the
+    // add the waves' partials in wave order (and, for paired blocks, the
     // two lane halves holding even and odd blocks) and store
 #pragma unroll
     for (int t = 0; t < MT; ++t)
@@ -340,19 +361,19 @@ void tile_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
             const int v = tid / 32;
             float tot = part[0][0][v][l] + part[0][0][v][l + 32];
 #pragma unroll
-            for (int w = 1; w < kWavesPerBlock; ++w) tot += part[w][0][v][l] + part[w][0][v][l + 32];
+            for (int w = 1; w < kWaves; ++w) tot += part[w][0][v][l] + part[w][0][v][l + 32];
             const int mrow = 4 * (l >> 4) + v;
             const int col = n0 + (l & 15);
             if (mrow < m && col < n) y[static_cast<int64_t>(mrow) * n + col] = tot;
         }
     } else {
-        for (int e = tid; e < MT * 4 * kWave; e += kBlockThreads) {
+        for (int e = tid; e < MT * 4 * kWave; e += kThreads) {
             const int l = e % kWave;
             const int v = (e / kWave) % 4;
             const int t = e / (kWave * 4);
             float tot = part[0][t][v][l];
 #pragma unroll
-            for (int w = 1; w < kWavesPerBlock; ++w) tot += part[w][t][v][l];
+            for (int w = 1; w < kWaves; ++w) tot += part[w][t][v][l];
             const int mrow = 16 * t + 4 * (l >> 4) + v;
             const int col = n0 + (l & 15);
             if (mrow < m && col < n) y[static_cast<int64_t>(mrow) * n + col] = tot;
@@ -368,12 +389,12 @@ hipError_t launch_tile_q4_0(const uint8_t* qs, const uint16_t* d, int64_t n, int
     const int grid = static_cast<int>((n + kRows - 1) / kRows);
     const int nb = static_cast<int>(k / 32);
     if (GQ_TILE_PAIRS && m <= 8)
-        return launch_kernel(tile_kernel<1, true>, dim3(grid), dim3(kBlockThreads), stream, qs, d,
+        return launch_kernel(tile_kernel<1, true>, dim3(grid), dim3(Tiling<1>::kThreads), stream, qs, d,
                              static_cast<int>(n), nb, m, xq, xd, y, blockdots);
     if (m <= 16)
-        return launch_kernel(tile_kernel<1, false>, dim3(grid), dim3(kBlockThreads), stream, qs, d,
+        return launch_kernel(tile_kernel<1, false>, dim3(grid), dim3(Tiling<1>::kThreads), stream, qs, d,
                              static_cast<int>(n), nb, m, xq, xd, y, blockdots);
-    return launch_kernel(tile_kernel<2, false>, dim3(grid), dim3(kBlockThreads), stream, qs, d,
+    return launch_kernel(tile_kernel<2, false>, dim3(grid), dim3(Tiling<2>::kThreads), stream, qs, d,
                          static_cast<int>(n), nb, m, xq, xd, y, blockdots);
 }
 
