@@ -776,7 +776,7 @@ KERNEL_LABELS = [
     ("argmax_reduce_kernel", "argmax stage 2 (one workgroup)"),
     ("qmv_kernel<2, 2, 1, 1, 2, false>", "FFN gate+up GELU: 2 x 8192x2048 Q4_0"),
     ("qmv_kernel<2, 2, 1, 1, 2, true>", "FFN gate+up GELU + rmsnorm"),
-    ("qmv_kernel<2, 0, 1, 4, 8, false>", "qmv Q4_0 fp32 x: down 2048x8192"),
+    ("qmv_kernel<2, 0, 1, 4, 4, false>", "qmv Q4_0 fp32 x: down 2048x8192"),
     ("qmv_kernel<2, 0, 1, 1, 2, false>", "qmv Q4_0 fp32 x: 2048x2048"),
     ("qmv_kernel<2, 0, 1, 1, 2, true>", "qmv Q4_0 + rmsnorm + residual: 2048x2048"),
     ("qmv_kernel<2, 1, 1, 1, 2, false>", "qmv Q4_0 Q8_0 x: 2048x2048 (pre-quantised, extra)"),
@@ -794,11 +794,43 @@ KERNEL_LABELS = [
 ]
 
 
+def _bench_line(path):
+    """The JSON result line of a bench.py run's output file, or None."""
+    if not path or not os.path.exists(path):
+        return None
+    found = None
+    for line in open(path):
+        if line.startswith("{"):
+            found = json.loads(line)
+    return found
+
+
+def _timed_trace_average(run_dir, run):
+    """Average duration (us) of the dominant kernel's dispatches inside the
+    timed region, from the kernel trace: its launches in dispatch order are W
+    warm-up steps, then the K timed steps."""
+    if run is None:
+        return None
+    files = glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        return None
+    durs = []
+    for r in csv.DictReader(open(files[0])):
+        if "qmv_kernel<8, 0, 2, 1, 4, false>" in r["Kernel_Name"]:
+            durs.append((int(r["Dispatch_Id"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    durs.sort()
+    w, k = run["warmup"], run["steps"]
+    sel = [d for _, d in durs[w:w + k]]
+    if len(sel) != k:
+        return None
+    return sum(sel) / len(sel) / 1e3
+
+
 def stats_summary(args):
     """Kernel table of a rocprofv3 --kernel-trace --stats run of the default
     benchmark, with the dominant kernel's rocprof average beside the live
     HIP-event average of the same run."""
-    run_dir = args.stats_summary
+    run_dir, _, bench_json = args.stats_summary.partition(",")
     files = glob.glob(os.path.join(run_dir, "**", "*kernel_stats.csv"), recursive=True)
     if not files:
         raise SystemExit("no kernel_stats.csv under %s" % run_dir)
@@ -808,7 +840,8 @@ def stats_summary(args):
         "# command (repository root R on the GPU host):",
         "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d $R/%s -o run \\" % run_dir,
         "#       --output-format csv -- python3 $R/bench.py > $R/%s.log" % run_dir.rstrip("/"),
-        "#   python3 bench.py --stats-summary %s --write-profile" % run_dir,
+        "#   python3 bench.py --stats-summary %s --write-profile"
+        % (run_dir + ("," + bench_json if bench_json else "")),
         "# durations in microseconds; kernel_source_hash = %s" % kernel_source_hash(),
         "# calls cover the whole run: warm-up, the timed steps, the breakdown, the extras and the",
         "# per-config pass (eager and graph launches, MALL-hot), so an average mixes those contexts",
@@ -822,20 +855,28 @@ def stats_summary(args):
         if "qmv_kernel<8, 0, 2, 1, 4, false>" in r["Name"]:
             dom = float(r["AverageNs"]) / 1e3
     log_file = run_dir.rstrip("/") + ".log"
-    ev = None
-    if os.path.exists(log_file):
-        for line in open(log_file):
-            if line.startswith("{"):
-                ev = json.loads(line)["roofline"]["avg_launch_us"]
+    run = _bench_line(log_file)
+    timed = _timed_trace_average(run_dir, run)
     if dom is not None:
         alg = 262144 * 64 * 34 + 2048 * 4 + 262144 * 4
         lines.append("")
         lines.append("# dominant kernel (vocab): %d B / %.2f us = %.2f TB/s = %.1f%% of 8 TB/s (rocprof average)"
                      % (alg, dom, alg / dom / 1e6, alg / dom / 1e6 / 8.0 * 100))
-        if ev is not None:
-            lines.append("# the same run's live HIP-event average over the timed launches: %.2f us (events bracket "
-                         "each launch, so they add the event-record overhead; difference %.1f%%)"
-                         % (ev, (ev / dom - 1) * 100))
+        if timed is not None:
+            lines.append("# rocprof average over the timed region's launches only (the kernel's dispatches W+1..W+K "
+                         "in the trace): %.2f us = %.1f%% of 8 TB/s" % (timed, alg / timed / 1e6 / 8.0 * 100))
+        if run is not None:
+            ev = run["roofline"]["avg_launch_us"]
+            lines.append("# the profiled run's live HIP-event average over the same launches: %.2f us (the events "
+                         "bracket each launch, and under the profiler each dispatch waits for its trace record; "
+                         "difference %.1f%%)" % (ev, (ev / (timed or dom) - 1) * 100))
+        plain = _bench_line(bench_json) if bench_json else None
+        if plain is not None:
+            ev = plain["roofline"]["avg_launch_us"]
+            lines.append("# the same command without the profiler (%s): HIP-event average %.2f us, "
+                         "roofline frac %.3f (difference %.1f%%)"
+                         % (os.path.basename(bench_json), ev, plain["roofline"]["frac"],
+                            (ev / (timed or dom) - 1) * 100))
     text = "\n".join(lines) + "\n"
     print(text)
     if args.write_profile:
@@ -880,7 +921,9 @@ def main():
     ap.add_argument("--counters-summary", default=None,
                     help="A_DIR,B_DIR of the two --mode pmc-step counter runs -> VALU / MFMA table")
     ap.add_argument("--stats-summary", default=None,
-                    help="rocprofv3 --kernel-trace --stats output dir of the default run -> kernel table")
+                    help="DIR[,BENCH_JSON]: rocprofv3 --kernel-trace --stats output dir of the default run "
+                         "(its stdout in DIR.log) and optionally the JSON output of the same command run "
+                         "without the profiler -> kernel table")
     ap.add_argument("--write-profile", action="store_true",
                     help="with --pmc-summary: write the summary under profiles/")
     args = ap.parse_args()

@@ -37,6 +37,9 @@
 #ifndef GQ_QMV_CARRY
 #define GQ_QMV_CARRY 1         // issue the next row group's loads before this one's reduction
 #endif
+#ifndef GQ_QMV_SPLIT_SUBS
+#define GQ_QMV_SPLIT_SUBS 2      // row groups per workgroup when rows are split over 4 waves (at most 16 waves)
+#endif
 #ifndef GQ_QMV_WAVES1
 #define GQ_QMV_WAVES1 4        // waves per workgroup for un-split rows (they share one LDS copy of x)
 #endif
@@ -44,7 +47,7 @@
 #define GQ_QMV_R_TALL 4        // rows per wave step for tall (n >= 65536) un-split matrices
 #endif
 #ifndef GQ_QMV_R_SPLIT
-#define GQ_QMV_R_SPLIT 8         // rows per wave step when a row is split over 4 or 8 waves
+#define GQ_QMV_R_SPLIT 4         // rows per wave step when a row is split over 4 or 8 waves
 #endif
 #ifndef GQ_QMV_NT
 #define GQ_QMV_NT 1            // non-temporal loads for the quant stream (read once)
@@ -171,8 +174,13 @@ __device__ __forceinline__ int unit_dot_q8(const uint4 q, const uint32_t* xr, in
     return s;
 }
 
-// Waves per workgroup for a K split over WS waves: at least 4.
-template <int WS> struct Waves { static constexpr int value = WS < 4 ? 4 : WS; };
+// Waves per workgroup for a K split over WS waves: at least 4; split rows
+// put GQ_QMV_SPLIT_SUBS row groups in one workgroup while that stays within
+// 16 waves (two 4-wave groups of 4 rows each keep more rows in flight per
+// workgroup than one group of 8 rows, at half the registers per lane).
+template <int WS> struct Waves {
+    static constexpr int value = WS < 4 ? 4 : (WS * GQ_QMV_SPLIT_SUBS > 16 ? WS : WS * GQ_QMV_SPLIT_SUBS);
+};
 template <> struct Waves<1> { static constexpr int value = GQ_QMV_WAVES1; };
 
 // FOLD selects the variant with the optional RMSNorm prologue and the
@@ -688,12 +696,12 @@ hipError_t launch_rows(QmvParams p, hipStream_t stream, int* grid_out) {
 }
 
 // Rows per wave step (measured on MI355X): rows split over 4 or 8 waves
-// stream 8 rows at a time to keep enough bytes in flight per wave; very tall
+// stream 4 rows at a time, with two row groups per workgroup; very tall
 // matrices take 4 (each wave loops over many groups); shorter ones take 2
 // so more waves share the dequantisation work.
 template <int TYPE, int MODE, int NI, int WS>
 hipError_t launch_cfg(QmvParams p, hipStream_t stream, int* grid_out) {
-    if constexpr (WS >= 16) {
+    if constexpr (Waves<WS>::value >= 16) {
         // 1024-thread workgroups cap a lane at 128 VGPRs: 4 rows (2 row pairs
         // for the gate+up FFN) fit unspilled
         return launch_rows<TYPE, MODE, NI, WS, (MODE == kFFN ? 2 : 4)>(p, stream, grid_out);

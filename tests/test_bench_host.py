@@ -101,3 +101,30 @@ def test_stats_summary_reports_the_dominant_kernel(tmp_path, capsys):
     assert "%d B / 86.00 us = %.2f TB/s" % (alg, alg / 86.0 / 1e6) in out
     assert "87.72 us" in out and "difference 2.0%" in out
     assert out.index("vocab") < out.index("runtime copy")    # sorted by total time
+
+
+def test_stats_summary_averages_the_timed_region_from_the_trace(tmp_path, capsys):
+    # 2 warm-up and 3 timed vocab launches, then a later (untimed) one; the
+    # profiled run's events read 90 us, the unprofiled run's 88 us
+    d = tmp_path / "prof"
+    d.mkdir()
+    with open(d / "run_kernel_stats.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"])
+        w.writerow([VOCAB, 6, 600000, 100000.0, 90.0, 80000, 200000, 1.0])
+    durs = [200000, 100000, 86000, 86000, 86000, 42000]
+    with open(d / "run_kernel_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writerow([1, COPY, 0, 5000])
+        # written out of dispatch order: the summary sorts by Dispatch_Id
+        for i, dur in reversed(list(enumerate(durs))):
+            w.writerow([10 + i, VOCAB, 1000000 * i, 1000000 * i + dur])
+    (tmp_path / "prof.log").write_text('[bench] x\n{"warmup": 2, "steps": 3, "roofline": {"avg_launch_us": 90.3}}\n')
+    plain = tmp_path / "plain.json"
+    plain.write_text('{"warmup": 2, "steps": 3, "roofline": {"avg_launch_us": 87.72, "frac": 0.81}}\n')
+    bench.stats_summary(argparse.Namespace(stats_summary="%s,%s" % (d, plain), write_profile=False))
+    out = capsys.readouterr().out
+    assert "timed region's launches only" in out and ": 86.00 us" in out
+    assert "90.30 us" in out and "difference 5.0%" in out
+    assert "87.72 us" in out and "difference 2.0%" in out and "0.810" in out
