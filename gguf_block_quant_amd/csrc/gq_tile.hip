@@ -49,6 +49,12 @@ namespace {
 #ifndef GQ_TILE_CHUNK2
 #define GQ_TILE_CHUNK2 16        // two row tiles: shorter chunks keep the LDS and registers in budget (measured)
 #endif
+#ifndef GQ_TILE_DEPTH1
+#define GQ_TILE_DEPTH1 1         // chunks whose global loads are in flight at once (one activation tile; measured)
+#endif
+#ifndef GQ_TILE_DEPTH2
+#define GQ_TILE_DEPTH2 1         // ... (two activation tiles; measured)
+#endif
 constexpr int kRows = 16;                          // weight rows per workgroup
 // Blocks per k chunk, and the LDS pitches that follow from it: a weight row
 // takes CH * 16 + 16 bytes (mod 256 = 16), an activation row CH * 32 + 32
@@ -60,6 +66,7 @@ template <int MT> struct Tiling {
     static constexpr int kWPitch = kChunk * 16 + 16;
     static constexpr int kXPitch = kChunk * 32 + 32;
     static constexpr int kWavePart = kChunk / kWaves;            // blocks per wave per chunk
+    static constexpr int kDepth = MT == 1 ? GQ_TILE_DEPTH1 : GQ_TILE_DEPTH2;
 };
 #ifndef GQ_TILE_BATCH
 #define GQ_TILE_BATCH 8
@@ -103,47 +110,83 @@ struct Stage {                                      // one chunk's global loads,
     uint16_t dw[DWV];
 };
 
+// One chunk's global loads into registers (cn >= 1 blocks of it exist).
+// Every thread issues every load of its pieces, straight-line: a piece that
+// does not exist (past the end of k, past the m activation rows, past the
+// piece count) reads a clamped, valid neighbour instead -- one that another
+// lane reads anyway -- and is zeroed when it is written to LDS. Addresses are
+// a workgroup-uniform base plus a 32-bit lane offset (one VGPR each).
 template <int MR, int CH, int T>
-__device__ __forceinline__ void stage_load(Stage<MR, CH, T>& st, int tid, int cb, int cn, int n0, int n, int nb,
-                                           int m, int64_t k, const uint8_t* qs, const uint16_t* d,
-                                           const int8_t* xq, const uint16_t* xd) {
+__device__ __forceinline__ void stage_load(Stage<MR, CH, T>& st, int tid, int cb, int cn, int rmax, int nb, int m,
+                                           int k, const uint8_t* wbase, const uint16_t* dbase, const int8_t* xq,
+                                           const uint16_t* xd) {
+    using S = Stage<MR, CH, T>;
     const int row_bytes = nb * 16;
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int i = 0; i < Stage<MR, CH, T>::WV; ++i) {
-        const int e = tid + i * T;
-        if (Stage<MR, CH, T>::kW % T != 0 && e >= Stage<MR, CH, T>::kW) break;
-        const int row = e / CH, b = e % CH;                  // a row's pieces are consecutive
-        const uint8_t* src = qs + static_cast<int64_t>(min(n0 + row, n - 1)) * row_bytes + (cb + b) * 16;
-        if (b < cn) {
-            typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-            const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
-            st.w[i] = make_uint4(t.x, t.y, t.z, t.w);
-        } else {
-            st.w[i] = make_uint4(0u, 0u, 0u, 0u);
-        }
+    for (int i = 0; i < S::WV; ++i) {
+        const int e = min(tid + i * T, S::kW - 1);
+        const int row = min(e / CH, rmax), b = min(e % CH, cn - 1);    // a row's pieces are consecutive
+        const uint32_t off = static_cast<uint32_t>(row * row_bytes + (cb + b) * 16);
+        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wbase + off));
+        st.w[i] = make_uint4(t.x, t.y, t.z, t.w);
     }
 #pragma unroll
-    for (int i = 0; i < Stage<MR, CH, T>::XV; ++i) {
-        const int e = tid + i * T;
-        if (Stage<MR, CH, T>::kX % T != 0 && e >= Stage<MR, CH, T>::kX) break;
-        const int row = e / (2 * CH), piece = e % (2 * CH);
-        st.x[i] = (row < m && piece < 2 * cn)
-                      ? *reinterpret_cast<const uint4*>(xq + row * k + cb * 32 + piece * 16)
-                      : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < S::XV; ++i) {
+        const int e = min(tid + i * T, S::kX - 1);
+        const int row = min(e / (2 * CH), m - 1), piece = min(e % (2 * CH), 2 * cn - 1);
+        const uint32_t off = static_cast<uint32_t>(row * k + cb * 32 + piece * 16);
+        st.x[i] = *reinterpret_cast<const uint4*>(xq + off);
     }
 #pragma unroll
-    for (int i = 0; i < Stage<MR, CH, T>::DXV; ++i) {
-        const int e = tid + i * T;
-        if (Stage<MR, CH, T>::kDX % T != 0 && e >= Stage<MR, CH, T>::kDX) break;
-        const int b = e / MR, row = e % MR;
-        st.dx[i] = (row < m && b < cn) ? xd[static_cast<int64_t>(row) * nb + cb + b] : uint16_t(0);
+    for (int i = 0; i < S::DXV; ++i) {
+        const int e = min(tid + i * T, S::kDX - 1);
+        const int b = min(e / MR, cn - 1), row = min(e % MR, m - 1);
+        st.dx[i] = xd[static_cast<uint32_t>(row * nb + cb + b)];
     }
 #pragma unroll
-    for (int i = 0; i < Stage<MR, CH, T>::DWV; ++i) {
+    for (int i = 0; i < S::DWV; ++i) {
+        const int e = min(tid + i * T, S::kDW - 1);
+        const int b = min(e / kRows, cn - 1), row = min(e % kRows, rmax);
+        st.dw[i] = dbase[static_cast<uint32_t>(row * nb + cb + b)];
+    }
+}
+
+// Registers -> LDS for a chunk of cn blocks; pieces that do not exist are
+// written as zeros (the compute reads whole chunks: zero weights and scales
+// add exactly 0), pieces past the count are not written.
+template <int MR, int CH, int T>
+__device__ __forceinline__ void stage_store(const Stage<MR, CH, T>& st, int tid, int cn, int m, uint8_t* ws,
+                                            int wpitch, int8_t* xs, int xpitch, float* dxs, float* dws) {
+    using S = Stage<MR, CH, T>;
+#pragma unroll
+    for (int i = 0; i < S::WV; ++i) {
         const int e = tid + i * T;
-        if (Stage<MR, CH, T>::kDW % T != 0 && e >= Stage<MR, CH, T>::kDW) break;
-        const int b = e / kRows, row = e % kRows;
-        st.dw[i] = (b < cn) ? d[static_cast<int64_t>(min(n0 + row, n - 1)) * nb + cb + b] : uint16_t(0);
+        if (S::kW % T != 0 && e >= S::kW) break;
+        const bool ok = e % CH < cn;
+        *reinterpret_cast<uint4*>(&ws[(e / CH) * wpitch + (e % CH) * 16]) = ok ? st.w[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < S::XV; ++i) {
+        const int e = tid + i * T;
+        if (S::kX % T != 0 && e >= S::kX) break;
+        const bool ok = e / (2 * CH) < m && e % (2 * CH) < 2 * cn;
+        *reinterpret_cast<uint4*>(&xs[(e / (2 * CH)) * xpitch + (e % (2 * CH)) * 16]) =
+            ok ? st.x[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < S::DXV; ++i) {
+        const int e = tid + i * T;
+        if (S::kDX % T != 0 && e >= S::kDX) break;
+        const bool ok = e % MR < m && e / MR < cn;
+        dxs[e] = ok ? half_bits_to_float(st.dx[i]) : 0.f;            // [b][row], row-major
+    }
+#pragma unroll
+    for (int i = 0; i < S::DWV; ++i) {
+        const int e = tid + i * T;
+        if (S::kDW % T != 0 && e >= S::kDW) break;
+        const bool ok = e / kRows < cn;
+        dws[e] = ok ? half_bits_to_float(st.dw[i]) : 0.f;            // [b][row], row-major
     }
 }
 
@@ -180,6 +223,7 @@ void tile_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
     const int s = lane >> 4;
     const int c = lane & 15;
     const int n0 = blockIdx.x * kRows;
+    __builtin_assume(nb >= 1);                      // k >= 32: the chunk loop runs at least once
     const int64_t k = static_cast<int64_t>(nb) * 32;
     const int ashift = (s >> 1) * 4;
 
@@ -189,41 +233,39 @@ void tile_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[t][v] = 0.f;
 
-    St st;
-    stage_load<MR, kChunk, kThreads>(st, tid, 0, min(kChunk, nb), n0, n, nb, m, k, qs, d, xq, xd);
+    // kDepth chunks' loads are in flight at once: chunk c's registers are
+    // refilled with chunk c + kDepth as soon as they are in LDS
+    constexpr int kDepth = Tiling<MT>::kDepth;
+    St st[kDepth];
+    // the workgroup's rows: base addresses, and the last row inside the matrix
+    const uint8_t* wbase = qs + static_cast<int64_t>(n0) * (nb * 16);
+    const uint16_t* dbase = d + static_cast<int64_t>(n0) * nb;
+    const int rmax = n - 1 - n0;
+#pragma unroll
+    for (int dd = 0; dd < kDepth; ++dd) {
+        if (dd == 0 || dd * kChunk < nb)
+            stage_load<MR, kChunk, kThreads>(st[dd], tid, dd * kChunk, min(kChunk, nb - dd * kChunk), rmax, nb, m,
+                                             static_cast<int>(k), wbase, dbase, xq, xd);
+        // chunk by chunk, in the loop's order: the wait for chunk 0 must not
+        // include chunk 1's loads on the way into the loop either
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
-    for (int cb = 0; cb < nb; cb += kChunk) {
+    for (int cb0 = 0; cb0 < nb; cb0 += kDepth * kChunk) {
+#pragma unroll
+    for (int dd = 0; dd < kDepth; ++dd) {
+        const int cb = cb0 + dd * kChunk;
+        if (cb >= nb) break;
         const int cn = min(kChunk, nb - cb);
-        // registers -> LDS
-#pragma unroll
-        for (int i = 0; i < St::WV; ++i) {
-            const int e = tid + i * kThreads;
-            if (St::kW % kThreads != 0 && e >= St::kW) break;
-            *reinterpret_cast<uint4*>(&ws[e / kChunk][(e % kChunk) * 16]) = st.w[i];
-        }
-#pragma unroll
-        for (int i = 0; i < St::XV; ++i) {
-            const int e = tid + i * kThreads;
-            if (St::kX % kThreads != 0 && e >= St::kX) break;
-            *reinterpret_cast<uint4*>(&xs[e / (2 * kChunk)][(e % (2 * kChunk)) * 16]) = st.x[i];
-        }
-#pragma unroll
-        for (int i = 0; i < St::DXV; ++i) {
-            const int e = tid + i * kThreads;
-            if (St::kDX % kThreads != 0 && e >= St::kDX) break;
-            dxs[e / MR][e % MR] = half_bits_to_float(st.dx[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < St::DWV; ++i) {
-            const int e = tid + i * kThreads;
-            if (St::kDW % kThreads != 0 && e >= St::kDW) break;
-            dws[e / kRows][e % kRows] = half_bits_to_float(st.dw[i]);
-        }
+        stage_store<MR, kChunk, kThreads>(st[dd], tid, cn, m, &ws[0][0], kWPitch, &xs[0][0], kXPitch, &dxs[0][0],
+                                          &dws[0][0]);
         __syncthreads();
-        // the next chunk's global loads fly while this chunk computes
-        if (cb + kChunk < nb)
-            stage_load<MR, kChunk, kThreads>(st, tid, cb + kChunk, min(kChunk, nb - cb - kChunk), n0, n, nb, m, k, qs, d,
-                                   xq, xd);
+        {
+            const int nx = cb + kDepth * kChunk;
+            if (nx < nb)
+                stage_load<MR, kChunk, kThreads>(st[dd], tid, nx, min(kChunk, nb - nx), rmax, nb, m,
+                                                 static_cast<int>(k), wbase, dbase, xq, xd);
+        }
 
         // this wave's blocks of the chunk, kBatch at a time: the batch's
         // scales are read from LDS first, then its MFMAs are issued, then
@@ -346,6 +388,7 @@ void tile_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
             }
         }
         __syncthreads();   // LDS is rewritten by the next chunk
+    }
     }
 
     // add the waves' partials in wave order (and, for paired blocks, the
