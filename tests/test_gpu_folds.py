@@ -34,7 +34,7 @@ def _case(qtype, n, k, seed):
 
 
 FOLD_SHAPES = [(Q8, 64, 256), (Q4, 2048, 2048), (Q4, 2048, 8192), (Q8, 300, 1056), (Q4, 64, 32768),
-               (Q8, 515, 4096), (Q4, 1, 32)]
+               (Q8, 515, 4096), (Q4, 1, 32), (Q4, 1001, 8192), (Q8, 77, 16384)]
 
 
 @pytest.mark.parametrize("qtype,n,k", FOLD_SHAPES)

@@ -67,6 +67,8 @@ SHAPES = [
     (Q8, 515, 2048), (Q4, 515, 4096),        # K split over 2 waves
     (Q8, 257, 8192), (Q4, 2048, 8192),       # the FFN down-projection width
     (Q8, 64, 32768), (Q4, 64, 32768),        # the maximum K (16-wave split)
+    (Q4, 5, 8192), (Q4, 1001, 8192),         # 4-wave split, two row groups per workgroup, ragged
+    (Q4, 77, 16384), (Q8, 45, 16384),        # 8-wave split (16-wave workgroups), ragged
 ]
 
 
@@ -193,7 +195,8 @@ def test_quantize_ragged_shapes(m, k):
 
 
 INT_SHAPES = [(Q4, 2048, 2048), (Q8, 64, 256), (Q4, 1, 32), (Q8, 1, 32), (Q4, 999, 96),
-              (Q8, 777, 1056), (Q4, 300, 8192), (Q8, 300, 8192), (Q4, 33, 32768)]
+              (Q8, 777, 1056), (Q4, 300, 8192), (Q8, 300, 8192), (Q4, 33, 32768), (Q4, 77, 16384),
+              (Q8, 5, 16384)]
 
 
 def _qmv8x(qtype):
@@ -276,7 +279,7 @@ def _ffn_case(n_ff, k, seed):
     return wl, down(h), down(y)
 
 
-@pytest.mark.parametrize("n_ff,k", [(8192, 2048), (1056, 96), (64, 32)])
+@pytest.mark.parametrize("n_ff,k", [(8192, 2048), (1056, 96), (64, 32), (224, 8192), (96, 16384)])
 def test_ffn_stage_by_stage(n_ff, k):
     wl, h, y = _ffn_case(n_ff, k, seed=0)
     ref = oracle.ffn_gate_up(Q4, wl["wg"], wl["wu"], n_ff, k, wl["x"])
@@ -290,6 +293,21 @@ def test_ffn_stage_by_stage(n_ff, k):
     Wd = np.abs(oracle.dequantize(Q4, wl["wd"], k, n_ff))
     ye, ae = oracle.matvec(Q4, wl["wd"], k, n_ff, ref["h"])
     check_within(y, ye, Wd @ hb + oracle.fp32_path_bound(ae), "end to end")
+
+
+@pytest.mark.parametrize("n_ff,k", [(1001, 2048), (77, 8192), (45, 16384), (3, 32768)])
+def test_ffn_gate_up_ragged_rows(n_ff, k):
+    """Gate+up alone at row counts that leave row groups (and, for split
+    rows, the second row group of a workgroup) partly or wholly past the end."""
+    rng = np.random.default_rng(n_ff + k)
+    wg = synth.q4_0_weights(rng, n_ff, k)
+    wu = synth.q4_0_weights(rng, n_ff, k)
+    x = synth.activations(rng, k)
+    g = packed(gq, Q4, wg, n_ff, k)
+    u = packed(gq, Q4, wu, n_ff, k)
+    h = down(gq.qffn_gate_up_gelu(g[0], g[1], u[0], u[1], n_ff, k, up(x)))
+    ref = oracle.ffn_gate_up(Q4, wg, wu, n_ff, k, x)
+    check_within(h, ref["h"], oracle.ffn_h_bound(ref["g"], ref["u"], ref["ag"], ref["au"], ref["h"]), "h")
 
 
 def test_ffn_gelu_on_exact_inputs():
