@@ -21,6 +21,7 @@
 // SafeC Gemma 4 DESIGN_NOTES page ("A dedicated GEMV kernel for the M==1
 // decode step") and the Gemma-4-E2B raw-Metal port page ("Why this exists").
 #include <atomic>
+#include <type_traits>
 
 #include "gq_device.hpp"
 #include "gq_launch.hpp"
@@ -33,9 +34,6 @@
 #endif
 #ifndef GQ_QMV_R_FFN
 #define GQ_QMV_R_FFN 2           // rows per wave step of the gate+up pass (each a gate and an up row)
-#endif
-#ifndef GQ_QMV_CARRY
-#define GQ_QMV_CARRY 1         // issue the next row group's loads before this one's reduction
 #endif
 #ifndef GQ_QMV_SPLIT_SUBS
 #define GQ_QMV_SPLIT_SUBS 2      // row groups per workgroup when rows are split over 4 waves (at most 16 waves)
@@ -196,7 +194,17 @@ void qmv_kernel(const QmvParams p) {
     constexpr int SUBS = WAVES / WS;                // independent row groups per workgroup
     constexpr int NMAT = (MODE == kFFN) ? 2 : 1;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    // Instantiations for very tall matrices (n >= 65536 takes R_TALL rows per
+    // step at WS = 1): each wave walks many row groups. These keep the wave
+    // index in a scalar register (the row arithmetic and each row's base
+    // address are then scalar), one scale per 32-bit register, and the
+    // pinned loop below; so does the gate+up pass. Measured on MI355X: the
+    // vocabulary head and the FFN gain from them, the one-group matvecs
+    // (2048 x 2048, the down projection) do not.
+    constexpr bool kManyGroups = (WS == 1 && R == GQ_QMV_R_TALL);
+    constexpr bool kPinned = kManyGroups || MODE == kFFN;
+    const int wave = kManyGroups ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave)
+                                 : static_cast<int>(threadIdx.x) / kWave;
     const int slice = wave % WS;
     const int sub = wave / WS;
     const int row_bytes = p.units * 16;
@@ -234,8 +242,12 @@ void qmv_kernel(const QmvParams p) {
     // contribute nothing: their activations are zero and their scale is
     // masked to zero below, so no load sits behind a divergent branch.
     uint4 q[NI][NMAT][R];
-    uint16_t db[NI][NMAT][R];
-    auto load_group = [&](int r0) {
+    // (two 16-bit scales packed into one register would make the compiler
+    // wait for their loads right where the next group's are issued; the
+    // other instantiations keep 16-bit scales, measured faster for them)
+    using ScaleT = std::conditional_t<kManyGroups, uint32_t, uint16_t>;
+    ScaleT db[NI][NMAT][R];
+    auto load_group = [&](uint4 (&qd)[NI][NMAT][R], ScaleT (&dd)[NI][NMAT][R], int r0) {
 #pragma unroll
         for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -251,11 +263,11 @@ void qmv_kernel(const QmvParams p) {
 #if GQ_QMV_NT
                     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
                     const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
-                    q[i][m][r] = make_uint4(t.x, t.y, t.z, t.w);
+                    qd[i][m][r] = make_uint4(t.x, t.y, t.z, t.w);
 #else
-                    q[i][m][r] = *reinterpret_cast<const uint4*>(src);
+                    qd[i][m][r] = *reinterpret_cast<const uint4*>(src);
 #endif
-                    db[i][m][r] = dm[static_cast<uint64_t>(row) * static_cast<uint32_t>(p.nb) + (uload[i] >> SH)];
+                    dd[i][m][r] = dm[static_cast<uint64_t>(row) * static_cast<uint32_t>(p.nb) + (uload[i] >> SH)];
                 }
             }
     };
@@ -330,9 +342,7 @@ void qmv_kernel(const QmvParams p) {
     // loads (the point of the order above)
     __builtin_amdgcn_sched_barrier(0);
     int it = blockIdx.x;
-#if GQ_QMV_CARRY
-    load_group((it * SUBS + sub) * R);
-#endif
+    load_group(q, db, (it * SUBS + sub) * R);
 
     // ---- activation registers for this lane's units ----------------------
     // Optional RMSNorm prologue (SafeC Gemma 4 DESIGN_NOTES page, "RMSNorm"):
@@ -501,31 +511,29 @@ void qmv_kernel(const QmvParams p) {
         }
     };
 
-    __shared__ float lpart[WAVES][NMAT][R];
-    for (; it * SUBS < p.row_groups; it += gridDim.x) {
-        const int g = it * SUBS + sub;
-        const int r0 = g * R;
-        const int itn = it + gridDim.x;
-#if !GQ_QMV_CARRY
-        load_group(r0);
-#endif
-        float acc[NMAT][R];
+    // ---- one row group: the dot over this lane's units ------------------
+    auto dot_group = [&](const uint4 (&qd)[NI][NMAT][R], const ScaleT (&dd)[NI][NMAT][R], int r0,
+                         float (&acc)[NMAT][R]) {
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
             for (int r = 0; r < R; ++r) acc[m][r] = 0.f;
-
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const float dw = uvalid[i] ? half_bits_to_float(db[i][m][r]) : 0.f;
+                    // the scale bits pass through an opaque statement here, at
+                    // their use: otherwise the compiler unpacks or masks them
+                    // right after the staging, waiting there for every load
+                    uint32_t dbits = dd[i][m][r];
+                    asm volatile("" : "+v"(dbits));
+                    const float dw = uvalid[i] ? half_bits_to_float(static_cast<uint16_t>(dbits)) : 0.f;
                     if constexpr (MODE != kQ8X) {
-                        acc[m][r] = fmaf(dw, unit_dot_f32<TYPE>(q[i][m][r], xr[i]), acc[m][r]);
+                        acc[m][r] = fmaf(dw, unit_dot_f32<TYPE>(qd[i][m][r], xr[i]), acc[m][r]);
                     } else {
-                        int s = unit_dot_q8<TYPE>(q[i][m][r], xqr[i], sxr[i]);
+                        int s = unit_dot_q8<TYPE>(qd[i][m][r], xqr[i], sxr[i]);
                         if constexpr (TYPE == kTypeQ8_0) {
                             // a block is two adjacent lanes' units: S_b = s(2t) + s(2t+1)
                             s += dpp_i32<kDppQuadSwap1>(s);
@@ -539,12 +547,11 @@ void qmv_kernel(const QmvParams p) {
                     }
                 }
         }
-#if GQ_QMV_CARRY
-        // the next row group's loads fly during the reduction and stores
-        if (itn * SUBS < p.row_groups) load_group((itn * SUBS + sub) * R);
-#endif
+    };
 
-        // ---- cross-lane and cross-wave reduction ---------------------------
+    // ---- cross-lane and cross-wave reduction, epilogue and store --------
+    __shared__ float lpart[WAVES][NMAT][R];
+    auto finish_group = [&](float (&acc)[NMAT][R], int r0) {
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -589,6 +596,45 @@ void qmv_kernel(const QmvParams p) {
                 }
             }
             __syncthreads();
+        }
+    };
+
+    // ---- the workgroup's row groups, gridDim.x apart ----------------------
+    // The grid never exceeds the groups, so the first one exists; the loop
+    // condition is uniform over the workgroup, so every wave reaches the
+    // barriers in finish_group. One register set: the next group's loads are
+    // issued after this group's dot (its quants are dead by then) and fly
+    // during the reduction and the stores.
+    if constexpr (kPinned) {
+        for (;;) {
+            const int r0 = (it * SUBS + sub) * R;
+            const int itn = it + gridDim.x;
+            const bool more = itn * SUBS < p.row_groups;
+            float acc[NMAT][R];
+            dot_group(q, db, r0, acc);
+            // pin the order: the dot is finished (its results pass through
+            // an opaque statement) before a memory barrier the next loads
+            // cannot be hoisted over -- otherwise they go out first into a
+            // second register set, and the loop copies one set into the other
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int r = 0; r < R; ++r) asm volatile("" : "+v"(acc[m][r]));
+            asm volatile("" ::: "memory");
+            if (more) load_group(q, db, (itn * SUBS + sub) * R);
+            finish_group(acc, r0);
+            if (!more) break;
+            it = itn;
+        }
+    } else {
+        // (the compiler is free to hoist the next group's loads here)
+        for (; it * SUBS < p.row_groups; it += gridDim.x) {
+            const int r0 = (it * SUBS + sub) * R;
+            const int itn = it + gridDim.x;
+            float acc[NMAT][R];
+            dot_group(q, db, r0, acc);
+            if (itn * SUBS < p.row_groups) load_group(q, db, (itn * SUBS + sub) * R);
+            finish_group(acc, r0);
         }
     }
 
