@@ -36,7 +36,10 @@
 #define GQ_QMV_R_FFN 2           // rows per wave step of the gate+up pass (each a gate and an up row)
 #endif
 #ifndef GQ_QMV_SPLIT_SUBS
-#define GQ_QMV_SPLIT_SUBS 2      // row groups per workgroup when rows are split over 4 waves (at most 16 waves)
+#define GQ_QMV_SPLIT_SUBS 1      // row groups per workgroup when rows are split over 4 waves (at most 16 waves)
+#endif
+#ifndef GQ_QMV_STAGE_WS
+#define GQ_QMV_STAGE_WS 4        // largest K split whose workgroups stage x in LDS (all of x: k <= 8192)
 #endif
 #ifndef GQ_QMV_WAVES1
 #define GQ_QMV_WAVES1 4        // waves per workgroup for un-split rows (they share one LDS copy of x)
@@ -174,8 +177,8 @@ __device__ __forceinline__ int unit_dot_q8(const uint4 q, const uint32_t* xr, in
 
 // Waves per workgroup for a K split over WS waves: at least 4; split rows
 // put GQ_QMV_SPLIT_SUBS row groups in one workgroup while that stays within
-// 16 waves (two 4-wave groups of 4 rows each keep more rows in flight per
-// workgroup than one group of 8 rows, at half the registers per lane).
+// 16 waves (measured: with x staged in LDS, one 4-row group per 4-wave
+// workgroup is the fastest for the 2048 x 8192 down projection).
 template <int WS> struct Waves {
     static constexpr int value = WS < 4 ? 4 : (WS * GQ_QMV_SPLIT_SUBS > 16 ? WS : WS * GQ_QMV_SPLIT_SUBS);
 };
@@ -208,13 +211,15 @@ void qmv_kernel(const QmvParams p) {
     const int slice = wave % WS;
     const int sub = wave / WS;
     const int row_bytes = p.units * 16;
-    // fp32 activations of un-split rows are staged through LDS (below)
-    constexpr bool kStage = (MODE != kQ8X) && (WS == 1);
+    // fp32 activations are staged through LDS (below) for un-split rows and
+    // for rows split over up to GQ_QMV_STAGE_WS waves (all of x, which the
+    // workgroup's row groups share)
+    constexpr bool kStage = (MODE != kQ8X) && (WS <= GQ_QMV_STAGE_WS);
     constexpr int kPitch = EPU + 4;
     constexpr int kThreads = WAVES * kWave;
     // float4s of x per thread when staging; the LDS copy is padded to whole
     // rounds of the workgroup so every thread writes its slots unconditionally
-    constexpr int kStageF4 = kStage ? (NI * kWave * EPU / 4 + kThreads - 1) / kThreads : 0;
+    constexpr int kStageF4 = kStage ? (WS * NI * kWave * EPU / 4 + kThreads - 1) / kThreads : 0;
     constexpr int kStageUnits = kStage ? (kStageF4 * kThreads * 4 + EPU - 1) / EPU : 1;
     __shared__ float xstage[kStage ? kStageUnits * kPitch : 1];
     // integer path with the quantiser folded in: the workgroup's Q8_0 codes
@@ -742,7 +747,7 @@ hipError_t launch_rows(QmvParams p, hipStream_t stream, int* grid_out) {
 }
 
 // Rows per wave step (measured on MI355X): rows split over 4 or 8 waves
-// stream 4 rows at a time, with two row groups per workgroup; very tall
+// stream 4 rows at a time; very tall
 // matrices take 4 (each wave loops over many groups); shorter ones take 2
 // so more waves share the dequantisation work.
 template <int TYPE, int MODE, int NI, int WS>
