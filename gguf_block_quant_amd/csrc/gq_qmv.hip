@@ -30,7 +30,7 @@
 #define GQ_QMV_MAX_GRID 1024   // workgroups of 4 waves (4 per CU on 256 CUs)
 #endif
 #ifndef GQ_QMV_R_SHORT
-#define GQ_QMV_R_SHORT 2         // rows per wave step for shorter (n < 65536) un-split matrices
+#define GQ_QMV_R_SHORT 1         // rows per wave step for shorter (n < 65536) un-split matrices
 #endif
 #ifndef GQ_QMV_R_FFN
 #define GQ_QMV_R_FFN 2           // rows per wave step of the gate+up pass (each a gate and an up row)
@@ -43,6 +43,15 @@
 #endif
 #ifndef GQ_QMV_WAVES1
 #define GQ_QMV_WAVES1 4        // waves per workgroup for un-split rows (they share one LDS copy of x)
+#endif
+#ifndef GQ_QMV_WAVES1_SHORT
+#define GQ_QMV_WAVES1_SHORT 8  // ... for shorter matvecs at R_SHORT rows per step (measured)
+#endif
+#ifndef GQ_QMV_WAVES1_Q8X
+#define GQ_QMV_WAVES1_Q8X 8    // ... for the integer path quantising x in its prologue (measured)
+#endif
+#ifndef GQ_QMV_R_Q8X
+#define GQ_QMV_R_Q8X 1         // rows per wave step of the integer path quantising x in its prologue (measured)
 #endif
 #ifndef GQ_QMV_R_TALL
 #define GQ_QMV_R_TALL 4        // rows per wave step for tall (n >= 65536) un-split matrices
@@ -179,21 +188,29 @@ __device__ __forceinline__ int unit_dot_q8(const uint4 q, const uint32_t* xr, in
 // put GQ_QMV_SPLIT_SUBS row groups in one workgroup while that stays within
 // 16 waves (measured: with x staged in LDS, one 4-row group per 4-wave
 // workgroup is the fastest for the 2048 x 8192 down projection).
-template <int WS> struct Waves {
-    static constexpr int value = WS < 4 ? 4 : (WS * GQ_QMV_SPLIT_SUBS > 16 ? WS : WS * GQ_QMV_SPLIT_SUBS);
+// Un-split rows take GQ_QMV_WAVES1 waves (the vocabulary head, the gate+up
+// pass), except shorter matvecs at R_SHORT rows per step and the integer
+// path with the quantiser folded in, whose workgroups each quantise all of x
+// first: there more waves share the staging or quantiser prologue
+// (GQ_QMV_WAVES1_SHORT, GQ_QMV_WAVES1_Q8X; measured).
+template <int WS, int MODE, bool FOLD, int R> struct Waves {
+    static constexpr int value =
+        WS == 1 ? ((MODE == kQ8X && FOLD)                    ? GQ_QMV_WAVES1_Q8X
+                   : (MODE != kFFN && R == GQ_QMV_R_SHORT) ? GQ_QMV_WAVES1_SHORT
+                                                           : GQ_QMV_WAVES1)
+                : (WS < 4 ? 4 : (WS * GQ_QMV_SPLIT_SUBS > 16 ? WS : WS * GQ_QMV_SPLIT_SUBS));
 };
-template <> struct Waves<1> { static constexpr int value = GQ_QMV_WAVES1; };
 
 // FOLD selects the variant with the optional RMSNorm prologue and the
 // residual / soft-cap / argmax epilogue (runtime flags in QmvParams); the
 // plain variant carries none of that code, so its register budget is
 // untouched.
 template <int TYPE, int MODE, int NI, int WS, int R, bool FOLD>
-__global__ __launch_bounds__(Waves<WS>::value * kWave)
+__global__ __launch_bounds__((Waves<WS, MODE, FOLD, R>::value * kWave))
 void qmv_kernel(const QmvParams p) {
     constexpr int EPU = Fmt<TYPE>::kElemsPerUnit;
     constexpr int SH = Fmt<TYPE>::kUnitToBlockShift;
-    constexpr int WAVES = Waves<WS>::value;
+    constexpr int WAVES = Waves<WS, MODE, FOLD, R>::value;
     constexpr int SUBS = WAVES / WS;                // independent row groups per workgroup
     constexpr int NMAT = (MODE == kFFN) ? 2 : 1;
     const int lane = threadIdx.x & (kWave - 1);
@@ -723,7 +740,7 @@ int resident_workgroups(K kernel, int threads) {
 
 template <int TYPE, int MODE, int NI, int WS, int R, bool FOLD>
 hipError_t launch_variant(QmvParams p, hipStream_t stream, int* grid_out) {
-    constexpr int WAVES = Waves<WS>::value;
+    constexpr int WAVES = Waves<WS, MODE, FOLD, R>::value;
     constexpr int SUBS = WAVES / WS;
     p.row_groups = (p.n + R - 1) / R;
     const int64_t iters = (static_cast<int64_t>(p.row_groups) + SUBS - 1) / SUBS;
@@ -747,12 +764,13 @@ hipError_t launch_rows(QmvParams p, hipStream_t stream, int* grid_out) {
 }
 
 // Rows per wave step (measured on MI355X): rows split over 4 or 8 waves
-// stream 4 rows at a time; very tall
-// matrices take 4 (each wave loops over many groups); shorter ones take 2
-// so more waves share the dequantisation work.
+// stream 4 rows at a time; very tall matrices take 4 (each wave loops over
+// many groups); the gate+up pass takes 2 row pairs; shorter matvecs, and the
+// integer path quantising x in its prologue, take 1 row at 8 waves per
+// workgroup, so more waves share the dequantisation work.
 template <int TYPE, int MODE, int NI, int WS>
 hipError_t launch_cfg(QmvParams p, hipStream_t stream, int* grid_out) {
-    if constexpr (Waves<WS>::value >= 16) {
+    if constexpr (Waves<WS, MODE, false, GQ_QMV_R_SPLIT>::value >= 16) {
         // 1024-thread workgroups cap a lane at 128 VGPRs: 4 rows (2 row pairs
         // for the gate+up FFN) fit unspilled
         return launch_rows<TYPE, MODE, NI, WS, (MODE == kFFN ? 2 : 4)>(p, stream, grid_out);
@@ -760,6 +778,9 @@ hipError_t launch_cfg(QmvParams p, hipStream_t stream, int* grid_out) {
         return launch_rows<TYPE, MODE, NI, WS, GQ_QMV_R_SPLIT>(p, stream, grid_out);
     } else {
         if (p.n >= 65536) return launch_rows<TYPE, MODE, NI, WS, GQ_QMV_R_TALL>(p, stream, grid_out);
+        if constexpr (MODE == kQ8X) {
+            if (p.x != nullptr) return launch_rows<TYPE, MODE, NI, WS, GQ_QMV_R_Q8X>(p, stream, grid_out);
+        }
         return launch_rows<TYPE, MODE, NI, WS, (MODE == kFFN ? GQ_QMV_R_FFN : GQ_QMV_R_SHORT)>(p, stream, grid_out);
     }
 }
