@@ -55,16 +55,30 @@ namespace {
 #ifndef GQ_TILE_DEPTH2
 #define GQ_TILE_DEPTH2 1         // ... (two activation tiles; measured)
 #endif
+#ifndef GQ_TILE_WPAD1
+#define GQ_TILE_WPAD1 16         // LDS row padding (bytes) of the staged weights, one activation tile
+#endif
+#ifndef GQ_TILE_XPAD1
+#define GQ_TILE_XPAD1 32         // ... of the staged activation codes
+#endif
+#ifndef GQ_TILE_WPAD2
+#define GQ_TILE_WPAD2 16         // ... weights, two activation tiles
+#endif
+#ifndef GQ_TILE_XPAD2
+#define GQ_TILE_XPAD2 16         // ... activation codes, two activation tiles (32 measured 3 % slower)
+#endif
 constexpr int kRows = 16;                          // weight rows per workgroup
-// Blocks per k chunk, and the LDS pitches that follow from it: a weight row
-// takes CH * 16 + 16 bytes (mod 256 = 16), an activation row CH * 32 + 32
-// (mod 256 = 32), so the fragment reads of the 16 rows spread over the banks.
+// Blocks per k chunk, and the LDS pitches that follow from it: a staged row
+// is padded by an odd number of 16-byte units or by 32 bytes (an activation
+// row CH * 32 + 32 for one tile, CH * 32 + 16 for two; a weight row
+// CH * 16 + 16), so the fragment reads of the 16 rows spread over the banks
+// (a pad of 64 bytes made the two-tile kernel 25 % slower).
 template <int MT> struct Tiling {
     static constexpr int kChunk = MT == 1 ? GQ_TILE_CHUNK1 : GQ_TILE_CHUNK2;
     static constexpr int kThreads = MT == 1 ? GQ_TILE_THREADS1 : GQ_TILE_THREADS2;
     static constexpr int kWaves = kThreads / kWave;
-    static constexpr int kWPitch = kChunk * 16 + 16;
-    static constexpr int kXPitch = kChunk * 32 + 32;
+    static constexpr int kWPitch = kChunk * 16 + (MT == 1 ? GQ_TILE_WPAD1 : GQ_TILE_WPAD2);
+    static constexpr int kXPitch = kChunk * 32 + (MT == 1 ? GQ_TILE_XPAD1 : GQ_TILE_XPAD2);
     static constexpr int kWavePart = kChunk / kWaves;            // blocks per wave per chunk
     static constexpr int kDepth = MT == 1 ? GQ_TILE_DEPTH1 : GQ_TILE_DEPTH2;
 };
