@@ -36,7 +36,7 @@ hipError_t launch_pack(int type, const uint8_t* blocks, int64_t n, int64_t k, ui
 hipError_t launch_quantize_q8_0(const float* x, int64_t m, int64_t k, int8_t* xq, uint16_t* xd,
                                 hipStream_t stream);
 
-constexpr size_t kArgmaxWorkspaceBytes = 8192;   // >= 8 bytes x the largest matvec grid
+constexpr size_t kArgmaxWorkspaceBytes = 16384;  // >= 8 bytes x the largest matvec grid
 
 hipError_t launch_qmv_f32(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k,
                           const float* x, const float* norm_w, float norm_eps, const float* residual,

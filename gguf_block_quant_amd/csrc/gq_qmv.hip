@@ -27,7 +27,7 @@
 #include "gq_launch.hpp"
 
 #ifndef GQ_QMV_MAX_GRID
-#define GQ_QMV_MAX_GRID 1024   // workgroups of 4 waves (4 per CU on 256 CUs)
+#define GQ_QMV_MAX_GRID 1280   // workgroups of 4 waves (5 per CU on 256 CUs; the vocabulary head, measured)
 #endif
 #ifndef GQ_QMV_R_SHORT
 #define GQ_QMV_R_SHORT 1         // rows per wave step for shorter (n < 65536) un-split matrices
@@ -708,6 +708,9 @@ void argmax_reduce_kernel(const unsigned long long* __restrict__ part, int npart
 namespace {
 
 constexpr int kMaxGrid = GQ_QMV_MAX_GRID;
+// the argmax first stage writes one 8-byte key per workgroup; no matvec grid
+// exceeds kMaxGrid (workgroups have at least 4 waves)
+static_assert(sizeof(unsigned long long) * kMaxGrid <= kArgmaxWorkspaceBytes, "argmax workspace too small");
 
 // Workgroups of a kernel that can be resident at once on the device: the
 // persistent grid is never larger, so no workgroup waits for a second round.
