@@ -140,3 +140,22 @@ def test_argmax_nan_and_norm():
     yr, ar = oracle.matvec(Q8, w, n, k, oracle.rmsnorm(x, g, EPS))
     check_within(lg, 30.0 * np.tanh(yr / 30.0), oracle.fp32_path_bound(ar) + 1e-5, "norm + cap")
     assert int(down(idx)[0]) == oracle.argmax_f32(lg)
+
+
+@pytest.mark.parametrize("qtype,n,k", [(Q8, 262144, 256), (Q4, 300000, 64)])
+def test_argmax_stays_inside_its_workspace(qtype, n, k):
+    """The first stage writes one key per workgroup into the caller's
+    workspace: at the largest grid (a tall matrix) every write stays inside
+    gq_argmax_workspace_bytes(); the bytes after it are untouched."""
+    rng = np.random.default_rng(n + k)
+    w = synth.weights(rng, qtype, n, k)
+    x = synth.activations(rng, k)
+    qs, d = packed(gq, qtype, w, n, k)
+    wsb = gq.argmax_workspace_bytes()
+    buf = torch.full((wsb + 4096,), 0xAB, dtype=torch.uint8, device="cuda")
+    ws = buf[:wsb]
+    idx, val, logits = _argmax(qtype)(qs, d, n, k, up(x), softcap=0.0, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.all(buf[wsb:] == 0xAB).item()
+    lg = down(logits)
+    assert int(down(idx)[0]) == oracle.argmax_f32(lg)
