@@ -218,11 +218,11 @@ void qmv_kernel(const QmvParams p) {
     // step at WS = 1): each wave walks many row groups. These keep the wave
     // index in a scalar register (the row arithmetic and each row's base
     // address are then scalar), one scale per 32-bit register, and the
-    // pinned loop below; so does the gate+up pass. Measured on MI355X: the
-    // vocabulary head and the FFN gain from them, the one-group matvecs
-    // (2048 x 2048, the down projection) do not.
+    // pinned loop below; so do the gate+up pass and split rows. Measured on
+    // MI355X: the vocabulary head, the FFN and the down projection gain from
+    // the pinned loop, the un-split one-group matvecs (2048 x 2048) do not.
     constexpr bool kManyGroups = (WS == 1 && R == GQ_QMV_R_TALL);
-    constexpr bool kPinned = kManyGroups || MODE == kFFN;
+    constexpr bool kPinned = kManyGroups || MODE == kFFN || WS > 1;
     const int wave = kManyGroups ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave)
                                  : static_cast<int>(threadIdx.x) / kWave;
     const int slice = wave % WS;
@@ -238,6 +238,7 @@ void qmv_kernel(const QmvParams p) {
     // rounds of the workgroup so every thread writes its slots unconditionally
     constexpr int kStageF4 = kStage ? (WS * NI * kWave * EPU / 4 + kThreads - 1) / kThreads : 0;
     constexpr int kStageUnits = kStage ? (kStageF4 * kThreads * 4 + EPU - 1) / EPU : 1;
+    static_assert(!kStage || kStageUnits >= WS * NI * kWave, "every lane's unit has a staged slot");
     __shared__ float xstage[kStage ? kStageUnits * kPitch : 1];
     // integer path with the quantiser folded in: the workgroup's Q8_0 codes
     // (4 per word) and binary16 scales of all of x
@@ -417,12 +418,14 @@ void qmv_kernel(const QmvParams p) {
         }
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const float* xs = &xstage[uload[i] * kPitch];
+            // the lane's own (unclamped) unit: the slots of units past the row
+            // hold zeros, so a lane past a short row needs no select here
+            const float* xs = &xstage[unit[i] * kPitch];
 #pragma unroll
             for (int v = 0; v < EPU / 4; ++v) {
                 const float4 t = *reinterpret_cast<const float4*>(xs + 4 * v);
-                xr[i][4 * v + 0] = uvalid[i] ? t.x : 0.f; xr[i][4 * v + 1] = uvalid[i] ? t.y : 0.f;
-                xr[i][4 * v + 2] = uvalid[i] ? t.z : 0.f; xr[i][4 * v + 3] = uvalid[i] ? t.w : 0.f;
+                xr[i][4 * v + 0] = t.x; xr[i][4 * v + 1] = t.y;
+                xr[i][4 * v + 2] = t.z; xr[i][4 * v + 3] = t.w;
             }
             dxr[i] = 0.f; sxr[i] = 0;
         }
