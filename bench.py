@@ -550,8 +550,27 @@ def cpu_baseline(host, weight_bytes_per_step, seconds, log):
         "sample": "%d full pass(es) of the step's workload (every kernel once, same inputs) through the "
                   "single-threaded fp64 C oracle, %.1f s; weight-block bytes / time" % (passes, el),
         "seconds_per_step": round(el / passes, 3),
-        "cpu": platform.processor() or platform.machine(),
+        "cpu": cpu_description(),
     }
+
+
+def cpu_description():
+    """Model name, sockets and logical CPUs of the host (from /proc/cpuinfo
+    where it exists)."""
+    model, sockets = None, set()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                key, _, val = line.partition(":")
+                key = key.strip()
+                if key == "model name" and model is None:
+                    model = val.strip()
+                elif key == "physical id":
+                    sockets.add(val.strip())
+    except OSError:
+        pass
+    model = model or platform.processor() or platform.machine()
+    return "%s; %d socket(s), %d logical CPUs" % (model, max(1, len(sockets)), os.cpu_count() or 1)
 
 
 def cpu_baseline_threads(host, weight_bytes_per_step, seconds, log):
@@ -606,6 +625,7 @@ def cpu_baseline_threads(host, weight_bytes_per_step, seconds, log):
         "sample": "%d full pass(es) of the step's workload through the fp64 C oracle, every matrix split "
                   "by rows over %d threads, %.1f s" % (passes, T, el),
         "seconds_per_step": round(el / passes, 3),
+        "cpu": cpu_description(),
     }
 
 
