@@ -172,41 +172,55 @@ __device__ __forceinline__ void stage_load(Stage<MR, CH, T>& st, int tid, int cb
     }
 }
 
-// Registers -> LDS for a chunk of cn blocks; pieces that do not exist are
-// written as zeros (the compute reads whole chunks: zero weights and scales
-// add exactly 0), pieces past the count are not written.
+// Registers -> LDS for a chunk of cn blocks. Every loaded piece is written
+// as it is (the clamped loads hold valid neighbours); then the scales of
+// blocks past cn are overwritten with zeros, so those blocks add exactly 0.
+// Pieces past the matrix rows or the m activation rows only produce results
+// that are never stored, so they need no clearing. (A select between a
+// loaded value and zero compiled to a branch that waited for that load
+// inside it, one piece at a time.) Pieces past the count are not written.
 template <int MR, int CH, int T>
 __device__ __forceinline__ void stage_store(const Stage<MR, CH, T>& st, int tid, int cn, int m, uint8_t* ws,
                                             int wpitch, int8_t* xs, int xpitch, float* dxs, float* dws) {
     using S = Stage<MR, CH, T>;
+    (void)m;
 #pragma unroll
     for (int i = 0; i < S::WV; ++i) {
         const int e = tid + i * T;
         if (S::kW % T != 0 && e >= S::kW) break;
-        const bool ok = e % CH < cn;
-        *reinterpret_cast<uint4*>(&ws[(e / CH) * wpitch + (e % CH) * 16]) = ok ? st.w[i] : make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(&ws[(e / CH) * wpitch + (e % CH) * 16]) = st.w[i];
     }
 #pragma unroll
     for (int i = 0; i < S::XV; ++i) {
         const int e = tid + i * T;
         if (S::kX % T != 0 && e >= S::kX) break;
-        const bool ok = e / (2 * CH) < m && e % (2 * CH) < 2 * cn;
-        *reinterpret_cast<uint4*>(&xs[(e / (2 * CH)) * xpitch + (e % (2 * CH)) * 16]) =
-            ok ? st.x[i] : make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(&xs[(e / (2 * CH)) * xpitch + (e % (2 * CH)) * 16]) = st.x[i];
     }
 #pragma unroll
     for (int i = 0; i < S::DXV; ++i) {
         const int e = tid + i * T;
         if (S::kDX % T != 0 && e >= S::kDX) break;
-        const bool ok = e % MR < m && e / MR < cn;
-        dxs[e] = ok ? half_bits_to_float(st.dx[i]) : 0.f;            // [b][row], row-major
+        dxs[e] = half_bits_to_float(st.dx[i]);                     // [b][row], row-major
     }
 #pragma unroll
     for (int i = 0; i < S::DWV; ++i) {
         const int e = tid + i * T;
         if (S::kDW % T != 0 && e >= S::kDW) break;
-        const bool ok = e / kRows < cn;
-        dws[e] = ok ? half_bits_to_float(st.dw[i]) : 0.f;            // [b][row], row-major
+        dws[e] = half_bits_to_float(st.dw[i]);                     // [b][row], row-major
+    }
+    if (cn < CH) {                                                  // the last, ragged chunk only
+#pragma unroll
+        for (int i = 0; i < S::DXV; ++i) {
+            const int e = tid + i * T;
+            if (S::kDX % T != 0 && e >= S::kDX) break;
+            if (e / MR >= cn) dxs[e] = 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < S::DWV; ++i) {
+            const int e = tid + i * T;
+            if (S::kDW % T != 0 && e >= S::kDW) break;
+            if (e / kRows >= cn) dws[e] = 0.f;
+        }
     }
 }
 
@@ -295,8 +309,8 @@ void tile_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
         // this wave's blocks of the chunk, kBatch at a time: the batch's
         // scales are read from LDS first, then its MFMAs are issued, then
         // their epilogues run (LDS and MFMA latency hide behind the batch).
-        // Blocks past the end of k need no branch: their staged weights and
-        // both scales are zero, so they add exactly 0.
+        // Blocks past the end of k need no branch: both their staged scales
+        // are zero, so they add exactly 0.
         const int b0 = wave * kWavePart;
         if constexpr (PAIR) {
             // lane (s, c): block bl + (s >> 1) of weight row c, nibble half s & 1
