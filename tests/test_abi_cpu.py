@@ -194,3 +194,18 @@ def test_chain_validation():
     assert L.gq_chain_launch(None, ctypes.c_void_p(A)) == NULL
     assert L.gq_chain_destroy(None) == OK                  # like free(NULL)
     assert L.gq_chain_launches(None) == 0
+
+
+def test_product_path_never_loads_the_oracle():
+    """The binding and the library are the product: importing the binding
+    and loading libgq pull in nothing from oracle/ (a fresh interpreter)."""
+    import subprocess
+    import sys
+    code = ("import sys, gguf_block_quant_amd as gq; gq.raw(); "
+            "bad = [m for m in sys.modules if m == 'oracle' or m.startswith('oracle.')]; "
+            "assert not bad, bad; "
+            "libs = open('/proc/self/maps').read(); "
+            "assert 'liboracle' not in libs and 'oracle.so' not in libs")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
