@@ -44,6 +44,9 @@
 #ifndef GQ_QMV_WAVES1
 #define GQ_QMV_WAVES1 4        // waves per workgroup for un-split rows (they share one LDS copy of x)
 #endif
+#ifndef GQ_QMV_WAVES1_TALL
+#define GQ_QMV_WAVES1_TALL 4   // ... for tall matrices at R_TALL rows per step (2 and 8 measured slower)
+#endif
 #ifndef GQ_QMV_WAVES1_SHORT
 #define GQ_QMV_WAVES1_SHORT 8  // ... for shorter matvecs at R_SHORT rows per step (measured)
 #endif
@@ -197,6 +200,7 @@ template <int WS, int MODE, bool FOLD, int R> struct Waves {
     static constexpr int value =
         WS == 1 ? ((MODE == kQ8X && FOLD)                    ? GQ_QMV_WAVES1_Q8X
                    : (MODE != kFFN && R == GQ_QMV_R_SHORT) ? GQ_QMV_WAVES1_SHORT
+                   : (R == GQ_QMV_R_TALL)                  ? GQ_QMV_WAVES1_TALL
                                                            : GQ_QMV_WAVES1)
                 : (WS < 4 ? 4 : (WS * GQ_QMV_SPLIT_SUBS > 16 ? WS : WS * GQ_QMV_SPLIT_SUBS));
 };
@@ -752,8 +756,8 @@ void argmax_reduce_kernel(const unsigned long long* __restrict__ part, int npart
 namespace {
 
 constexpr int kMaxGrid = GQ_QMV_MAX_GRID;
-// the argmax first stage writes one 8-byte key per workgroup; no matvec grid
-// exceeds kMaxGrid (workgroups have at least 4 waves)
+// the argmax first stage writes one 8-byte key per workgroup (its grid is
+// also capped to the workspace at launch)
 static_assert(sizeof(unsigned long long) * kMaxGrid <= kArgmaxWorkspaceBytes, "argmax workspace too small");
 
 // Workgroups of a kernel that can be resident at once on the device: the
@@ -795,6 +799,9 @@ hipError_t launch_variant(QmvParams p, hipStream_t stream, int* grid_out) {
     int64_t cap = resident_workgroups(kernel, WAVES * kWave);
     const int64_t max_grid = kMaxGrid * 4 / WAVES;
     cap = cap < max_grid ? cap : max_grid;
+    // the argmax first stage writes one 8-byte key per workgroup
+    const int64_t max_parts = static_cast<int64_t>(kArgmaxWorkspaceBytes / sizeof(unsigned long long));
+    if (p.part != nullptr && cap > max_parts) cap = max_parts;
     const int grid = static_cast<int>(iters < cap ? iters : cap);
     if (grid_out != nullptr) *grid_out = grid;
     return launch_kernel(kernel, dim3(grid), dim3(WAVES * kWave), stream, p);
