@@ -7,15 +7,18 @@
 //    (32 elements). Lane l of a wave owns units l, l+64, ... of its K-slice,
 //    so each load instruction reads 1 KiB of one row contiguously.
 //  * The activation values a lane needs for its units are loaded once into
-//    VGPRs and reused for every row the wave streams (x is read from HBM
-//    once per wave, not once per row).
+//    VGPRs and reused for every row the wave streams; for k <= 8192 the
+//    workgroup first stages all of x in LDS (one read of x per workgroup).
 //  * A wave streams R rows per step (R x NI independent 16-byte loads in
 //    flight per lane), dequantises and dot-reduces in registers, and sums
-//    the lanes with DPP (wave_sum), fixed order, no atomics.
+//    the lanes with DPP (wave_sum), fixed order, no atomics. The next row
+//    group's loads go out after the current group's dot, into the same
+//    registers.
 //  * Long rows (large k) are split over WS waves of the workgroup; their
 //    partial sums meet in LDS and are added in slice order.
-//  * The grid is persistent-ish: workgroups stride over row groups so each
-//    wave amortises its activation load over many rows.
+//  * The grid is persistent: at most the resident workgroups, striding over
+//    the row groups, so each wave amortises its activation load over many
+//    rows.
 // The decode projection being a weight-streaming matvec, and the lesson that
 // an M == 1 product wants its own kernel rather than a tiled GEMM, follow the
 // SafeC Gemma 4 DESIGN_NOTES page ("A dedicated GEMV kernel for the M==1
