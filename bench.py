@@ -862,6 +862,11 @@ def stats_summary(args):
         "#       --output-format csv -- python3 $R/bench.py > $R/%s.log" % run_dir.rstrip("/"),
         "#   python3 bench.py --stats-summary %s --write-profile"
         % (run_dir + ("," + bench_json if bench_json else "")),
+    ]
+    if bench_json:
+        lines.append("# (%s: the output of `python3 bench.py > %s`, the same command without the profiler)"
+                     % (bench_json, bench_json))
+    lines += [
         "# durations in microseconds; kernel_source_hash = %s" % kernel_source_hash(),
         "# calls cover the whole run: warm-up, the timed steps, the breakdown, the extras and the",
         "# per-config pass (eager and graph launches, MALL-hot), so an average mixes those contexts",
