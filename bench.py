@@ -373,12 +373,32 @@ def per_config(step, ceiling_gbps, log, rotate_bytes=2 << 30):
                  [pair for pair in zip(gate_up, down)]))
     rows.append(("C4 qmv_q8_0 262144x2048", 570425344, 8192 + 1048576,
                  [(L.gq_qmv_q8_0, (P(q), P(d), 262144, 2048, P(x4), P(y4), sp)) for q, d in step.vocab_sets]))
+    # one GPU's share when the path is split over 8 GPUs (rows of the vocab
+    # head; gate/up rows and down's k for the FFN, whose partial y would then
+    # be summed across GPUs): the kernels at the shapes one GPU would run.
+    # Row shards are contiguous views of the full copies; down's k shards
+    # are packed on their own.
+    y4s = torch.empty(32768, dtype=torch.float32, device=dev)
+    rows.append(("C4/8 qmv_q8_0 32768x2048 (one GPU's rows of 8)", 71303168, 8192 + 131072,
+                 [(L.gq_qmv_q8_0, (P(q[s * 32768:(s + 1) * 32768]), P(d[s * 32768:(s + 1) * 32768]), 32768, 2048,
+                                   P(x4), P(y4s), sp)) for q, d in step.vocab_sets for s in range(8)]))
+    wd_blocks = host["c3"]["wd"]
+    wds = [copies(Q4, np.ascontiguousarray(wd_blocks[:, s * 32:(s + 1) * 32]), 2048, 1024, nf) for s in range(8)]
+    h3s, y3s = torch.empty(1024, dtype=torch.float32, device=dev), torch.empty(2048, dtype=torch.float32, device=dev)
+    gate_up8 = [(L.gq_qffn_gate_up_gelu, (P(g[0][s * 1024:(s + 1) * 1024]), P(g[1][s * 1024:(s + 1) * 1024]),
+                                          P(u[0][s * 1024:(s + 1) * 1024]), P(u[1][s * 1024:(s + 1) * 1024]),
+                                          1024, 2048, P(x3), P(h3s), sp))
+                for g, u in zip(wg, wu) for s in range(8)]
+    down8 = [(L.gq_qmv_q4_0, (P(q), P(d), 2048, 1024, P(h3s), P(y3s), sp)) for c in range(nf) for s in range(8)
+             for q, d in [wds[s][c]]]
+    rows.append(("C3/8 FFN gate+up 2x1024x2048 then down 2048x1024 (one GPU's share of 8, pairs)",
+                 3 * 1179648, 8192 + 2 * 4096 + 8192, [pair for pair in zip(gate_up8, down8)]))
     w5 = copies(Q4, host["c5"]["w"], 8192, 2048, ncopies(9437184))
     for m in (8, 16, 32):
         rows.append(("C5 qmm_tile_m 8192x2048 M=%d" % m, 9437184, m * 2176 + m * 8192 * 4,
                      [(L.gq_qmm_tile_m, (P(q), P(d), 8192, 2048, m, P(acts[m][0]), P(acts[m][1]), P(yt[m]), None,
                                          sp)) for q, d in w5]))
-    keep = [w1, w2, wg, wu, wd, w5, x1, y1, x2, y2, xq2, xd2, x3, h3, y3, x4, y4, acts, yt]
+    keep = [w1, w2, wg, wu, wd, wds, w5, x1, y1, x2, y2, xq2, xd2, x3, h3, y3, x4, y4, y4s, h3s, y3s, acts, yt]
 
     def issue(launch):
         for fn, fargs in (launch if isinstance(launch[0], tuple) else (launch,)):

@@ -61,6 +61,7 @@ def test_pack_unaligned_source():
 SHAPES = [
     (Q8, 64, 256),       # the small Q8_0 workload
     (Q4, 2048, 2048),    # the 2048 x 2048 Q4_0 workload
+    (Q8, 32768, 2048),   # one GPU's rows of the vocab head split 8 ways
     (Q8, 1, 32), (Q4, 1, 32),                # smallest legal shape
     (Q8, 1001, 96), (Q4, 1001, 160),         # ragged rows, partial wave of units
     (Q8, 300, 1056), (Q4, 300, 3040),        # K not a multiple of a wave's span
@@ -279,7 +280,8 @@ def _ffn_case(n_ff, k, seed):
     return wl, down(h), down(y)
 
 
-@pytest.mark.parametrize("n_ff,k", [(8192, 2048), (1056, 96), (64, 32), (224, 8192), (96, 16384)])
+@pytest.mark.parametrize("n_ff,k", [(8192, 2048), (1024, 2048),   # the FFN; one GPU's share of 8
+                                    (1056, 96), (64, 32), (224, 8192), (96, 16384)])
 def test_ffn_stage_by_stage(n_ff, k):
     wl, h, y = _ffn_case(n_ff, k, seed=0)
     ref = oracle.ffn_gate_up(Q4, wl["wg"], wl["wu"], n_ff, k, wl["x"])
