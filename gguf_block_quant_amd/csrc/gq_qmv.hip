@@ -33,7 +33,7 @@
 #define GQ_QMV_MAX_GRID 1280   // workgroups of 4 waves (5 per CU on 256 CUs; the vocabulary head, measured)
 #endif
 #ifndef GQ_QMV_R_SHORT
-#define GQ_QMV_R_SHORT 1         // rows per wave step for shorter (n < 65536) un-split matrices
+#define GQ_QMV_R_SHORT 1         // rows per wave step for shorter un-split matrices
 #endif
 #ifndef GQ_QMV_R_FFN
 #define GQ_QMV_R_FFN 2           // rows per wave step of the gate+up pass (each a gate and an up row)
@@ -60,7 +60,13 @@
 #define GQ_QMV_R_Q8X 1         // rows per wave step of the integer path quantising x in its prologue (measured)
 #endif
 #ifndef GQ_QMV_R_TALL
-#define GQ_QMV_R_TALL 4        // rows per wave step for tall (n >= 65536) un-split matrices
+#define GQ_QMV_R_TALL 4        // rows per wave step for tall un-split matrices
+#endif
+#ifndef GQ_QMV_TALL_MIN_BYTES
+#define GQ_QMV_TALL_MIN_BYTES (16 << 20)   // fp32-x matvecs with at least this many quant bytes take R_TALL rows
+#endif                                      // per step (measured: Q8_0 from 8192 x 2048, Q4_0 from 16384 x 2048)
+#ifndef GQ_QMV_TALL_MIN_N
+#define GQ_QMV_TALL_MIN_N 65536  // ... the other un-split paths from this many rows
 #endif
 #ifndef GQ_QMV_R_SPLIT
 #define GQ_QMV_R_SPLIT 4         // rows per wave step when a row is split over 4 or 8 waves
@@ -221,8 +227,9 @@ void qmv_kernel(const QmvParams p) {
     constexpr int SUBS = WAVES / WS;                // independent row groups per workgroup
     constexpr int NMAT = (MODE == kFFN) ? 2 : 1;
     const int lane = threadIdx.x & (kWave - 1);
-    // Instantiations for very tall matrices (n >= 65536 takes R_TALL rows per
-    // step at WS = 1): each wave walks many row groups. These keep the wave
+    // Instantiations for tall matrices (R_TALL rows per step at WS = 1: fp32
+    // x from 16 MiB of quants, the other paths from 65536 rows): each wave
+    // walks many row groups. These keep the wave
     // index in a scalar register (the row arithmetic and each row's base
     // address are then scalar), one scale per 32-bit register, and the
     // pinned loop below; so do the gate+up pass and split rows. Measured on
@@ -834,7 +841,9 @@ hipError_t launch_cfg(QmvParams p, hipStream_t stream, int* grid_out) {
     } else if constexpr (WS >= 4) {
         return launch_rows<TYPE, MODE, NI, WS, GQ_QMV_R_SPLIT>(p, stream, grid_out);
     } else {
-        if (p.n >= 65536) return launch_rows<TYPE, MODE, NI, WS, GQ_QMV_R_TALL>(p, stream, grid_out);
+        const bool tall = MODE == kF32 ? static_cast<int64_t>(p.n) * p.units * 16 >= GQ_QMV_TALL_MIN_BYTES
+                                       : p.n >= GQ_QMV_TALL_MIN_N;
+        if (tall) return launch_rows<TYPE, MODE, NI, WS, GQ_QMV_R_TALL>(p, stream, grid_out);
         if constexpr (MODE == kQ8X) {
             if (p.x != nullptr) return launch_rows<TYPE, MODE, NI, WS, GQ_QMV_R_Q8X>(p, stream, grid_out);
         }

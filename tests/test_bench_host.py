@@ -81,7 +81,7 @@ def test_counter_summary_normalises_grbm_over_xcds(tmp_path, capsys):
     _write_counters(str(tmp_path / "b"), b)
     bench.counters_summary(argparse.Namespace(counters_summary="%s,%s" % (tmp_path / "a", tmp_path / "b"),
                                               write_profile=False))
-    line = [ln for ln in capsys.readouterr().out.splitlines() if ln.startswith("qmv Q8_0 fp32 x: vocab")][0]
+    line = [ln for ln in capsys.readouterr().out.splitlines() if ln.startswith("qmv Q8_0 fp32 x, tall: vocab")][0]
     fields = line.split()
     assert "50.0%" in fields and "25.00%" in fields
 
@@ -125,6 +125,6 @@ def test_stats_summary_averages_the_timed_region_from_the_trace(tmp_path, capsys
     plain.write_text('{"warmup": 2, "steps": 3, "roofline": {"avg_launch_us": 87.72, "frac": 0.81}}\n')
     bench.stats_summary(argparse.Namespace(stats_summary="%s,%s" % (d, plain), write_profile=False))
     out = capsys.readouterr().out
-    assert "timed region's launches only" in out and ": 86.00 us" in out
+    assert "timed region's launches" in out and "B / 86.00 us" in out
     assert "90.30 us" in out and "difference 5.0%" in out
     assert "87.72 us" in out and "difference 2.0%" in out and "0.810" in out

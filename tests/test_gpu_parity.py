@@ -62,6 +62,8 @@ SHAPES = [
     (Q8, 64, 256),       # the small Q8_0 workload
     (Q4, 2048, 2048),    # the 2048 x 2048 Q4_0 workload
     (Q8, 32768, 2048),   # one GPU's rows of the vocab head split 8 ways
+    (Q8, 8192, 2048), (Q8, 8195, 2048),      # 16 MiB of quants: four rows per step (ragged)
+    (Q4, 16384, 2048), (Q4, 12288, 2048),    # ... Q4_0 at and below that size
     (Q8, 1, 32), (Q4, 1, 32),                # smallest legal shape
     (Q8, 1001, 96), (Q4, 1001, 160),         # ragged rows, partial wave of units
     (Q8, 300, 1056), (Q4, 300, 3040),        # K not a multiple of a wave's span
