@@ -65,8 +65,11 @@
 #ifndef GQ_QMV_TALL_MIN_BYTES
 #define GQ_QMV_TALL_MIN_BYTES (16 << 20)   // fp32-x matvecs with at least this many quant bytes take R_TALL rows
 #endif                                      // per step (measured: Q8_0 from 8192 x 2048, Q4_0 from 16384 x 2048)
+#ifndef GQ_QMV_TALL_MIN_BYTES_Q8
+#define GQ_QMV_TALL_MIN_BYTES_Q8 (32 << 20)  // ... pre-quantised x from this many (measured: Q8_0 16384 x 2048
+#endif                                        // 8.23 -> 7.74 us, 8192 x 2048 slower)
 #ifndef GQ_QMV_TALL_MIN_N
-#define GQ_QMV_TALL_MIN_N 65536  // ... the other un-split paths from this many rows
+#define GQ_QMV_TALL_MIN_N 65536  // ... the other un-split paths (gate+up, x quantised in the kernel) from this many rows
 #endif
 #ifndef GQ_QMV_R_SPLIT
 #define GQ_QMV_R_SPLIT 4         // rows per wave step when a row is split over 4 or 8 waves
@@ -228,8 +231,8 @@ void qmv_kernel(const QmvParams p) {
     constexpr int NMAT = (MODE == kFFN) ? 2 : 1;
     const int lane = threadIdx.x & (kWave - 1);
     // Instantiations for tall matrices (R_TALL rows per step at WS = 1: fp32
-    // x from 16 MiB of quants, the other paths from 65536 rows): each wave
-    // walks many row groups. These keep the wave
+    // x from 16 MiB of quants, pre-quantised x from 32 MiB, the other paths
+    // from 65536 rows): each wave walks many row groups. These keep the wave
     // index in a scalar register (the row arithmetic and each row's base
     // address are then scalar), one scale per 32-bit register, and the
     // pinned loop below; so do the gate+up pass and split rows. Measured on
@@ -841,8 +844,10 @@ hipError_t launch_cfg(QmvParams p, hipStream_t stream, int* grid_out) {
     } else if constexpr (WS >= 4) {
         return launch_rows<TYPE, MODE, NI, WS, GQ_QMV_R_SPLIT>(p, stream, grid_out);
     } else {
-        const bool tall = MODE == kF32 ? static_cast<int64_t>(p.n) * p.units * 16 >= GQ_QMV_TALL_MIN_BYTES
-                                       : p.n >= GQ_QMV_TALL_MIN_N;
+        const int64_t quant_bytes = static_cast<int64_t>(p.n) * p.units * 16;
+        const bool tall = MODE == kF32                        ? quant_bytes >= GQ_QMV_TALL_MIN_BYTES
+                          : (MODE == kQ8X && p.x == nullptr) ? quant_bytes >= GQ_QMV_TALL_MIN_BYTES_Q8
+                                                             : p.n >= GQ_QMV_TALL_MIN_N;
         if (tall) return launch_rows<TYPE, MODE, NI, WS, GQ_QMV_R_TALL>(p, stream, grid_out);
         if constexpr (MODE == kQ8X) {
             if (p.x != nullptr) return launch_rows<TYPE, MODE, NI, WS, GQ_QMV_R_Q8X>(p, stream, grid_out);

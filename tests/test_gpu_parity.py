@@ -198,6 +198,7 @@ def test_quantize_ragged_shapes(m, k):
 
 
 INT_SHAPES = [(Q4, 2048, 2048), (Q8, 64, 256), (Q4, 1, 32), (Q8, 1, 32), (Q4, 999, 96),
+              (Q8, 16384, 2048), (Q8, 16387, 2048), (Q4, 32768, 2048), (Q8, 8192, 2048),   # 32 MiB crossover
               (Q8, 777, 1056), (Q4, 300, 8192), (Q8, 300, 8192), (Q4, 33, 32768), (Q4, 77, 16384),
               (Q8, 5, 16384)]
 
