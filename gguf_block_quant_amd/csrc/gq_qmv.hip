@@ -641,16 +641,34 @@ void qmv_kernel(const QmvParams p) {
             for (int r = 0; r < R; ++r) acc[m][r] = wave_sum(acc[m][r]);
 
         if constexpr (WS == 1) {
-            if (lane == 0) {
+            // The gate+up pass and the folded variants: lane r finishes row
+            // r of the group (the reduced sums are wave-uniform), so the R
+            // rows' epilogues -- GELU, soft cap, argmax key -- run side by
+            // side (measured: gate+up 5.91 -> 5.63 us, the fused vocab head
+            // 90.8 -> 88.9 us). The plain matvec keeps one lane storing its
+            // R rows (85.4 vs 86.0 us for the vocab head).
+            constexpr bool kLaneRows = MODE == kFFN || FOLD;
+            if constexpr (kLaneRows) {
+                if (lane < R) {
+                    float a0 = acc[0][0], a1 = acc[NMAT - 1][0];
+#pragma unroll
+                    for (int r = 1; r < R; ++r) {
+                        a0 = lane == r ? acc[0][r] : a0;
+                        a1 = lane == r ? acc[NMAT - 1][r] : a1;
+                    }
+                    const int row = r0 + lane;
+                    if (row < p.n) {
+                        if constexpr (MODE == kFFN)
+                            emit(row, gelu_tanh(inv * a0) * (inv * a1));
+                        else
+                            emit(row, inv * a0);
+                    }
+                }
+            } else if (lane == 0) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     const int row = r0 + r;
-                    if (row < p.n) {
-                        if constexpr (MODE == kFFN)
-                            emit(row, gelu_tanh(inv * acc[0][r]) * (inv * acc[1][r]));
-                        else
-                            emit(row, inv * acc[0][r]);
-                    }
+                    if (row < p.n) emit(row, inv * acc[0][r]);
                 }
             }
         } else {
