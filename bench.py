@@ -814,14 +814,14 @@ KERNEL_LABELS = [
     ("qmv_kernel<8, 0, 2, 1, 4, false>", "qmv Q8_0 fp32 x, tall: vocab 262144 (+1/8) x2048"),
     ("qmv_kernel<8, 0, 2, 1, 4, true>", "qmv Q8_0 + rmsnorm + softcap + argmax stage 1: vocab"),
     ("argmax_reduce_kernel", "argmax stage 2 (one workgroup)"),
-    ("qmv_kernel<2, 2, 1, 1, 2, false>", "FFN gate+up GELU: 2 x 8192x2048 Q4_0"),
+    ("qmv_kernel<2, 2, 1, 1, 2, false>", "FFN gate+up GELU Q4_0: 2 x 8192 (+1/8) x2048"),
     ("qmv_kernel<2, 2, 1, 1, 2, true>", "FFN gate+up GELU + rmsnorm"),
     ("qmv_kernel<2, 0, 1, 4, 4, false>", "qmv Q4_0 fp32 x: down 2048x8192"),
-    ("qmv_kernel<2, 0, 1, 1, 2, false>", "qmv Q4_0 fp32 x: 2048x2048"),
-    ("qmv_kernel<2, 0, 1, 1, 2, true>", "qmv Q4_0 + rmsnorm + residual: 2048x2048"),
-    ("qmv_kernel<2, 1, 1, 1, 2, false>", "qmv Q4_0 Q8_0 x: 2048x2048 (pre-quantised, extra)"),
-    ("qmv_kernel<2, 1, 1, 1, 2, true>", "qmv Q4_0 Q8_0 x quantised in the prologue: 2048x2048"),
-    ("qmv_kernel<8, 0, 1, 1, 2, false>", "qmv Q8_0 fp32 x: 64x256 (latency point)"),
+    ("qmv_kernel<2, 0, 1, 1, 1, false>", "qmv Q4_0 fp32 x: 2048x2048 (+ down's 2048x1024 shard)"),
+    ("qmv_kernel<2, 0, 1, 1, 1, true>", "qmv Q4_0 + rmsnorm + residual: 2048x2048"),
+    ("qmv_kernel<2, 1, 1, 1, 1, false>", "qmv Q4_0 Q8_0 x: 2048x2048 (pre-quantised, extra)"),
+    ("qmv_kernel<2, 1, 1, 1, 1, true>", "qmv Q4_0 Q8_0 x quantised in the prologue: 2048x2048"),
+    ("qmv_kernel<8, 0, 1, 1, 1, false>", "qmv Q8_0 fp32 x: 64x256 (latency point)"),
     ("tile_kernel<1, true>", "tile M <= 8, paired blocks: 8192x2048 at M = 8 (and 4)"),
     ("tile_kernel<1, false>", "tile M <= 16: 8192x2048 at M = 16"),
     ("tile_kernel<2, false>", "tile M <= 32: 8192x2048 at M = 32"),
