@@ -673,16 +673,96 @@ def pmc_mode(args, log):
 
 
 def pmc_step_mode(args, log):
-    """Three steps (every launch of the step, 3 times), for the VALU and
-    MFMA counter passes."""
+    """Three steps (every launch of the step, 3 times), then a calibration
+    copy of known size (3 launches), for the per-kernel counter passes
+    (VALU / MFMA, and HBM bytes). Prints the step's launches with their
+    algorithmic bytes as one JSON line, in launch order."""
     import torch
 
     step = Step(1, log)
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for i in range(3):
         step.run(i)
+    for _ in range(3):
+        dst.copy_(src)
     torch.cuda.synchronize()
-    log("pmc pass done: 3 steps of %d launches" % len(step.names))
+    print(json.dumps({"step_launches": [[n, w, o] for n, _, _, w, o in step.sets[0]], "steps": 3}), flush=True)
+    log("pmc pass done: 3 steps of %d launches, 3 x copy of %d bytes" % (len(step.names), COPY_BYTES))
+
+
+STEP_TRAFFIC_FILE = os.path.join(PROFILES, "decode_step_hbm_traffic.txt")
+
+
+def _counter_dispatches(run_dir, counter):
+    """(dispatch id, kernel, grid, value) of one counter, in dispatch order."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % run_dir)
+    rows = []
+    for fn in files:
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") == counter:
+                    rows.append((int(row["Dispatch_Id"]), row["Kernel_Name"], int(row["Grid_Size"]),
+                                 float(row["Counter_Value"])))
+    return sorted(rows)
+
+
+def step_traffic_summary(args):
+    """HBM bytes of every kernel of the step against its algorithmic bytes,
+    from a FETCH_SIZE and a WRITE_SIZE run of ``--mode pmc-step``: the step's
+    kernels are its matvec and tile dispatches in launch order (3 steps);
+    each counter is scaled by its reading for the device copy of known size
+    at the end of the same run."""
+    fetch_dir, write_dir = args.step_traffic_summary.split(",")
+    run = None
+    for line in open(fetch_dir.rstrip("/") + ".log"):
+        if line.startswith('{"step_launches"'):
+            run = json.loads(line)
+    if run is None:
+        raise SystemExit("no step_launches line in %s.log" % fetch_dir.rstrip("/"))
+    launches, steps = run["step_launches"], run["steps"]
+    per = {}
+    for counter, run_dir in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_dispatches(run_dir, counter)
+        work = [r for r in rows if "qmv_kernel" in r[1] or "tile_kernel" in r[1]]
+        if len(work) != steps * len(launches):
+            raise SystemExit("%s: %d matvec/tile dispatches, expected %d" % (run_dir, len(work),
+                                                                             steps * len(launches)))
+        copies = [r for r in rows if "copy" in r[1].lower()]
+        big = max(r[2] for r in copies)
+        cal = [r[3] for r in copies if r[2] == big][-3:]
+        factor = COPY_BYTES / (1024.0 * (sum(cal) / len(cal)))
+        for i, r in enumerate(work):
+            per.setdefault(launches[i % len(launches)][0], {}).setdefault(counter, []).append(
+                r[3] * 1024.0 * factor)
+        per.setdefault("_factor", {})[counter] = factor
+    lines = [
+        "# HBM traffic per kernel of one decode step (bench.py --mode pmc-step: 3 steps), MI355X",
+        "# commands (repository root R on the GPU host; one counter per run):",
+        "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -d $R/%s -o run \\" % fetch_dir,
+        "#       --output-format csv -- python3 $R/bench.py --mode pmc-step > $R/%s.log" % fetch_dir.rstrip("/"),
+        "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -d $R/%s -o run \\" % write_dir,
+        "#       --output-format csv -- python3 $R/bench.py --mode pmc-step > $R/%s.log" % write_dir.rstrip("/"),
+        "#   python3 bench.py --step-traffic-summary %s,%s --write-profile" % (fetch_dir, write_dir),
+        "# each counter scaled by its reading for a %d-byte device copy in the same run (factors: FETCH_SIZE "
+        "%.4f, WRITE_SIZE %.4f); bytes per launch, mean of %d launches"
+        % (COPY_BYTES, per["_factor"]["FETCH_SIZE"], per["_factor"]["WRITE_SIZE"], steps),
+        "# algorithmic = weight blocks + activations read + outputs written, as the benchmark counts them",
+        "# kernel_source_hash = %s" % kernel_source_hash(),
+        "%-46s %13s %11s %13s %8s" % ("launch", "fetch_B", "write_B", "algorithmic_B", "ratio"),
+    ]
+    for name, w, o in launches:
+        f = sum(per[name]["FETCH_SIZE"]) / steps
+        wr = sum(per[name]["WRITE_SIZE"]) / steps
+        lines.append("%-46s %13.0f %11.0f %13d %8.3f" % (name[:46], f, wr, w + o, (f + wr) / (w + o)))
+    text = "\n".join(lines) + "\n"
+    print(text)
+    if args.write_profile:
+        with open(STEP_TRAFFIC_FILE, "w") as f:
+            f.write(text)
 
 
 COUNTERS_FILE = os.path.join(PROFILES, "decode_step_valu_mfma_counters.txt")
@@ -970,6 +1050,8 @@ def main():
     ap.add_argument("--pmc-summary", default=None)
     ap.add_argument("--counters-summary", default=None,
                     help="A_DIR,B_DIR of the two --mode pmc-step counter runs -> VALU / MFMA table")
+    ap.add_argument("--step-traffic-summary", metavar="FETCH_DIR,WRITE_DIR",
+                    help="FETCH_SIZE and WRITE_SIZE runs of --mode pmc-step -> HBM bytes per kernel of the step")
     ap.add_argument("--stats-summary", default=None,
                     help="DIR[,BENCH_JSON]: rocprofv3 --kernel-trace --stats output dir of the default run "
                          "(its stdout in DIR.log) and optionally the JSON output of the same command run "
@@ -989,6 +1071,9 @@ def main():
         return
     if args.counters_summary:
         counters_summary(args)
+        return
+    if args.step_traffic_summary:
+        step_traffic_summary(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

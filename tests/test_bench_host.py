@@ -128,3 +128,24 @@ def test_stats_summary_averages_the_timed_region_from_the_trace(tmp_path, capsys
     assert "timed region's launches" in out and "B / 86.00 us" in out
     assert "90.30 us" in out and "difference 5.0%" in out
     assert "87.72 us" in out and "difference 2.0%" in out and "0.810" in out
+
+
+def test_step_traffic_summary_matches_launches_and_calibrates(tmp_path, capsys):
+    # a step of two launches, run twice, then the calibration copy; the copy
+    # reads 2x its bytes on FETCH_SIZE (factor 0.5) and 1x on WRITE_SIZE
+    tile = "void gq::(anonymous namespace)::tile_kernel<1, true>(unsigned char const*)"
+    kib = bench.COPY_BYTES / 1024.0
+    launches = [["qmv_q8_0 vocab", 1000, 24], ["tile M=8", 2000, 48]]
+    fetch = [(COPY, 512, 1.0)] + [(VOCAB, 262144, 2.0), (tile, 262144, 4.0)] * 2 + [(COPY, 1 << 20, 2 * kib)] * 3
+    write = [(COPY, 512, 1.0)] + [(VOCAB, 262144, 0.5), (tile, 262144, 1.0)] * 2 + [(COPY, 1 << 20, kib)] * 3
+    _write_counters(str(tmp_path / "f"), [(k, g, "FETCH_SIZE", v) for k, g, v in fetch])
+    _write_counters(str(tmp_path / "w"), [(k, g, "WRITE_SIZE", v) for k, g, v in write])
+    (tmp_path / "f.log").write_text('[bench] x\n{"step_launches": %s, "steps": 2}\n' % str(launches).replace("'", '"'))
+    bench.step_traffic_summary(argparse.Namespace(step_traffic_summary="%s,%s" % (tmp_path / "f", tmp_path / "w"),
+                                                  write_profile=False))
+    out = capsys.readouterr().out.splitlines()
+    vocab = [ln for ln in out if ln.startswith("qmv_q8_0 vocab")][0].split()
+    tile_ln = [ln for ln in out if ln.startswith("tile M=8")][0].split()
+    # fetch 2 KiB x 0.5 = 1024 B, write 0.5 KiB x 1 = 512 B, against 1024 algorithmic bytes
+    assert vocab[-4:] == ["1024", "512", "1024", "1.500"]
+    assert tile_ln[-4:] == ["2048", "1024", "2048", "1.500"]
