@@ -35,9 +35,11 @@ def _case(qtype, n, k, seed):
 
 FOLD_SHAPES = [(Q8, 64, 256), (Q4, 2048, 2048), (Q4, 2048, 8192), (Q8, 300, 1056), (Q4, 64, 32768),
                (Q8, 515, 4096), (Q4, 1, 32), (Q4, 1001, 8192), (Q8, 77, 16384)]
+# at least 16 MiB of quants: four rows per wave step, rows finished on separate lanes (ragged last group)
+TALL_FOLD_SHAPES = [(Q8, 8195, 2048), (Q4, 16385, 2048)]
 
 
-@pytest.mark.parametrize("qtype,n,k", FOLD_SHAPES)
+@pytest.mark.parametrize("qtype,n,k", FOLD_SHAPES + TALL_FOLD_SHAPES)
 def test_rmsnorm_prologue(qtype, n, k):
     w, x, g, _ = _case(qtype, n, k, n + k)
     qs, d = packed(gq, qtype, w, n, k)
@@ -47,7 +49,7 @@ def test_rmsnorm_prologue(qtype, n, k):
     check_within(y, yr, oracle.fp32_path_bound(ar), "rmsnorm prologue")
 
 
-@pytest.mark.parametrize("qtype,n,k", FOLD_SHAPES[:4])
+@pytest.mark.parametrize("qtype,n,k", FOLD_SHAPES[:4] + TALL_FOLD_SHAPES)
 def test_residual_epilogue_and_in_place(qtype, n, k):
     w, x, g, res = _case(qtype, n, k, 3 * n + k)
     qs, d = packed(gq, qtype, w, n, k)
@@ -107,7 +109,8 @@ def test_vocab_head_full_size():
     assert np.array_equal(down(raw).view(np.uint32), down(gq.qmv_q8_0(qs, d, n, k, up(x))).view(np.uint32))
 
 
-@pytest.mark.parametrize("qtype,n,k", [(Q8, 5000, 256), (Q4, 3000, 2048), (Q4, 700, 8192), (Q8, 1, 32)])
+@pytest.mark.parametrize("qtype,n,k", [(Q8, 5000, 256), (Q4, 3000, 2048), (Q4, 700, 8192), (Q8, 1, 32),
+                                       (Q8, 8195, 2048)])
 def test_argmax_ties_go_to_lowest_row(qtype, n, k):
     rng = np.random.default_rng(n)
     w = synth.weights(rng, qtype, n, k)
