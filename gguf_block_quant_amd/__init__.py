@@ -126,26 +126,70 @@ def _torch():
     return torch
 
 
-def _ptr(t, name):
+def _dtypes(kind):
+    """Accepted torch dtypes per argument kind."""
+    torch = _torch()
+    return {
+        "f32": (torch.float32,),
+        "i8": (torch.int8,),
+        "i32": (torch.int32,),
+        "h16": (torch.int16, torch.uint16),          # binary16 bit patterns
+        "bytes": None,                               # raw bytes: any dtype, sized in bytes
+    }[kind]
+
+
+def _ptr(t, name, kind="bytes", need=0):
+    """Device pointer of tensor ``t`` after checking it can hold what the C
+    entry point will touch: ``need`` elements of ``kind`` (for "bytes", need
+    is a byte count and any dtype is accepted). The C ABI sees only pointers,
+    so a short or mistyped buffer would be read or written out of bounds on
+    the device; it is refused here with ValueError before any call."""
     if t is None:
         return None
-    if not t.is_cuda:
-        raise ValueError("%s must be a device tensor" % name)
+    dts = _dtypes(kind)
+    if dts is not None and t.dtype not in dts:
+        raise ValueError("%s must have dtype %s, got %s" % (name, " or ".join(str(d) for d in dts), t.dtype))
+    have = t.numel() * t.element_size() if dts is None else t.numel()
+    need = max(0, int(need))
+    if have < need:
+        raise ValueError("%s holds %d %s, the call needs %d" % (name, have, "bytes" if dts is None else "elements",
+                                                              need))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
-    return ctypes.c_void_p(t.data_ptr())
+    p = _TensorPtr(t.data_ptr())
+    p.name, p.on_device = name, bool(t.is_cuda)
+    return p
+
+
+class _TensorPtr(ctypes.c_void_p):
+    """A tensor's data pointer; _call checks that it is device memory once
+    every argument's size and dtype has been checked."""
+
+
+def _nb(k):
+    """Blocks (or block scales) per row of k elements."""
+    return max(0, int(k)) // 32
+
+
+class _CurrentStream:
+    """Placeholder for "torch's current stream", resolved by _call after the
+    tensor checks (so those run, and fail, without a device)."""
 
 
 def _stream(stream):
-    torch = _torch()
     if stream is None:
-        stream = torch.cuda.current_stream()
+        return _CurrentStream()
     if isinstance(stream, int):
         return ctypes.c_void_p(stream)
     return ctypes.c_void_p(stream.cuda_stream)
 
 
 def _call(fn, *args):
+    for a in args:
+        if isinstance(a, _TensorPtr) and not a.on_device:
+            raise ValueError("%s must be a device tensor" % a.name)
+    args = [ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream) if isinstance(a, _CurrentStream) else a
+            for a in args]
     st = getattr(raw(), fn)(*args)
     if st != GQ_OK:
         raise GQError(st, fn)
@@ -159,6 +203,23 @@ def _like(ref, shape, dtype):
 # ----------------------------------------------------------------------------
 # entry points
 # ----------------------------------------------------------------------------
+# Each entry point checks its tensors against the sizes its C call will touch
+# (_ptr) for shapes the C ABI accepts; for any other shape the sizes are not
+# checked (_dims gives zeros) and the C entry point returns its own status.
+
+def _dims(n, k, m=1):
+    """(n, k, m) if the C ABI accepts the shape, else (0, 0, 0)."""
+    n, k, m = int(n), int(k), int(m)
+    if n >= 1 and k >= 32 and k % 32 == 0 and m >= 1:
+        return n, k, m
+    return 0, 0, 0
+
+
+def _weights(qtype, qs, d, n, k, names=("qs", "d")):
+    n_, k_, _ = _dims(n, k)
+    qb = packed_qs_bytes(qtype, n_, k_) if n_ else 0
+    return (_ptr(qs, names[0], "bytes", qb), _ptr(d, names[1], "h16", n_ * _nb(k_)))
+
 
 def pack(qtype, blocks, n, k, qs=None, d=None, stream=None):
     """GGUF blocks (device uint8, n*k/32 blocks) -> packed (qs, d)."""
@@ -168,7 +229,9 @@ def pack(qtype, blocks, n, k, qs=None, d=None, stream=None):
                    torch.int8 if qtype == TYPE_Q8_0 else torch.uint8)
     if d is None:
         d = _like(blocks, (n, k // 32), torch.int16)
-    _call("gq_pack", qtype, _ptr(blocks, "blocks"), n, k, _ptr(qs, "qs"), _ptr(d, "d"), _stream(stream))
+    n_, k_, _ = _dims(n, k)
+    _call("gq_pack", qtype, _ptr(blocks, "blocks", "bytes", n_ * _nb(k_) * block_bytes(qtype)), n, k,
+          *_weights(qtype, qs, d, n, k), _stream(stream))
     return qs, d
 
 
@@ -180,75 +243,84 @@ def quantize_q8_0(x, xq=None, xd=None, stream=None):
         xq = _like(x, tuple(x.shape), torch.int8)
     if xd is None:
         xd = _like(x, tuple(x.shape[:-1]) + (k // 32,), torch.int16)
-    _call("gq_quantize_q8_0", _ptr(x, "x"), m, k, _ptr(xq, "xq"), _ptr(xd, "xd"), _stream(stream))
+    m_, k_, _ = _dims(m, k)
+    _call("gq_quantize_q8_0", _ptr(x, "x", "f32", m_ * k_), m, k, _ptr(xq, "xq", "i8", m_ * k_),
+          _ptr(xd, "xd", "h16", m_ * _nb(k_)), _stream(stream))
     return xq, xd
 
 
-def _qmv_f32(fn, qs, d, n, k, x, y, stream):
+def _qmv_f32(fn, qtype, qs, d, n, k, x, y, stream):
     torch = _torch()
     if y is None:
         y = _like(x, (n,), torch.float32)
-    _call(fn, _ptr(qs, "qs"), _ptr(d, "d"), n, k, _ptr(x, "x"), _ptr(y, "y"), _stream(stream))
+    n_, k_, _ = _dims(n, k)
+    _call(fn, *_weights(qtype, qs, d, n, k), n, k, _ptr(x, "x", "f32", k_), _ptr(y, "y", "f32", n_),
+          _stream(stream))
     return y
 
 
 def qmv_q8_0(qs, d, n, k, x, y=None, stream=None):
-    return _qmv_f32("gq_qmv_q8_0", qs, d, n, k, x, y, stream)
+    return _qmv_f32("gq_qmv_q8_0", TYPE_Q8_0, qs, d, n, k, x, y, stream)
 
 
 def qmv_q4_0(qs, d, n, k, x, y=None, stream=None):
-    return _qmv_f32("gq_qmv_q4_0", qs, d, n, k, x, y, stream)
+    return _qmv_f32("gq_qmv_q4_0", TYPE_Q4_0, qs, d, n, k, x, y, stream)
 
 
-def _qmv_q8(fn, qs, d, n, k, xq, xd, y, blockdots, stream):
+def _qmv_q8(fn, qtype, qs, d, n, k, xq, xd, y, blockdots, stream):
     torch = _torch()
     if y is None:
         y = _like(xq, (n,), torch.float32)
-    _call(fn, _ptr(qs, "qs"), _ptr(d, "d"), n, k, _ptr(xq, "xq"), _ptr(xd, "xd"), _ptr(y, "y"),
-          _ptr(blockdots, "blockdots"), _stream(stream))
+    n_, k_, _ = _dims(n, k)
+    _call(fn, *_weights(qtype, qs, d, n, k), n, k, _ptr(xq, "xq", "i8", k_), _ptr(xd, "xd", "h16", _nb(k_)),
+          _ptr(y, "y", "f32", n_), _ptr(blockdots, "blockdots", "i32", n_ * _nb(k_)), _stream(stream))
     return y
 
 
 def qmv_q8_0_q8(qs, d, n, k, xq, xd, y=None, blockdots=None, stream=None):
-    return _qmv_q8("gq_qmv_q8_0_q8", qs, d, n, k, xq, xd, y, blockdots, stream)
+    return _qmv_q8("gq_qmv_q8_0_q8", TYPE_Q8_0, qs, d, n, k, xq, xd, y, blockdots, stream)
 
 
 def qmv_q4_0_q8(qs, d, n, k, xq, xd, y=None, blockdots=None, stream=None):
-    return _qmv_q8("gq_qmv_q4_0_q8", qs, d, n, k, xq, xd, y, blockdots, stream)
+    return _qmv_q8("gq_qmv_q4_0_q8", TYPE_Q4_0, qs, d, n, k, xq, xd, y, blockdots, stream)
 
 
-def _qmv_q8x(fn, qs, d, n, k, x, y, blockdots, xq_out, xd_out, stream):
+def _qmv_q8x(fn, qtype, qs, d, n, k, x, y, blockdots, xq_out, xd_out, stream):
     torch = _torch()
     if y is None:
         y = _like(x, (n,), torch.float32)
-    _call(fn, _ptr(qs, "qs"), _ptr(d, "d"), n, k, _ptr(x, "x"), _ptr(xq_out, "xq_out"), _ptr(xd_out, "xd_out"),
-          _ptr(y, "y"), _ptr(blockdots, "blockdots"), _stream(stream))
+    n_, k_, _ = _dims(n, k)
+    _call(fn, *_weights(qtype, qs, d, n, k), n, k, _ptr(x, "x", "f32", k_), _ptr(xq_out, "xq_out", "i8", k_),
+          _ptr(xd_out, "xd_out", "h16", _nb(k_)), _ptr(y, "y", "f32", n_),
+          _ptr(blockdots, "blockdots", "i32", n_ * _nb(k_)), _stream(stream))
     return y
 
 
 def qmv_q8_0_q8x(qs, d, n, k, x, y=None, blockdots=None, xq_out=None, xd_out=None, stream=None):
     """Integer path quantising the fp32 x itself (no separate quantise launch)."""
-    return _qmv_q8x("gq_qmv_q8_0_q8x", qs, d, n, k, x, y, blockdots, xq_out, xd_out, stream)
+    return _qmv_q8x("gq_qmv_q8_0_q8x", TYPE_Q8_0, qs, d, n, k, x, y, blockdots, xq_out, xd_out, stream)
 
 
 def qmv_q4_0_q8x(qs, d, n, k, x, y=None, blockdots=None, xq_out=None, xd_out=None, stream=None):
-    return _qmv_q8x("gq_qmv_q4_0_q8x", qs, d, n, k, x, y, blockdots, xq_out, xd_out, stream)
+    return _qmv_q8x("gq_qmv_q4_0_q8x", TYPE_Q4_0, qs, d, n, k, x, y, blockdots, xq_out, xd_out, stream)
 
 
 def qmv_q8_0_ex(qs, d, n, k, x, norm_weight=None, norm_eps=1e-6, residual=None, y=None, stream=None):
-    return _qmv_ex("gq_qmv_q8_0_ex", qs, d, n, k, x, norm_weight, norm_eps, residual, y, stream)
+    return _qmv_ex("gq_qmv_q8_0_ex", TYPE_Q8_0, qs, d, n, k, x, norm_weight, norm_eps, residual, y, stream)
 
 
 def qmv_q4_0_ex(qs, d, n, k, x, norm_weight=None, norm_eps=1e-6, residual=None, y=None, stream=None):
-    return _qmv_ex("gq_qmv_q4_0_ex", qs, d, n, k, x, norm_weight, norm_eps, residual, y, stream)
+    return _qmv_ex("gq_qmv_q4_0_ex", TYPE_Q4_0, qs, d, n, k, x, norm_weight, norm_eps, residual, y, stream)
 
 
-def _qmv_ex(fn, qs, d, n, k, x, norm_weight, norm_eps, residual, y, stream):
+def _qmv_ex(fn, qtype, qs, d, n, k, x, norm_weight, norm_eps, residual, y, stream):
     torch = _torch()
     if y is None:
         y = _like(x, (n,), torch.float32)
-    _call(fn, _ptr(qs, "qs"), _ptr(d, "d"), n, k, _ptr(x, "x"), _ptr(norm_weight, "norm_weight"),
-          float(norm_eps), _ptr(residual, "residual"), _ptr(y, "y"), _stream(stream))
+    n_, k_, _ = _dims(n, k)
+    _call(fn, *_weights(qtype, qs, d, n, k), n, k, _ptr(x, "x", "f32", k_),
+          _ptr(norm_weight, "norm_weight", "f32", k_), float(norm_eps), _ptr(residual, "residual", "f32", n_),
+          _ptr(y, "y", "f32", n_), _stream(stream))
     return y
 
 
@@ -256,7 +328,8 @@ def argmax_workspace_bytes() -> int:
     return raw().gq_argmax_workspace_bytes()
 
 
-def _qmv_argmax(fn, qs, d, n, k, x, norm_weight, norm_eps, softcap, logits, workspace, index, value, stream):
+def _qmv_argmax(fn, qtype, qs, d, n, k, x, norm_weight, norm_eps, softcap, logits, workspace, index, value,
+                stream):
     torch = _torch()
     if logits is None:
         logits = _like(x, (n,), torch.float32)
@@ -266,24 +339,31 @@ def _qmv_argmax(fn, qs, d, n, k, x, norm_weight, norm_eps, softcap, logits, work
         index = _like(x, (1,), torch.int32)
     if value is None:
         value = _like(x, (1,), torch.float32)
-    _call(fn, _ptr(qs, "qs"), _ptr(d, "d"), n, k, _ptr(x, "x"), _ptr(norm_weight, "norm_weight"),
-          float(norm_eps), float(softcap), _ptr(logits, "logits"), _ptr(workspace, "workspace"),
-          workspace.numel() * workspace.element_size(), _ptr(index, "index"), _ptr(value, "value"),
-          _stream(stream))
+    n_, k_, _ = _dims(n, k)
+    _call(fn, *_weights(qtype, qs, d, n, k), n, k, _ptr(x, "x", "f32", k_),
+          _ptr(norm_weight, "norm_weight", "f32", k_), float(norm_eps), float(softcap),
+          _ptr(logits, "logits", "f32", n_), _ptr(workspace, "workspace", "bytes", argmax_workspace_bytes()),
+          workspace.numel() * workspace.element_size(), _ptr(index, "index", "i32", 1),
+          _ptr(value, "value", "f32", 1), _stream(stream))
     return index, value, logits
 
 
 def qmv_q8_0_argmax(qs, d, n, k, x, norm_weight=None, norm_eps=1e-6, softcap=30.0, logits=None,
                     workspace=None, index=None, value=None, stream=None):
     """Vocabulary head: returns (index int32[1], value fp32[1], logits fp32[n])."""
-    return _qmv_argmax("gq_qmv_q8_0_argmax", qs, d, n, k, x, norm_weight, norm_eps, softcap, logits,
+    return _qmv_argmax("gq_qmv_q8_0_argmax", TYPE_Q8_0, qs, d, n, k, x, norm_weight, norm_eps, softcap, logits,
                        workspace, index, value, stream)
 
 
 def qmv_q4_0_argmax(qs, d, n, k, x, norm_weight=None, norm_eps=1e-6, softcap=30.0, logits=None,
                     workspace=None, index=None, value=None, stream=None):
-    return _qmv_argmax("gq_qmv_q4_0_argmax", qs, d, n, k, x, norm_weight, norm_eps, softcap, logits,
+    return _qmv_argmax("gq_qmv_q4_0_argmax", TYPE_Q4_0, qs, d, n, k, x, norm_weight, norm_eps, softcap, logits,
                        workspace, index, value, stream)
+
+
+def _ffn_weights(g_qs, g_d, u_qs, u_d, n_ff, k):
+    return (*_weights(TYPE_Q4_0, g_qs, g_d, n_ff, k, ("g_qs", "g_d")),
+            *_weights(TYPE_Q4_0, u_qs, u_d, n_ff, k, ("u_qs", "u_d")))
 
 
 def qffn_gate_up_gelu_ex(g_qs, g_d, u_qs, u_d, n_ff, k, x, norm_weight=None, norm_eps=1e-6, h=None,
@@ -291,9 +371,10 @@ def qffn_gate_up_gelu_ex(g_qs, g_d, u_qs, u_d, n_ff, k, x, norm_weight=None, nor
     torch = _torch()
     if h is None:
         h = _like(x, (n_ff,), torch.float32)
-    _call("gq_qffn_gate_up_gelu_ex", _ptr(g_qs, "g_qs"), _ptr(g_d, "g_d"), _ptr(u_qs, "u_qs"),
-          _ptr(u_d, "u_d"), n_ff, k, _ptr(x, "x"), _ptr(norm_weight, "norm_weight"), float(norm_eps),
-          _ptr(h, "h"), _stream(stream))
+    n_, k_, _ = _dims(n_ff, k)
+    _call("gq_qffn_gate_up_gelu_ex", *_ffn_weights(g_qs, g_d, u_qs, u_d, n_ff, k), n_ff, k,
+          _ptr(x, "x", "f32", k_), _ptr(norm_weight, "norm_weight", "f32", k_), float(norm_eps),
+          _ptr(h, "h", "f32", n_), _stream(stream))
     return h
 
 
@@ -301,8 +382,9 @@ def qffn_gate_up_gelu(g_qs, g_d, u_qs, u_d, n_ff, k, x, h=None, stream=None):
     torch = _torch()
     if h is None:
         h = _like(x, (n_ff,), torch.float32)
-    _call("gq_qffn_gate_up_gelu", _ptr(g_qs, "g_qs"), _ptr(g_d, "g_d"), _ptr(u_qs, "u_qs"),
-          _ptr(u_d, "u_d"), n_ff, k, _ptr(x, "x"), _ptr(h, "h"), _stream(stream))
+    n_, k_, _ = _dims(n_ff, k)
+    _call("gq_qffn_gate_up_gelu", *_ffn_weights(g_qs, g_d, u_qs, u_d, n_ff, k), n_ff, k,
+          _ptr(x, "x", "f32", k_), _ptr(h, "h", "f32", n_), _stream(stream))
     return h
 
 
@@ -310,8 +392,10 @@ def qmm_tile_m(qs, d, n, k, m, xq, xd, y=None, blockdots=None, stream=None):
     torch = _torch()
     if y is None:
         y = _like(xq, (m, n), torch.float32)
-    _call("gq_qmm_tile_m", _ptr(qs, "qs"), _ptr(d, "d"), n, k, m, _ptr(xq, "xq"), _ptr(xd, "xd"),
-          _ptr(y, "y"), _ptr(blockdots, "blockdots"), _stream(stream))
+    n_, k_, m_ = _dims(n, k, m) if 1 <= int(m) <= 32 else (0, 0, 0)
+    _call("gq_qmm_tile_m", *_weights(TYPE_Q4_0, qs, d, n_, k_), n, k, m, _ptr(xq, "xq", "i8", m_ * k_),
+          _ptr(xd, "xd", "h16", m_ * _nb(k_)), _ptr(y, "y", "f32", m_ * n_),
+          _ptr(blockdots, "blockdots", "i32", m_ * n_ * _nb(k_)), _stream(stream))
     return y
 
 

@@ -56,6 +56,15 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
+// Sum of a double over the 64 lanes of the wave (xor butterfly: lane i and
+// lane i ^ o add the same two values, so every lane ends with the same bits,
+// and the order is fixed run to run).
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
 // Exact int8x4 dot product with int32 accumulate (v_dot4_i32_i8).
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4(static_cast<int>(a), static_cast<int>(b), c, false);

@@ -264,7 +264,7 @@ void qmv_kernel(const QmvParams p) {
     constexpr int kQxWords = kQuantX ? kQuantF4 * kThreads : 1;       // whole rounds, as above
     __shared__ uint32_t qx_s[kQxWords];
     __shared__ uint16_t qd_s[kQuantX ? kQxWords / 8 : 1];
-    __shared__ float nss[WAVES];
+    __shared__ double nss[WAVES];
 
     // ---- this lane's units ------------------------------------------------
     int unit[NI];
@@ -417,14 +417,23 @@ void qmv_kernel(const QmvParams p) {
     // ---- activation registers for this lane's units ----------------------
     // Optional RMSNorm prologue (SafeC Gemma 4 DESIGN_NOTES page, "RMSNorm"):
     // x <- x * (mean(x^2) + eps)^-1/2 * w, the weight multiplying directly.
-    // The scale is one scalar per activation vector, so only w is folded into
-    // the activations here and the scalar multiplies each finished row:
-    // y = inv * (W (x * w)). The sum of squares is taken from the raw x.
+    // The sum of squares of the raw x is taken in fp64 (x^2 of any finite
+    // fp32 value is exact there, and k <= 32768 such terms can neither
+    // overflow nor underflow to zero unless x is zero), and the scale
+    // inv = (sum / k + eps)^-1/2 stays in fp64; w is folded into the staged
+    // activations and inv into each lane's activation registers (an fp64
+    // product rounded once to fp32) before any dot, so the dot products run
+    // on the normalised activations, |x_i * inv| <= sqrt(k), for any finite
+    // x -- no fp32 overflow of the sum or of the scale.
     float xr[(MODE == kQ8X) ? 1 : NI][(MODE == kQ8X) ? 1 : EPU];
     uint32_t xqr[(MODE == kQ8X) ? NI : 1][(MODE == kQ8X) ? EPU / 4 : 1];
     float dxr[NI];
     int sxr[NI];
-    float ss = 0.f;
+    double ss = 0.0;
+    auto norm_scale = [&](double sum) {
+        return 1.0 / sqrt(sum / static_cast<double>(p.k) + static_cast<double>(p.norm_eps));
+    };
+    auto scaled = [](float v, double s) { return static_cast<float>(static_cast<double>(v) * s); };
     if constexpr (kStage) {
         // Un-split rows: every wave of the workgroup needs all of x, so the
         // workgroup reads it (and w) from memory once into LDS, padded to a
@@ -447,14 +456,12 @@ void qmv_kernel(const QmvParams p) {
             if constexpr (FOLD) {
                 if (norm) {
                     const float4 g = gpre[u];
-                    if constexpr (kZeroPass) {
-                        float q = t.x * t.x;
-                        q = fmaf(t.y, t.y, q); q = fmaf(t.z, t.z, q); q = fmaf(t.w, t.w, q);
-                        ss += j < nf4 ? q : 0.f;
-                    } else {
-                        ss = fmaf(t.x, t.x, ss); ss = fmaf(t.y, t.y, ss);
-                        ss = fmaf(t.z, t.z, ss); ss = fmaf(t.w, t.w, ss);
-                    }
+                    double q = static_cast<double>(t.x) * static_cast<double>(t.x);
+                    q = fma(static_cast<double>(t.y), static_cast<double>(t.y), q);
+                    q = fma(static_cast<double>(t.z), static_cast<double>(t.z), q);
+                    q = fma(static_cast<double>(t.w), static_cast<double>(t.w), q);
+                    if constexpr (kZeroPass) ss += j < nf4 ? q : 0.0;
+                    else ss += q;                // t is zero past k
                     t.x *= g.x; t.y *= g.y; t.z *= g.z; t.w *= g.w;
                 }
             }
@@ -472,17 +479,18 @@ void qmv_kernel(const QmvParams p) {
         }
         if constexpr (FOLD) {
             if (norm) {
-                ss = wave_sum(ss);
+                ss = wave_sum_f64(ss);
                 if (lane == 0) nss[wave] = ss;
             }
         }
         __syncthreads();
+        double inv = 1.0;
         if constexpr (FOLD) {
             if (norm) {
-                float t = nss[0];
+                double t = nss[0];
 #pragma unroll
                 for (int w = 1; w < WAVES; ++w) t += nss[w];
-                ss = t;
+                inv = norm_scale(t);
             }
         }
 #pragma unroll
@@ -492,7 +500,11 @@ void qmv_kernel(const QmvParams p) {
             const float* xs = &xstage[unit[i] * kPitch];
 #pragma unroll
             for (int v = 0; v < EPU / 4; ++v) {
-                const float4 t = *reinterpret_cast<const float4*>(xs + 4 * v);
+                float4 t = *reinterpret_cast<const float4*>(xs + 4 * v);
+                if constexpr (FOLD) {
+                    t.x = scaled(t.x, inv); t.y = scaled(t.y, inv);
+                    t.z = scaled(t.z, inv); t.w = scaled(t.w, inv);
+                }
                 xr[i][4 * v + 0] = t.x; xr[i][4 * v + 1] = t.y;
                 xr[i][4 * v + 2] = t.z; xr[i][4 * v + 3] = t.w;
             }
@@ -568,27 +580,26 @@ void qmv_kernel(const QmvParams p) {
 #pragma unroll
                     for (int v = 0; v < EPU / 4; ++v) {
                         const float4 g = gd4[i][v];
-                        ss = fmaf(xr[i][4 * v + 0], xr[i][4 * v + 0], ss);
-                        ss = fmaf(xr[i][4 * v + 1], xr[i][4 * v + 1], ss);
-                        ss = fmaf(xr[i][4 * v + 2], xr[i][4 * v + 2], ss);
-                        ss = fmaf(xr[i][4 * v + 3], xr[i][4 * v + 3], ss);
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            ss = fma(static_cast<double>(xr[i][4 * v + c]), static_cast<double>(xr[i][4 * v + c]), ss);
                         xr[i][4 * v + 0] *= g.x; xr[i][4 * v + 1] *= g.y;
                         xr[i][4 * v + 2] *= g.z; xr[i][4 * v + 3] *= g.w;
                     }
                 }
-                ss = wave_sum(ss);
+                ss = wave_sum_f64(ss);
                 if (lane == 0) nss[wave] = ss;
                 __syncthreads();
-                float t = nss[sub * WS];
+                double t = nss[sub * WS];
 #pragma unroll
                 for (int sl = 1; sl < WS; ++sl) t += nss[sub * WS + sl];
-                ss = t;
+                const double inv = norm_scale(t);
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+#pragma unroll
+                    for (int e = 0; e < EPU; ++e) xr[i][e] = scaled(xr[i][e], inv);
             }
         }
-    }
-    float inv = 1.0f;
-    if constexpr (MODE != kQ8X && FOLD) {
-        if (norm) inv = 1.0f / sqrtf(ss / static_cast<float>(p.k) + p.norm_eps);
     }
 
     // ---- epilogue of one finished row: residual, soft cap, store, argmax --
@@ -670,16 +681,16 @@ void qmv_kernel(const QmvParams p) {
                     const int row = r0 + lane;
                     if (row < p.n) {
                         if constexpr (MODE == kFFN)
-                            emit(row, gelu_tanh(inv * a0) * (inv * a1));
+                            emit(row, gelu_tanh(a0) * a1);
                         else
-                            emit(row, inv * a0);
+                            emit(row, a0);
                     }
                 }
             } else if (lane == 0) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     const int row = r0 + r;
-                    if (row < p.n) emit(row, inv * acc[0][r]);
+                    if (row < p.n) emit(row, acc[0][r]);
                 }
             }
         } else {
@@ -702,9 +713,9 @@ void qmv_kernel(const QmvParams p) {
                 }
                 if (row < p.n) {
                     if constexpr (MODE == kFFN)
-                        emit(row, gelu_tanh(inv * tot[0]) * (inv * tot[1]));
+                        emit(row, gelu_tanh(tot[0]) * tot[1]);
                     else
-                        emit(row, inv * tot[0]);
+                        emit(row, tot[0]);
                 }
             }
             __syncthreads();
@@ -802,9 +813,6 @@ constexpr int kMaxGrid = GQ_QMV_MAX_GRID;
 // also capped to the workspace at launch)
 static_assert(sizeof(unsigned long long) * kMaxGrid <= kArgmaxWorkspaceBytes, "argmax workspace too small");
 
-// Workgroups of a kernel that can be resident at once on the device: the
-// persistent grid is never larger, so no workgroup waits for a second round.
-// The per-kernel occupancy is a property of the code object, queried once.
 // Compute units of the current device, queried once per device.
 inline int device_cus() {
     constexpr int kMaxDevices = 64;
@@ -821,14 +829,15 @@ inline int device_cus() {
     return cus;
 }
 
+// Workgroups of one kernel that can be resident on a CU at once: a property
+// of that kernel's code object (registers, LDS, workgroup size). The caller
+// keeps the answer in a function-local static of its own instantiation, so
+// every kernel variant has its own (one query per variant per process).
 template <typename K>
-int resident_workgroups(K kernel, int threads) {
-    static const int per_cu = [&] {
-        int b = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kernel, threads, 0) != hipSuccess || b < 1) b = 1;
-        return b;
-    }();
-    return per_cu * device_cus();
+int occupancy_per_cu(K kernel, int threads) {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kernel, threads, 0) != hipSuccess || b < 1) b = 1;
+    return b;
 }
 
 template <int TYPE, int MODE, int NI, int WS, int R, bool FOLD>
@@ -838,7 +847,10 @@ hipError_t launch_variant(QmvParams p, hipStream_t stream, int* grid_out) {
     p.row_groups = (p.n + R - 1) / R;
     const int64_t iters = (static_cast<int64_t>(p.row_groups) + SUBS - 1) / SUBS;
     const auto kernel = qmv_kernel<TYPE, MODE, NI, WS, R, FOLD>;
-    int64_t cap = resident_workgroups(kernel, WAVES * kWave);
+    // resident workgroups: the persistent grid is never larger, so no
+    // workgroup waits for a second dispatch round (one static per variant)
+    static const int per_cu = occupancy_per_cu(kernel, WAVES * kWave);
+    int64_t cap = static_cast<int64_t>(per_cu) * device_cus();
     const int64_t max_grid = kMaxGrid * 4 / WAVES;
     cap = cap < max_grid ? cap : max_grid;
     // the argmax first stage writes one 8-byte key per workgroup

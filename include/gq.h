@@ -45,19 +45,29 @@
  *  - stream is a hipStream_t passed as void*; NULL is the default stream.
  *    Work is enqueued asynchronously on that stream.
  *  - Shapes: n >= 1, k >= 32, k % 32 == 0, else GQ_ERR_SHAPE. Each entry
- *    point documents its maximum k (GQ_ERR_UNSUPPORTED beyond it); n is
- *    limited to 2^31 - 1 rows.
+ *    point documents its maximum k (GQ_ERR_UNSUPPORTED beyond it); n (and
+ *    m of gq_quantize_q8_0) is limited to 2^30 rows (GQ_ERR_UNSUPPORTED
+ *    beyond it).
  *  - Alignment: qs, x, h and xq 16 bytes; d and xd 2 bytes; y and blockdots
  *    4 bytes; else GQ_ERR_ALIGN.
  *  - An output range overlapping any input range gives GQ_ERR_ALIAS.
+ *  - Special values: every binary16 scale bit pattern is accepted; +-0 and
+ *    subnormal scales are decoded exactly. A row with a non-finite weight
+ *    scale (+-Inf, NaN) in any block gets a non-finite output, as the plain
+ *    definition sum_c w[r][c] x[c] does (NaN or +-Inf; which of the two is
+ *    not specified: the kernels factor the block scale out of its 32
+ *    products). Non-finite activations propagate the same way.
  *  - All validation is synchronous and happens before any HIP call: a call
  *    that returns an error has launched nothing and written nothing.
  *  - GQ_ERR_LAUNCH reports a failed kernel launch: the status returned by
  *    hipLaunchKernel for that launch (gq_last_hip_error() gives the HIP
  *    code). Faults inside a kernel are asynchronous and surface at the
  *    caller's next synchronisation.
- *  - No global state: calls are reentrant and thread-safe. Identical inputs
- *    give bitwise-identical outputs (fixed reduction order, no atomics).
+ *  - No mutable shared state: calls are reentrant and thread-safe. libgq
+ *    keeps only read-only caches filled on first use (each device's compute
+ *    unit count, each kernel's resident workgroups per compute unit), which
+ *    every thread computes identically. Identical inputs give
+ *    bitwise-identical outputs (fixed reduction order, no atomics).
  */
 #ifndef GQ_H
 #define GQ_H
@@ -87,10 +97,16 @@ enum {
     GQ_TYPE_Q8_0 = 8         /* GGUF type id of Q8_0 */
 };
 
-/* Version of this header's signatures; bumped on any change. */
+/* Version of this header's signatures; bumped on any change, so that a
+ * caller can probe what the loaded library supports before using it (the
+ * capability probe of the TensorSharp Gemma 4 page, batched fused decode
+ * section: the managed side queries the native library and keeps older
+ * behaviour for what it lacks). */
 int gq_abi_version(void);
 
-/* Static, never-NULL description of a status code. */
+/* Static, never-NULL description of a status code (for the caller's error
+ * messages; same batched fused decode section: failures are reported, not
+ * silently routed to another path). */
 const char *gq_status_str(int status);
 
 /* The hipError_t value (as int) returned by the calling thread's most recent
@@ -111,7 +127,12 @@ size_t gq_packed_d_bytes(int64_t n, int64_t k);
  * gq_pack -- split n x k/32 GGUF blocks (device memory, 34 or 18 bytes each,
  * contiguous, any byte alignment) into the packed qs and d arrays above.
  * No value changes. blocks must not overlap qs or d. Any k that is a
- * multiple of 32 is accepted.
+ * multiple of 32 is accepted. A one-time, load-time re-layout of each weight
+ * into the layout its kernel streams best, derived from the canonical file
+ * and moving the same bytes (Gemma-4-E2B raw-Metal port page,
+ * "Architecture", pack bullet: every tensor stored in kernel layout; Gem
+ * native architecture page, "M4 Max operating assumptions": a packed sidecar
+ * reproducibly derived from the canonical GGUF).
  */
 int gq_pack(int type, const void *blocks, int64_t n, int64_t k,
             void *qs, uint16_t *d, void *stream);
@@ -151,7 +172,10 @@ int gq_qmv_q4_0(const uint8_t *qs, const uint16_t *d, int64_t n, int64_t k,
  *    x * (mean(x^2) + norm_eps)^(-1/2) * norm_weight, with the weight
  *    applied directly (SafeC Gemma 4 DESIGN_NOTES page, "RMSNorm"; Gemma 4
  *    uses norm_eps = 1e-6); norm_weight fp32 [k], 16-byte aligned;
- *    norm_eps >= 0 and finite, else GQ_ERR_VALUE;
+ *    norm_eps >= 0 and finite, else GQ_ERR_VALUE. The sum of squares is
+ *    taken in fp64 and the scale applied to the activations before the
+ *    products, so any finite x is supported as long as every product
+ *    x[c] * norm_weight[c] is finite in fp32 (|x w| <= 3.4e38);
  *  - if residual is not NULL, y[r] = residual[r] + (W x)[r]; residual fp32
  *    [n], 4-byte aligned; y may equal residual (in-place accumulate) but
  *    may not overlap it otherwise.
