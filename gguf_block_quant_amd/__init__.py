@@ -56,6 +56,7 @@ _SIGS = {
     "gq_argmax_workspace_bytes": ([], ctypes.c_size_t),
     "gq_qmv_q8_0_argmax": ([_P, _P, _I64, _I64, _P, _P, _F, _F, _P, _P, ctypes.c_size_t, _P, _P, _P], _I),
     "gq_qmv_q4_0_argmax": ([_P, _P, _I64, _I64, _P, _P, _F, _F, _P, _P, ctypes.c_size_t, _P, _P, _P], _I),
+    "gq_qmv_q8_0_argmax_noalloc": ([_P, _P, _I64, _I64, _P, _P, _F, _F, _P, _P, _P, _P], _I),
     "gq_qmm_tile_m": ([_P, _P, _I64, _I64, _I, _P, _P, _P, _P, _P], _I),
     "gq_chain_begin": ([_P], _I),
     "gq_chain_end": ([_P, ctypes.POINTER(_P)], _I),
@@ -359,6 +360,25 @@ def qmv_q4_0_argmax(qs, d, n, k, x, norm_weight=None, norm_eps=1e-6, softcap=30.
                     workspace=None, index=None, value=None, stream=None):
     return _qmv_argmax("gq_qmv_q4_0_argmax", TYPE_Q4_0, qs, d, n, k, x, norm_weight, norm_eps, softcap, logits,
                        workspace, index, value, stream)
+
+
+def qmv_q8_0_argmax_noalloc(qs, d, n, k, x, norm_weight=None, norm_eps=1e-6, softcap=30.0, logits=None,
+                            index=None, value=None, stream=None):
+    """The vocabulary head without a workspace (library-held device scratch;
+    calls overlapping on one device race). Returns (index, value, logits)."""
+    torch = _torch()
+    if logits is None:
+        logits = _like(x, (n,), torch.float32)
+    if index is None:
+        index = _like(x, (1,), torch.int32)
+    if value is None:
+        value = _like(x, (1,), torch.float32)
+    n_, k_, _ = _dims(n, k)
+    _call("gq_qmv_q8_0_argmax_noalloc", *_weights(TYPE_Q8_0, qs, d, n, k), n, k, _ptr(x, "x", "f32", k_),
+          _ptr(norm_weight, "norm_weight", "f32", k_), float(norm_eps), float(softcap),
+          _ptr(logits, "logits", "f32", n_), _ptr(index, "index", "i32", 1), _ptr(value, "value", "f32", 1),
+          _stream(stream))
+    return index, value, logits
 
 
 def _ffn_weights(g_qs, g_d, u_qs, u_d, n_ff, k):

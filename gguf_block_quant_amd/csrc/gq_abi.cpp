@@ -125,6 +125,24 @@ int qmv_argmax(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k
                                            index, value, as_stream(stream)));
 }
 
+int qmv_argmax_noalloc(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k, const float* x,
+                       const float* norm_w, float norm_eps, float softcap, float* logits, int32_t* index,
+                       float* value, void* stream) {
+    if (x == nullptr || logits == nullptr || index == nullptr || value == nullptr) return GQ_ERR_NULL;
+    int st = check_weights(type, qs, d, n, k);
+    if (st != GQ_OK) return st;
+    if (!aligned(x, 16) || !aligned(logits, 4) || !aligned(index, 4) || !aligned(value, 4)) return GQ_ERR_ALIGN;
+    st = check_fold(norm_w, norm_eps, nullptr);
+    if (st != GQ_OK) return st;
+    if (!(softcap >= 0.0f) || !(softcap < 1e30f)) return GQ_ERR_VALUE;
+    const Range outs[] = {{logits, static_cast<size_t>(n) * 4}, {index, 4}, {value, 4}};
+    const Range ins[] = {{qs, qs_bytes(type, n, k)}, {d, d_bytes(n, k)}, {x, static_cast<size_t>(k) * 4},
+                         {norm_w, norm_w ? static_cast<size_t>(k) * 4 : 0}};
+    if (any_alias(outs, ins)) return GQ_ERR_ALIAS;
+    return status_of(gq::launch_qmv_argmax_noalloc(type, qs, d, n, k, x, norm_w, norm_eps, softcap, logits, index,
+                                                   value, as_stream(stream)));
+}
+
 int qmv_q8(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k, const int8_t* xq,
            const uint16_t* xd, float* y, int32_t* blockdots, void* stream) {
     if (xq == nullptr || xd == nullptr || y == nullptr) return GQ_ERR_NULL;
@@ -253,6 +271,13 @@ int gq_qmv_q4_0_argmax(const uint8_t* qs, const uint16_t* d, int64_t n, int64_t 
                        size_t workspace_bytes, int32_t* index, float* value, void* stream) {
     return qmv_argmax(GQ_TYPE_Q4_0, qs, d, n, k, x, norm_weight, norm_eps, softcap, logits, workspace,
                       workspace_bytes, index, value, stream);
+}
+
+int gq_qmv_q8_0_argmax_noalloc(const int8_t* qs, const uint16_t* d, int64_t n, int64_t k, const float* x,
+                               const float* norm_weight, float norm_eps, float softcap, float* logits,
+                               int32_t* index, float* value, void* stream) {
+    return qmv_argmax_noalloc(GQ_TYPE_Q8_0, qs, d, n, k, x, norm_weight, norm_eps, softcap, logits, index, value,
+                              stream);
 }
 
 int gq_qmv_q8_0_q8(const int8_t* qs, const uint16_t* d, int64_t n, int64_t k, const int8_t* xq,

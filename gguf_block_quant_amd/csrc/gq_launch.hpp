@@ -46,6 +46,12 @@ hipError_t launch_qmv_argmax(int type, const void* qs, const uint16_t* d, int64_
                              const float* x, const float* norm_w, float norm_eps, float softcap,
                              float* y, void* workspace, int32_t* index, float* value, hipStream_t stream);
 
+// The same with the first stage's keys in a library-held device array
+// (no workspace argument, nothing allocated).
+hipError_t launch_qmv_argmax_noalloc(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k,
+                                     const float* x, const float* norm_w, float norm_eps, float softcap,
+                                     float* y, int32_t* index, float* value, hipStream_t stream);
+
 hipError_t launch_qmv_q8(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k,
                          const int8_t* xq, const uint16_t* xd, float* y, int32_t* blockdots,
                          hipStream_t stream);

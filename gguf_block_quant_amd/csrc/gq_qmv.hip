@@ -24,6 +24,7 @@
 // SafeC Gemma 4 DESIGN_NOTES page ("A dedicated GEMV kernel for the M==1
 // decode step") and the Gemma-4-E2B raw-Metal port page ("Why this exists").
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "gq_device.hpp"
@@ -950,6 +951,53 @@ hipError_t launch_qmv_argmax(int type, const void* qs, const uint16_t* d, int64_
     if (e != hipSuccess) return e;
     return launch_kernel(argmax_reduce_kernel, dim3(1), dim3(1024), stream,
                          static_cast<const unsigned long long*>(workspace), grid, index, value);
+}
+
+// ---- the argmax's partials in library-held device memory -----------------
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops): the first stage's per-workgroup keys go to this file-scope array
+// instead of a caller workspace. Its size is the workspace size, which the
+// first stage's grid never exceeds (the grid is capped at it at launch). Each
+// device holds its own copy until the process ends; host code reaches it only
+// through the address hipGetSymbolAddress returns for the current device
+// (the array's name on the host is a stand-in, not a device address). The
+// stages write every key they read, so no part of it needs clearing; calls
+// that overlap on one device share it and race.
+static __device__ __align__(256) unsigned long long scratch[kArgmaxWorkspaceBytes / sizeof(unsigned long long)];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices];     // per device, set once under the mutex
+
+// This device's address of `scratch`, looked up on the first call on the
+// device (with that device current) and kept.
+hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_qmv_argmax_noalloc(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k,
+                                     const float* x, const float* norm_w, float norm_eps, float softcap,
+                                     float* y, int32_t* index, float* value, hipStream_t stream) {
+    static_assert(sizeof(scratch) == kArgmaxWorkspaceBytes, "scratch holds one workspace");
+    void* ws = nullptr;
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return e;
+    return launch_qmv_argmax(type, qs, d, n, k, x, norm_w, norm_eps, softcap, y, ws, index, value, stream);
 }
 
 hipError_t launch_qmv_q8(int type, const void* qs, const uint16_t* d, int64_t n, int64_t k,

@@ -79,7 +79,7 @@
 extern "C" {
 #endif
 
-#define GQ_ABI_VERSION 4
+#define GQ_ABI_VERSION 5
 
 enum {
     GQ_OK = 0,
@@ -213,6 +213,24 @@ int gq_qmv_q4_0_argmax(const uint8_t *qs, const uint16_t *d, int64_t n, int64_t 
                        float softcap, float *logits, void *workspace,
                        size_t workspace_bytes, int32_t *index, float *value,
                        void *stream);
+
+/*
+ * gq_qmv_q8_0_argmax_noalloc -- gq_qmv_q8_0_argmax for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): no workspace argument; the per-workgroup
+ * partials between the two stages live in a library-held device array of
+ * gq_argmax_workspace_bytes() bytes (16 KiB) per device, which the first
+ * stage's grid never exceeds, so every n is accepted. That array is looked
+ * up on the first call on each device and kept until the process ends; the
+ * call allocates nothing. Every call on a device shares that device's array:
+ * calls that overlap on one device (concurrent streams or threads) race and
+ * must be serialised by the caller. Results are bit-identical to
+ * gq_qmv_q8_0_argmax's. Arguments, limits and errors as gq_qmv_q8_0_argmax.
+ */
+int gq_qmv_q8_0_argmax_noalloc(const int8_t *qs, const uint16_t *d, int64_t n, int64_t k,
+                               const float *x, const float *norm_weight, float norm_eps,
+                               float softcap, float *logits, int32_t *index, float *value,
+                               void *stream);
 
 /*
  * gq_qmv_q8_0_q8 / gq_qmv_q4_0_q8 -- decode matvec against one Q8_0

@@ -40,7 +40,7 @@ def test_header_symbols_all_exported():
 
 
 def test_version_and_status_strings():
-    assert gq.abi_version() == 4
+    assert gq.abi_version() == 5
     for s in range(8):
         assert gq.status_str(s)
     assert gq.status_str(99) == "unknown status"
@@ -175,6 +175,23 @@ def test_argmax_validation(fn):
     assert f(A, B, 64, 256, C, None, 0.0, 30.0, D, W + 4, ws, I, V, None) == ALIGN
     assert f(A, B, 64, 256, C, None, 0.0, 30.0, D, D + 64, ws, I, V, None) == ALIAS   # workspace over logits
     assert f(A, B, 64, 256, C, None, 0.0, 30.0, D, W, ws, W + 16, V, None) == ALIAS   # index inside workspace
+
+
+def test_argmax_noalloc_validation():
+    """The allocation-free vocabulary head validates like the workspace one
+    (no workspace argument to check)."""
+    f = L.gq_qmv_q8_0_argmax_noalloc
+    I, V = 0x71000000, 0x72000000
+    # (qs, d, n, k, x, norm_w, eps, softcap, logits, index, value, stream)
+    assert f(A, B, 64, 256, C, None, 0.0, 30.0, None, I, V, None) == NULL
+    assert f(A, B, 64, 256, C, None, 0.0, 30.0, D, None, V, None) == NULL
+    assert f(A, B, 64, 250, C, None, 0.0, 30.0, D, I, V, None) == SHAPE
+    assert f(A, B, 64, 65536, C, None, 0.0, 30.0, D, I, V, None) == UNSUP
+    assert f(A, B, 64, 256, C, None, 0.0, -1.0, D, I, V, None) == VALUE
+    assert f(A, B, 64, 256, C + 4, None, 0.0, 30.0, D, I, V, None) == ALIGN
+    assert f(A, B, 64, 256, C, None, 0.0, 30.0, D, I + 2, V, None) == ALIGN
+    assert f(A, B, 64, 256, C, None, 0.0, 30.0, D, D + 16, V, None) == ALIAS     # index over logits
+    assert f(A, B, 64, 256, C, None, 0.0, 30.0, C, I, V, None) == ALIAS          # logits over x
 
 
 def test_ffn_ex_validation():
