@@ -21,6 +21,8 @@ CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast
 
 TYPE_Q4_0 = 2
 TYPE_Q8_0 = 8
+TYPE_Q4_K = 12
+TYPE_Q6_K = 14
 
 
 def build(force: bool = True) -> str:
@@ -49,6 +51,8 @@ def lib():
         L.or_f32_to_fp16_rne.restype = ctypes.c_uint16
         L.or_block_bytes.argtypes = [ctypes.c_int]
         L.or_block_bytes.restype = ctypes.c_size_t
+        L.or_block_elems.argtypes = [ctypes.c_int]
+        L.or_block_elems.restype = I64
         L.or_dequantize.argtypes = [ctypes.c_int, P, I64, I64, P]
         L.or_matvec.argtypes = [ctypes.c_int, P, I64, I64, P, P, P]
         L.or_matvec_rows.argtypes = [ctypes.c_int, P, I64, I64, P, I64, P, P, P]
@@ -95,6 +99,10 @@ def fp16_to_f64_array(bits) -> np.ndarray:
 
 def f32_to_fp16(x: float) -> int:
     return int(lib().or_f32_to_fp16_rne(float(np.float32(x))))
+
+
+def block_elems(qtype) -> int:
+    return int(lib().or_block_elems(qtype))
 
 
 def dequantize(qtype, blocks, n, k) -> np.ndarray:

@@ -32,6 +32,29 @@
  *    fp32 then round-to-nearest-even to binary16; q = clamp(round-half-away(
  *    x / d), -127, 127) with the division in fp32 by the fp16-rounded scale;
  *    q = 0 when that scale is zero.  Inputs are assumed finite.
+ *  - K-quant super-blocks (the jouleclaw-loader-gguf BENCHMARKS page gives
+ *    only the arithmetic: "Q4_K matmul", 32-element sub-blocks with a scale
+ *    and a minimum, w = d_sub * q - m_sub; "Q5_K + Q6_K matmul", Q6_K with
+ *    two high bits per element and a signed -32 offset). The byte layout is
+ *    the GGUF one, which the pages do not print: 256 elements per
+ *    super-block.
+ *      Q4_K, 144 bytes: binary16 d, binary16 dmin, 12 bytes holding eight
+ *      6-bit sub-block scales sc_j and eight 6-bit minimums m_j, then 128
+ *      bytes of 4-bit quants. For j < 4, sc_j and m_j are the low six bits of
+ *      bytes j and j+4 of the 12; for j >= 4 their low four bits come from
+ *      byte j+4 (low nibble for sc_j, high nibble for m_j) and their top two
+ *      bits from the top two bits of byte j-4 (sc_j) and byte j (m_j). Quant
+ *      byte 32g + l (g < 4, l < 32) holds element 64g + l in its low nibble
+ *      and element 64g + 32 + l in its high nibble. Element e belongs to
+ *      sub-block e / 32 and is d sc_j q_e - dmin m_j.
+ *      Q6_K, 210 bytes: 128 bytes ql (low four bits), 64 bytes qh (high two
+ *      bits), 16 int8 scales, binary16 d. In half h (elements 128h ..
+ *      128h + 127; ql bytes 64h.., qh bytes 32h..), for l < 32: ql byte l
+ *      gives the low bits of elements l (low nibble) and l + 64 (high
+ *      nibble), ql byte l + 32 those of elements l + 32 and l + 96, and qh
+ *      byte l the high bits of elements l, l + 32, l + 64, l + 96 in its bit
+ *      pairs 0-1, 2-3, 4-5, 6-7 (element numbers relative to the half).
+ *      Element e uses scale e / 16 and is d sc (q_e - 32).
  */
 #include <math.h>
 #include <stdint.h>
@@ -44,8 +67,11 @@
 #endif
 
 #define OR_QK 32
+#define OR_QK_K 256
 #define OR_TYPE_Q4_0 2
 #define OR_TYPE_Q8_0 8
+#define OR_TYPE_Q4_K 12
+#define OR_TYPE_Q6_K 14
 
 /* ------------------------------------------------------------------------ */
 /* IEEE-754 binary16 <-> wider types, written out bit by bit.                */
@@ -105,7 +131,69 @@ size_t or_block_bytes(int type)
 {
     if (type == OR_TYPE_Q8_0) return 34;
     if (type == OR_TYPE_Q4_0) return 18;
+    if (type == OR_TYPE_Q4_K) return 144;
+    if (type == OR_TYPE_Q6_K) return 210;
     return 0;
+}
+
+/* Elements per block: 32, or 256 for the K-quant super-blocks. */
+int64_t or_block_elems(int type)
+{
+    return (type == OR_TYPE_Q4_K || type == OR_TYPE_Q6_K) ? OR_QK_K : OR_QK;
+}
+
+static int is_kquant(int type)
+{
+    return type == OR_TYPE_Q4_K || type == OR_TYPE_Q6_K;
+}
+
+/* The 6-bit scale and minimum of Q4_K sub-block j from the 12 packed bytes. */
+static void q4_k_scale_min(const uint8_t *s12, int j, int *sc, int *m)
+{
+    if (j < 4) {
+        *sc = s12[j] & 63;
+        *m = s12[j + 4] & 63;
+    } else {
+        *sc = (s12[j + 4] & 15) | ((s12[j - 4] >> 6) << 4);
+        *m = (s12[j + 4] >> 4) | ((s12[j] >> 6) << 4);
+    }
+}
+
+/* The 256 dequantised values of one K-quant super-block, in fp64. */
+static void kblock_values(int type, const uint8_t *blk, double w[OR_QK_K])
+{
+    if (type == OR_TYPE_Q4_K) {
+        double d = or_fp16_to_f64((uint16_t)(blk[0] | (blk[1] << 8)));
+        double dmin = or_fp16_to_f64((uint16_t)(blk[2] | (blk[3] << 8)));
+        const uint8_t *s12 = blk + 4, *qs = blk + 16;
+        int q[OR_QK_K];
+        for (int g = 0; g < 4; ++g)
+            for (int l = 0; l < 32; ++l) {
+                q[64 * g + l] = qs[32 * g + l] & 15;
+                q[64 * g + 32 + l] = qs[32 * g + l] >> 4;
+            }
+        for (int e = 0; e < OR_QK_K; ++e) {
+            int sc, m;
+            q4_k_scale_min(s12, e / 32, &sc, &m);
+            w[e] = d * (double)sc * (double)q[e] - dmin * (double)m;
+        }
+    } else {
+        const uint8_t *ql = blk, *qh = blk + 128;
+        const int8_t *sc = (const int8_t *)(blk + 192);
+        double d = or_fp16_to_f64((uint16_t)(blk[208] | (blk[209] << 8)));
+        int q[OR_QK_K];
+        for (int h = 0; h < 2; ++h)
+            for (int l = 0; l < 32; ++l) {
+                const uint8_t *L = ql + 64 * h, *H = qh + 32 * h;
+                int *Q = q + 128 * h;
+                Q[l] = (L[l] & 15) | (((H[l] >> 0) & 3) << 4);
+                Q[l + 32] = (L[l + 32] & 15) | (((H[l] >> 2) & 3) << 4);
+                Q[l + 64] = (L[l] >> 4) | (((H[l] >> 4) & 3) << 4);
+                Q[l + 96] = (L[l + 32] >> 4) | (((H[l] >> 6) & 3) << 4);
+            }
+        for (int e = 0; e < OR_QK_K; ++e)
+            w[e] = d * (double)sc[e / 16] * (double)(q[e] - 32);
+    }
 }
 
 /* Integer quant values of one block: Q8_0 q_i, Q4_0 (nibble_i - 8). */
@@ -132,7 +220,14 @@ static double block_scale(const uint8_t *blk)
 int or_dequantize(int type, const uint8_t *blocks, int64_t n, int64_t k, double *w)
 {
     size_t bb = or_block_bytes(type);
-    if (!bb || k <= 0 || k % OR_QK || n < 0) return 1;
+    if (!bb || k <= 0 || k % or_block_elems(type) || n < 0) return 1;
+    if (is_kquant(type)) {
+        int64_t nsb = k / OR_QK_K;
+        for (int64_t r = 0; r < n; ++r)
+            for (int64_t b = 0; b < nsb; ++b)
+                kblock_values(type, blocks + (size_t)(r * nsb + b) * bb, w + r * k + b * OR_QK_K);
+        return 0;
+    }
     int64_t nb = k / OR_QK;
     int q[OR_QK];
     for (int64_t r = 0; r < n; ++r)
@@ -154,7 +249,25 @@ int or_matvec(int type, const uint8_t *blocks, int64_t n, int64_t k,
               const double *x, double *y, double *a)
 {
     size_t bb = or_block_bytes(type);
-    if (!bb || k <= 0 || k % OR_QK || n < 0) return 1;
+    if (!bb || k <= 0 || k % or_block_elems(type) || n < 0) return 1;
+    if (is_kquant(type)) {
+        int64_t nsb = k / OR_QK_K;
+        double w[OR_QK_K];
+        for (int64_t r = 0; r < n; ++r) {
+            double sum = 0.0, asum = 0.0;
+            for (int64_t b = 0; b < nsb; ++b) {
+                kblock_values(type, blocks + (size_t)(r * nsb + b) * bb, w);
+                for (int i = 0; i < OR_QK_K; ++i) {
+                    double p = w[i] * x[b * OR_QK_K + i];
+                    sum += p;
+                    asum += fabs(p);
+                }
+            }
+            y[r] = sum;
+            if (a) a[r] = asum;
+        }
+        return 0;
+    }
     int64_t nb = k / OR_QK;
     int q[OR_QK];
     for (int64_t r = 0; r < n; ++r) {
@@ -223,7 +336,7 @@ int or_blockdots(int type, const uint8_t *blocks, int64_t n, int64_t k,
                  int32_t *S, double *y, double *a)
 {
     size_t bb = or_block_bytes(type);
-    if (!bb || k <= 0 || k % OR_QK || n < 0 || m < 0) return 1;
+    if (!bb || is_kquant(type) || k <= 0 || k % OR_QK || n < 0 || m < 0) return 1;
     int64_t nb = k / OR_QK;
     int q[OR_QK];
     int rc = 0;
@@ -285,8 +398,8 @@ int or_matvec_rows(int type, const uint8_t *blocks, int64_t n, int64_t k,
                    double *y, double *a)
 {
     size_t bb = or_block_bytes(type);
-    if (!bb || k <= 0 || k % OR_QK) return 1;
-    int64_t nb = k / OR_QK;
+    if (!bb || k <= 0 || k % or_block_elems(type)) return 1;
+    int64_t nb = k / or_block_elems(type);
     for (int64_t i = 0; i < nrows; ++i) {
         if (rows[i] < 0 || rows[i] >= n) return 1;
         const uint8_t *row = blocks + (size_t)(rows[i] * nb) * bb;

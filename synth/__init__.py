@@ -29,7 +29,19 @@ Q8_0_BLOCK = np.dtype([("d", "<u2"), ("qs", "i1", (32,))])
 Q4_0_BLOCK = np.dtype([("d", "<u2"), ("qs", "u1", (16,))])
 assert Q8_0_BLOCK.itemsize == 34 and Q4_0_BLOCK.itemsize == 18
 
-BLOCK_DTYPE = {TYPE_Q8_0: Q8_0_BLOCK, TYPE_Q4_0: Q4_0_BLOCK}
+# K-quant super-blocks of 256 elements (GGUF layout; the pages give only the
+# arithmetic, see the oracle's header): Q4_K = binary16 d, binary16 dmin,
+# 12 bytes of packed 6-bit sub-block scales and minimums, 128 quant bytes;
+# Q6_K = 128 bytes of low quant bits, 64 bytes of high bits, 16 int8 scales,
+# binary16 d.
+QK_K = 256
+TYPE_Q4_K = 12
+TYPE_Q6_K = 14
+Q4_K_BLOCK = np.dtype([("d", "<u2"), ("dmin", "<u2"), ("scales", "u1", (12,)), ("qs", "u1", (128,))])
+Q6_K_BLOCK = np.dtype([("ql", "u1", (128,)), ("qh", "u1", (64,)), ("scales", "i1", (16,)), ("d", "<u2")])
+assert Q4_K_BLOCK.itemsize == 144 and Q6_K_BLOCK.itemsize == 210
+
+BLOCK_DTYPE = {TYPE_Q8_0: Q8_0_BLOCK, TYPE_Q4_0: Q4_0_BLOCK, TYPE_Q4_K: Q4_K_BLOCK, TYPE_Q6_K: Q6_K_BLOCK}
 
 
 def block_dtype(qtype: int) -> np.dtype:
@@ -82,11 +94,44 @@ def q4_0_weights(rng, n: int, k: int, scale_lo=1e-3, scale_hi=1e-2) -> np.ndarra
     return blocks
 
 
+def q4_k_weights(rng, n: int, k: int, scale_lo=1e-4, scale_hi=3e-4) -> np.ndarray:
+    """(n, k/256) Q4_K super-blocks: uniform quant bytes (both nibbles uniform
+    on 0..15), uniform bytes for the 12 packed scale/min bytes (every 6-bit
+    field uniform on 0..63), then binary16 d and dmin uniform in
+    [scale_lo, scale_hi] (so d sc and dmin m stay below about 0.02)."""
+    assert k % QK_K == 0
+    nsb = k // QK_K
+    blocks = np.empty((n, nsb), dtype=Q4_K_BLOCK)
+    blocks["qs"] = rng.integers(0, 256, size=(n, nsb, 128), dtype=np.uint8)
+    blocks["scales"] = rng.integers(0, 256, size=(n, nsb, 12), dtype=np.uint8)
+    blocks["d"] = fp16_scales(rng, (n, nsb), scale_lo, scale_hi)
+    blocks["dmin"] = fp16_scales(rng, (n, nsb), scale_lo, scale_hi)
+    return blocks
+
+
+def q6_k_weights(rng, n: int, k: int, scale_lo=1e-5, scale_hi=1e-4) -> np.ndarray:
+    """(n, k/256) Q6_K super-blocks: uniform low-bit and high-bit bytes (every
+    6-bit quant uniform on 0..63), int8 scales uniform on [-128, 127], then
+    binary16 d uniform in [scale_lo, scale_hi]."""
+    assert k % QK_K == 0
+    nsb = k // QK_K
+    blocks = np.empty((n, nsb), dtype=Q6_K_BLOCK)
+    blocks["ql"] = rng.integers(0, 256, size=(n, nsb, 128), dtype=np.uint8)
+    blocks["qh"] = rng.integers(0, 256, size=(n, nsb, 64), dtype=np.uint8)
+    blocks["scales"] = rng.integers(-128, 128, size=(n, nsb, 16), dtype=np.int8)
+    blocks["d"] = fp16_scales(rng, (n, nsb), scale_lo, scale_hi)
+    return blocks
+
+
 def weights(rng, qtype: int, n: int, k: int, **kw) -> np.ndarray:
     if qtype == TYPE_Q8_0:
         return q8_0_weights(rng, n, k, **kw)
     if qtype == TYPE_Q4_0:
         return q4_0_weights(rng, n, k, **kw)
+    if qtype == TYPE_Q4_K:
+        return q4_k_weights(rng, n, k, **kw)
+    if qtype == TYPE_Q6_K:
+        return q6_k_weights(rng, n, k, **kw)
     raise ValueError(qtype)
 
 
