@@ -24,6 +24,8 @@ LIB_PATH = os.path.join(_HERE, "libgq.so")
 
 TYPE_Q4_0 = 2
 TYPE_Q8_0 = 8
+TYPE_Q4_K = 12
+TYPE_Q6_K = 14
 
 GQ_OK = 0
 STATUS_NAMES = {0: "GQ_OK", 1: "GQ_ERR_NULL", 2: "GQ_ERR_SHAPE", 3: "GQ_ERR_ALIGN",
@@ -57,6 +59,10 @@ _SIGS = {
     "gq_qmv_q8_0_argmax": ([_P, _P, _I64, _I64, _P, _P, _F, _F, _P, _P, ctypes.c_size_t, _P, _P, _P], _I),
     "gq_qmv_q4_0_argmax": ([_P, _P, _I64, _I64, _P, _P, _F, _F, _P, _P, ctypes.c_size_t, _P, _P, _P], _I),
     "gq_qmv_q8_0_argmax_noalloc": ([_P, _P, _I64, _I64, _P, _P, _F, _F, _P, _P, _P, _P], _I),
+    "gq_kq_packed_bytes": ([_I, _I64, _I64], ctypes.c_size_t),
+    "gq_kq_pack": ([_I, _P, _I64, _I64, _P, _P], _I),
+    "gq_qmv_q4_k": ([_P, _I64, _I64, _P, _P, _P], _I),
+    "gq_qmv_q6_k": ([_P, _I64, _I64, _P, _P, _P], _I),
     "gq_qmm_tile_m": ([_P, _P, _I64, _I64, _I, _P, _P, _P, _P, _P], _I),
     "gq_chain_begin": ([_P], _I),
     "gq_chain_end": ([_P, ctypes.POINTER(_P)], _I),
@@ -379,6 +385,46 @@ def qmv_q8_0_argmax_noalloc(qs, d, n, k, x, norm_weight=None, norm_eps=1e-6, sof
           _ptr(logits, "logits", "f32", n_), _ptr(index, "index", "i32", 1), _ptr(value, "value", "f32", 1),
           _stream(stream))
     return index, value, logits
+
+
+def kq_packed_bytes(qtype: int, n: int, k: int) -> int:
+    return raw().gq_kq_packed_bytes(qtype, n, k)
+
+
+def _kq_dims(n, k):
+    n, k = int(n), int(k)
+    return (n, k) if n >= 1 and k >= 256 and k % 256 == 0 else (0, 0)
+
+
+def kq_pack(qtype, blocks, n, k, packed=None, stream=None):
+    """GGUF Q4_K / Q6_K super-blocks (device uint8) -> one packed uint8 buffer."""
+    torch = _torch()
+    n_, k_ = _kq_dims(n, k)
+    need = kq_packed_bytes(qtype, n_, k_) if n_ else 0
+    if packed is None:
+        packed = _like(blocks, (max(need, 1),), torch.uint8)
+    _call("gq_kq_pack", qtype, _ptr(blocks, "blocks", "bytes", n_ * (k_ // 256) * block_bytes(qtype)), n, k,
+          _ptr(packed, "packed", "bytes", need), _stream(stream))
+    return packed
+
+
+def _qmv_kq(fn, qtype, packed, n, k, x, y, stream):
+    torch = _torch()
+    if y is None:
+        y = _like(x, (n,), torch.float32)
+    n_, k_ = _kq_dims(n, k)
+    need = kq_packed_bytes(qtype, n_, k_) if n_ else 0
+    _call(fn, _ptr(packed, "packed", "bytes", need), n, k, _ptr(x, "x", "f32", k_), _ptr(y, "y", "f32", n_),
+          _stream(stream))
+    return y
+
+
+def qmv_q4_k(packed, n, k, x, y=None, stream=None):
+    return _qmv_kq("gq_qmv_q4_k", TYPE_Q4_K, packed, n, k, x, y, stream)
+
+
+def qmv_q6_k(packed, n, k, x, y=None, stream=None):
+    return _qmv_kq("gq_qmv_q6_k", TYPE_Q6_K, packed, n, k, x, y, stream)
 
 
 def _ffn_weights(g_qs, g_d, u_qs, u_d, n_ff, k):

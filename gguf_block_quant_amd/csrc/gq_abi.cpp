@@ -43,6 +43,14 @@ bool any_alias(const Range (&outs)[NO], const Range (&ins)[NI]) {
 }
 
 inline bool type_ok(int type) { return type == GQ_TYPE_Q4_0 || type == GQ_TYPE_Q8_0; }
+inline bool kq_type_ok(int type) { return type == GQ_TYPE_Q4_K || type == GQ_TYPE_Q6_K; }
+
+// n x k shape check of the K-quant entry points (whole 256-element super-blocks).
+inline int check_kq_shape(int64_t n, int64_t k) {
+    if (n < 1 || k < 256 || k % 256 != 0) return GQ_ERR_SHAPE;
+    if (n > kMaxRows || k > kMaxK) return GQ_ERR_UNSUPPORTED;
+    return GQ_OK;
+}
 
 // n x k shape check shared by every entry point.
 inline int check_shape(int64_t n, int64_t k) {
@@ -199,6 +207,8 @@ const char* gq_status_str(int status) {
 size_t gq_block_bytes(int type) {
     if (type == GQ_TYPE_Q8_0) return 34;
     if (type == GQ_TYPE_Q4_0) return 18;
+    if (type == GQ_TYPE_Q4_K) return 144;
+    if (type == GQ_TYPE_Q6_K) return 210;
     return 0;
 }
 
@@ -338,6 +348,50 @@ int gq_qffn_gate_up_gelu_ex(const uint8_t* g_qs, const uint16_t* g_d, const uint
                             const uint16_t* u_d, int64_t n_ff, int64_t k, const float* x,
                             const float* norm_weight, float norm_eps, float* h, void* stream) {
     return ffn(g_qs, g_d, u_qs, u_d, n_ff, k, x, norm_weight, norm_eps, h, stream);
+}
+
+size_t gq_kq_packed_bytes(int type, int64_t n, int64_t k) {
+    if (!kq_type_ok(type) || check_kq_shape(n, k) != GQ_OK) return 0;
+    return gq::kq_layout(type, n, k, nullptr);
+}
+
+int gq_kq_pack(int type, const void* blocks, int64_t n, int64_t k, void* packed, void* stream) {
+    if (blocks == nullptr || packed == nullptr) return GQ_ERR_NULL;
+    if (!kq_type_ok(type)) return GQ_ERR_UNSUPPORTED;
+    int st = check_kq_shape(n, k);
+    if (st != GQ_OK) return st;
+    if (!aligned(packed, 16)) return GQ_ERR_ALIGN;
+    const size_t bb = type == GQ_TYPE_Q4_K ? 144 : 210;
+    const Range outs[] = {{packed, gq::kq_layout(type, n, k, nullptr)}};
+    const Range ins[] = {{blocks, static_cast<size_t>(n) * static_cast<size_t>(k / 256) * bb}};
+    if (any_alias(outs, ins)) return GQ_ERR_ALIAS;
+    return status_of(gq::launch_kq_pack(type, static_cast<const uint8_t*>(blocks), n, k,
+                                        static_cast<uint8_t*>(packed), as_stream(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+int qmv_kq(int type, const void* packed, int64_t n, int64_t k, const float* x, float* y, void* stream) {
+    if (packed == nullptr || x == nullptr || y == nullptr) return GQ_ERR_NULL;
+    int st = check_kq_shape(n, k);
+    if (st != GQ_OK) return st;
+    if (!aligned(packed, 16) || !aligned(x, 16) || !aligned(y, 4)) return GQ_ERR_ALIGN;
+    const Range outs[] = {{y, static_cast<size_t>(n) * 4}};
+    const Range ins[] = {{packed, gq::kq_layout(type, n, k, nullptr)}, {x, static_cast<size_t>(k) * 4}};
+    if (any_alias(outs, ins)) return GQ_ERR_ALIAS;
+    return status_of(gq::launch_qmv_kq(type, static_cast<const uint8_t*>(packed), n, k, x, y, as_stream(stream)));
+}
+}  // namespace
+
+extern "C" {
+
+int gq_qmv_q4_k(const void* packed, int64_t n, int64_t k, const float* x, float* y, void* stream) {
+    return qmv_kq(GQ_TYPE_Q4_K, packed, n, k, x, y, stream);
+}
+
+int gq_qmv_q6_k(const void* packed, int64_t n, int64_t k, const float* x, float* y, void* stream) {
+    return qmv_kq(GQ_TYPE_Q6_K, packed, n, k, x, y, stream);
 }
 
 int gq_qmm_tile_m(const uint8_t* qs, const uint16_t* d, int64_t n, int64_t k, int m, const int8_t* xq,

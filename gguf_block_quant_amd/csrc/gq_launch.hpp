@@ -63,6 +63,13 @@ hipError_t launch_ffn_gate_up(const uint8_t* g_qs, const uint16_t* g_d, const ui
                               const uint16_t* u_d, int64_t n_ff, int64_t k, const float* x,
                               const float* norm_w, float norm_eps, float* h, hipStream_t stream);
 
+// K-quant super-blocks (Q4_K = 12, Q6_K = 14; 256 elements, k % 256 == 0)
+size_t kq_layout(int type, int64_t n, int64_t k, size_t* offsets /* [4] or NULL */);
+hipError_t launch_kq_pack(int type, const uint8_t* blocks, int64_t n, int64_t k, uint8_t* packed,
+                          hipStream_t stream);
+hipError_t launch_qmv_kq(int type, const uint8_t* packed, int64_t n, int64_t k, const float* x, float* y,
+                         hipStream_t stream);
+
 hipError_t launch_tile_q4_0(const uint8_t* qs, const uint16_t* d, int64_t n, int64_t k, int m,
                             const int8_t* xq, const uint16_t* xd, float* y, int32_t* blockdots,
                             hipStream_t stream);

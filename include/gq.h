@@ -79,7 +79,7 @@
 extern "C" {
 #endif
 
-#define GQ_ABI_VERSION 5
+#define GQ_ABI_VERSION 6
 
 enum {
     GQ_OK = 0,
@@ -94,7 +94,9 @@ enum {
 
 enum {
     GQ_TYPE_Q4_0 = 2,        /* GGUF type id of Q4_0 */
-    GQ_TYPE_Q8_0 = 8         /* GGUF type id of Q8_0 */
+    GQ_TYPE_Q8_0 = 8,        /* GGUF type id of Q8_0 */
+    GQ_TYPE_Q4_K = 12,       /* GGUF type id of Q4_K (256-element super-blocks) */
+    GQ_TYPE_Q6_K = 14        /* GGUF type id of Q6_K (256-element super-blocks) */
 };
 
 /* Version of this header's signatures; bumped on any change, so that a
@@ -115,7 +117,8 @@ const char *gq_status_str(int status);
  * not change it. */
 int gq_last_hip_error(void);
 
-/* Bytes of one GGUF block of `type` (34 or 18), 0 for an unknown type. */
+/* Bytes of one GGUF block of `type` (34, 18; 144 or 210 for the 256-element
+ * K-quant super-blocks), 0 for an unknown type. */
 size_t gq_block_bytes(int type);
 
 /* Sizes of the packed arrays for an n x k matrix: qs is n*k (Q8_0) or
@@ -306,6 +309,48 @@ int gq_qffn_gate_up_gelu_ex(const uint8_t *g_qs, const uint16_t *g_d,
 int gq_qmm_tile_m(const uint8_t *qs, const uint16_t *d, int64_t n, int64_t k, int m,
                   const int8_t *xq, const uint16_t *xd, float *y,
                   int32_t *blockdots, void *stream);
+
+/*
+ * K-quant super-blocks: Q4_K and Q6_K, 256 elements each (distributed Gemma 4
+ * GGUF files are mostly Q4_K_M / UD-Q4_K_XL: TensorSharp Gemma 4 page, model
+ * table). The arithmetic is the jouleclaw-loader-gguf BENCHMARKS page's
+ * ("Q4_K matmul": 32-element sub-blocks with a 6-bit scale and a 6-bit
+ * minimum, w = d sc q - dmin m, summed as d sc sum(x q) - dmin m sum(x);
+ * "Q5_K + Q6_K matmul": Q6_K has four low bits, two high bits and a signed
+ * -32 offset, w = d sc (q - 32) with one int8 scale per 16 elements). The
+ * GGUF byte layout the pages do not print:
+ *  - Q4_K, 144 B: binary16 d, binary16 dmin, 12 bytes of scales/minimums
+ *    (for sub-block j < 4: the low six bits of bytes j and j+4; for j >= 4:
+ *    the low and high nibble of byte j+4 and the top two bits of bytes j-4
+ *    and j), 128 quant bytes (byte 32g + l: element 64g + l in the low
+ *    nibble, element 64g + 32 + l in the high one);
+ *  - Q6_K, 210 B: ql[128], qh[64], int8 scales[16], binary16 d; in half h
+ *    and for l < 32, ql byte 64h + l holds the low bits of elements
+ *    128h + l (low nibble) and 128h + l + 64 (high), ql byte 64h + l + 32
+ *    those of 128h + l + 32 and 128h + l + 96, and qh byte 32h + l their
+ *    high bits in bit pairs 0-1, 2-3, 4-5 and 6-7; element e uses scale e/16.
+ * A matrix of n rows and k columns (k % 256 == 0) is n * k/256 super-blocks,
+ * row-major.
+ *
+ * gq_kq_pack splits the GGUF super-blocks (device memory, contiguous, any
+ * alignment) into ONE packed device buffer of gq_kq_packed_bytes(type, n, k)
+ * bytes, 16-byte aligned, holding byte-for-byte copies in 256-byte aligned
+ * sections (the load-time kernel-layout pack of gq_pack):
+ *  - Q4_K: quants [n][k/2], then headers [n][k/256][16] (d, dmin, the 12
+ *    scale bytes);
+ *  - Q6_K: ql [n][k/2], qh [n][k/4], scales [n][k/16], d [n][k/256].
+ * gq_kq_packed_bytes returns 0 for an unknown type or invalid shape.
+ *
+ * gq_qmv_q4_k / gq_qmv_q6_k -- decode matvec on a packed K-quant matrix
+ * with fp32 activations: y[r] = sum_c w[r][c] x[c] accumulated in fp32,
+ * |y - y_exact| <= 1e-4 * sum_c |w x| + 1e-6. x fp32 [k] (16-byte aligned),
+ * y fp32 [n]. k must be a multiple of 256 (else GQ_ERR_SHAPE), at most
+ * 32768 (else GQ_ERR_UNSUPPORTED). Special values as for the other matvecs.
+ */
+size_t gq_kq_packed_bytes(int type, int64_t n, int64_t k);
+int gq_kq_pack(int type, const void *blocks, int64_t n, int64_t k, void *packed, void *stream);
+int gq_qmv_q4_k(const void *packed, int64_t n, int64_t k, const float *x, float *y, void *stream);
+int gq_qmv_q6_k(const void *packed, int64_t n, int64_t k, const float *x, float *y, void *stream);
 
 /*
  * Decode-step chaining. A decode step is a fixed sequence of many small

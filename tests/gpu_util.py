@@ -44,3 +44,25 @@ def check_within(y, y_ref, bound, what):
     assert bad.size == 0, "%s: %d of %d outside tolerance; first %s: got %r ref %r bound %r" % (
         what, bad.size, y.size, bad[:3], y.reshape(-1)[bad[:3]], np.asarray(y_ref).reshape(-1)[bad[:3]],
         np.asarray(bound).reshape(-1)[bad[:3]])
+
+
+def packed_kq(gq, qtype, blocks, n, k):
+    """Upload canonical GGUF K-quant super-blocks and pack them on the device."""
+    raw = up(synth.as_bytes(blocks).reshape(-1))
+    return gq.kq_pack(qtype, raw, n, k)
+
+
+def check_special(y, yr, ar, what):
+    """Finite oracle values: within the fp32-path bound. Non-finite ones (a
+    non-finite scale in the row): the GPU value is non-finite too, and where
+    both are infinite they have the same sign."""
+    import oracle
+    y = np.asarray(y, dtype=np.float64).reshape(-1)
+    yr = np.asarray(yr, dtype=np.float64).reshape(-1)
+    ar = np.asarray(ar, dtype=np.float64).reshape(-1)
+    fin_r, fin_g = np.isfinite(yr), np.isfinite(y)
+    bad = np.nonzero(fin_r != fin_g)[0]
+    assert bad.size == 0, "%s: finiteness differs at %s: got %r ref %r" % (what, bad[:5], y[bad[:5]], yr[bad[:5]])
+    inf = np.isinf(y) & np.isinf(yr)
+    assert np.array_equal(np.sign(y[inf]), np.sign(yr[inf])), what + ": sign of Inf"
+    check_within(y[fin_r], yr[fin_r], oracle.fp32_path_bound(ar[fin_r]), what)

@@ -40,7 +40,7 @@ def test_header_symbols_all_exported():
 
 
 def test_version_and_status_strings():
-    assert gq.abi_version() == 5
+    assert gq.abi_version() == 6
     for s in range(8):
         assert gq.status_str(s)
     assert gq.status_str(99) == "unknown status"
@@ -192,6 +192,31 @@ def test_argmax_noalloc_validation():
     assert f(A, B, 64, 256, C, None, 0.0, 30.0, D, I + 2, V, None) == ALIGN
     assert f(A, B, 64, 256, C, None, 0.0, 30.0, D, D + 16, V, None) == ALIAS     # index over logits
     assert f(A, B, 64, 256, C, None, 0.0, 30.0, C, I, V, None) == ALIAS          # logits over x
+
+
+def test_kquant_validation():
+    """K-quant entry points: whole 256-element super-blocks, k <= 32768."""
+    Q4K, Q6K = 12, 14
+    assert gq.block_bytes(Q4K) == 144 and gq.block_bytes(Q6K) == 210
+    assert gq.kq_packed_bytes(Q4K, 4, 256) == 512 + 4 * 16          # quants, then 16-byte headers
+    assert gq.kq_packed_bytes(Q6K, 4, 256) == 512 + 256 + 256 + 8   # ql, qh, scales (padded to 256), d
+    assert gq.kq_packed_bytes(Q4K, 4, 288) == 0 and gq.kq_packed_bytes(Q4_0 := 2, 4, 256) == 0
+    for fn in (L.gq_qmv_q4_k, L.gq_qmv_q6_k):
+        assert fn(None, 4, 256, C, D, None) == NULL
+        assert fn(A, 4, 256, None, D, None) == NULL
+        assert fn(A, 4, 288, C, D, None) == SHAPE
+        assert fn(A, 0, 256, C, D, None) == SHAPE
+        assert fn(A, 4, 128, C, D, None) == SHAPE
+        assert fn(A, 4, 65536, C, D, None) == UNSUP
+        assert fn(A + 8, 4, 256, C, D, None) == ALIGN
+        assert fn(A, 4, 256, C + 4, D, None) == ALIGN
+        assert fn(A, 4, 256, C, A + 64, None) == ALIAS                       # y inside the packed weights
+    f = L.gq_kq_pack
+    assert f(Q4K, None, 4, 256, A, None) == NULL
+    assert f(2, B, 4, 256, A, None) == UNSUP
+    assert f(Q6K, B, 4, 300, A, None) == SHAPE
+    assert f(Q6K, B, 4, 256, A + 8, None) == ALIGN
+    assert f(Q6K, B, 4, 256, B + 16, None) == ALIAS
 
 
 def test_ffn_ex_validation():

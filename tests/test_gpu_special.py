@@ -18,7 +18,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import check_within, down, packed, up
+from gpu_util import check_special, check_within, down, packed, up
 
 pytestmark = pytest.mark.gpu
 
@@ -52,18 +52,6 @@ def plant_rows(rng, w, patterns, rows):
     for r in rows:
         w["d"][r, rng.integers(0, nb)] = patterns[r % len(patterns)]
     return w
-
-
-def check_special(y, yr, ar, what):
-    y = np.asarray(y, dtype=np.float64).reshape(-1)
-    yr = np.asarray(yr, dtype=np.float64).reshape(-1)
-    ar = np.asarray(ar, dtype=np.float64).reshape(-1)
-    fin_r, fin_g = np.isfinite(yr), np.isfinite(y)
-    bad = np.nonzero(fin_r != fin_g)[0]
-    assert bad.size == 0, "%s: finiteness differs at %s: got %r ref %r" % (what, bad[:5], y[bad[:5]], yr[bad[:5]])
-    inf = np.isinf(y) & np.isinf(yr)
-    assert np.array_equal(np.sign(y[inf]), np.sign(yr[inf])), what + ": sign of Inf"
-    check_within(y[fin_r], yr[fin_r], oracle.fp32_path_bound(ar[fin_r]), what)
 
 
 def special_weights(qtype, n, k, seed, nonfinite_rows=True):
