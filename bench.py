@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark: effective weight GB/s of the block-quantised decode hot path.
 
-One *step* is one pass of the whole hot path over one batch of synthetic
+One *step* is one pass of the M = 1 hot path over one batch of synthetic
 inputs, shaped like one decode step that streams many different weights
-(the pages define effective bandwidth as bytes per token x tokens/s):
+(the pages define effective bandwidth as bytes per token x tokens/s; the
+metric is the M = 1 matvec's):
 
   1. qmv_q4_0           Q4_0 2048 x 2048, fp32 x
   2. qmv_q4_0_q8x       Q4_0 2048 x 2048, the same x quantised to Q8_0 in the
@@ -12,7 +13,11 @@ inputs, shaped like one decode step that streams many different weights
   3. qffn_gate_up_gelu  Q4_0 gate and up 8192 x 2048 -> h = G(gate x) * up x
   4. qmv_q4_0           Q4_0 down 2048 x 8192 against h
   5. qmv_q8_0           Q8_0 vocab 262144 x 2048 (0.57 GB of blocks), fp32 x
-  6. qmm_tile_m         Q4_0 8192 x 2048 against M = 8, 16, 32 Q8_0 rows
+
+The prefill tile (qmm_tile_m, Q4_0 8192 x 2048 against M = 8, 16, 32 Q8_0
+rows) is the path's other form; it is timed the same way in a loop of its
+own right after the steps and reported as ``prefill_tiles`` (its bytes are
+not M = 1 bytes, so they stay out of ``value``).
 
 Every weight matrix is a distinct allocation, and ``--sets`` full copies of
 the step's weights are rotated so nothing is served from the 256 MB
@@ -26,6 +31,7 @@ blocks + x + y) / its average duration from HIP events recorded around each
 of its launches on the launch stream inside the timed region.
 
 Also reported beside ``value`` (none of them replaces it):
+  prefill_tiles        the three tiles per pass, timed like the steps
   chained              the same step recorded once per weight set with
                        gq_chain_* and replayed (one submission per step)
   read_stream_ceiling  best bandwidth of a plain 16-byte read-and-XOR kernel
@@ -39,7 +45,8 @@ Also reported beside ``value`` (none of them replaces it):
                        host's issue time per launch, and 64-launch graph
                        figures over distinct copies and over one copy
                        (MALL-hot); the 64x256 Q8_0 config is a launch-latency
-                       point, not a roofline point
+                       point, not a roofline point; Q4_K / Q6_K matvecs at
+                       the 2048 x 2048, 8192 x 2048 and 262144 x 2048 shapes
 
 Modes:
   python bench.py [--steps K --warmup W]    the benchmark (one JSON line)
@@ -211,6 +218,7 @@ class Step:
             self.keep.append((w2a, w2b, wg, wu, wd, wv, wt))
             self.vocab_qs = getattr(self, "vocab_qs", []) + [wv[0]]
             self.vocab_sets = getattr(self, "vocab_sets", []) + [wv]
+            self.tile_weights = getattr(self, "tile_weights", []) + [wt]
             launches = [
                 ("qmv_q4_0 2048x2048", L.gq_qmv_q4_0, (P(w2a[0]), P(w2a[1]), 2048, 2048, P(x2), P(y2a), sp),
                  2048 * 64 * 18, 8192 + 8192),
@@ -225,11 +233,13 @@ class Step:
                 (DOMINANT, L.gq_qmv_q8_0, (P(wv[0]), P(wv[1]), 262144, 2048, P(x4), P(y4), sp),
                  262144 * 64 * 34, 8192 + 262144 * 4),
             ]
+            tiles = []
             for m in (8, 16, 32):
-                launches.append(("qmm_tile_m 8192x2048 M=%d" % m, L.gq_qmm_tile_m,
-                                 (P(wt[m][0]), P(wt[m][1]), 8192, 2048, m, P(acts[m][0]), P(acts[m][1]),
-                                  P(yt[m]), None, sp), 8192 * 64 * 18, m * 2176 + m * 8192 * 4))
+                tiles.append(("qmm_tile_m 8192x2048 M=%d" % m, L.gq_qmm_tile_m,
+                              (P(wt[m][0]), P(wt[m][1]), 8192, 2048, m, P(acts[m][0]), P(acts[m][1]),
+                               P(yt[m]), None, sp), 8192 * 64 * 18, m * 2176 + m * 8192 * 4))
             self.sets.append(launches)
+            self.tile_sets = getattr(self, "tile_sets", []) + [tiles]
             if s == 0:
                 # entry points beyond the step (the folds around a projection,
                 # the vocabulary head, a batched-decode tile), timed on their own
@@ -266,9 +276,11 @@ class Step:
         torch.cuda.synchronize()
         log("packed %d weight set(s) in %.1fs" % (sets, time.time() - t0))
         self.names = [l[0] for l in self.sets[0]]
-        self.weight_bytes = {l[0]: l[3] for l in self.sets[0]}
-        self.other_bytes = {l[0]: l[4] for l in self.sets[0]}
-        self.step_weight_bytes = sum(self.weight_bytes.values())
+        self.tile_names = [l[0] for l in self.tile_sets[0]]
+        self.weight_bytes = {l[0]: l[3] for l in self.sets[0] + self.tile_sets[0]}
+        self.other_bytes = {l[0]: l[4] for l in self.sets[0] + self.tile_sets[0]}
+        self.step_weight_bytes = sum(self.weight_bytes[n] for n in self.names)
+        self.tile_weight_bytes = sum(self.weight_bytes[n] for n in self.tile_names)
 
     def record_chains(self):
         """One recorded chain per weight set: the whole step as one graph."""
@@ -282,10 +294,12 @@ class Step:
     def replay(self, i):
         self.chains[i % len(self.chains)].launch(self.stream)
 
-    def run(self, i, events=None):
-        """Enqueue step i; events maps a launch name to a list collecting
-        (start, end) event pairs recorded around that launch."""
-        for name, fn, args, _, _ in self.sets[i % len(self.sets)]:
+    def run(self, i, events=None, tiles=False):
+        """Enqueue step i (or, with tiles, pass i of the prefill tiles);
+        events maps a launch name to a list collecting (start, end) event
+        pairs recorded around that launch."""
+        sets = self.tile_sets if tiles else self.sets
+        for name, fn, args, _, _ in sets[i % len(sets)]:
             if events is not None and name in events:
                 a = TimingEvent()
                 b = TimingEvent()
@@ -398,7 +412,28 @@ def per_config(step, ceiling_gbps, log, rotate_bytes=2 << 30):
         rows.append(("C5 qmm_tile_m 8192x2048 M=%d" % m, 9437184, m * 2176 + m * 8192 * 4,
                      [(L.gq_qmm_tile_m, (P(q), P(d), 8192, 2048, m, P(acts[m][0]), P(acts[m][1]), P(yt[m]), None,
                                          sp)) for q, d in w5]))
-    keep = [w1, w2, wg, wu, wd, wds, w5, x1, y1, x2, y2, xq2, xd2, x3, h3, y3, x4, y4, y4s, h3s, y3s, acts, yt]
+    # K-quant matvecs (fp32 x, k = 2048): the decode shapes, and a
+    # vocabulary-sized matrix that streams from HBM at the steady rate
+    def kq_copies(qtype, blocks, n, k, count):
+        raw = up(synth.as_bytes(blocks).reshape(-1))
+        out = [gq.kq_pack(qtype, raw, n, k) for _ in range(count)]
+        torch.cuda.synchronize()
+        return out
+
+    xk = up(synth.activations(np.random.default_rng(5), 2048))
+    kq_keep = [xk]
+    for qtype, tname, fn, sb_bytes in ((gq.TYPE_Q4_K, "Q4_K", L.gq_qmv_q4_k, 144),
+                                      (gq.TYPE_Q6_K, "Q6_K", L.gq_qmv_q6_k, 210)):
+        for n in (2048, 8192, 262144):
+            wbytes = n * 8 * sb_bytes
+            kc = kq_copies(qtype, synth.weights(np.random.default_rng(n + qtype), qtype, n, 2048), n, 2048,
+                           ncopies(wbytes))
+            yk = torch.empty(n, dtype=torch.float32, device=dev)
+            kq_keep += [kc, yk]
+            rows.append(("K qmv_%s %dx2048" % (tname.lower(), n), wbytes, 8192 + 4 * n,
+                         [(fn, (P(pk), n, 2048, P(xk), P(yk), sp)) for pk in kc]))
+    keep = [w1, w2, wg, wu, wd, wds, w5, x1, y1, x2, y2, xq2, xd2, x3, h3, y3, x4, y4, y4s, h3s, y3s, acts, yt,
+            kq_keep]
 
     def issue(launch):
         for fn, fargs in (launch if isinstance(launch[0], tuple) else (launch,)):
@@ -540,7 +575,7 @@ def cpu_baseline(host, weight_bytes_per_step, seconds, log):
 
     import oracle
 
-    c2, c3, c4, c5 = host["c2"], host["c3"], host["c4"], host["c5"]
+    c2, c3, c4 = host["c2"], host["c3"], host["c4"]
     Q4, Q8 = oracle.TYPE_Q4_0, oracle.TYPE_Q8_0
 
     def one_pass():
@@ -550,8 +585,6 @@ def cpu_baseline(host, weight_bytes_per_step, seconds, log):
         f = oracle.ffn_gate_up(Q4, c3["wg"], c3["wu"], 8192, 2048, c3["x"])
         oracle.matvec(Q4, c3["wd"], 2048, 8192, f["h"])
         oracle.matvec(Q8, c4["w"], 262144, 2048, c4["x"])
-        for m in (8, 16, 32):
-            oracle.blockdots(Q4, c5["w"], 8192, 2048, c5["acts"][m][0], c5["acts"][m][1], want_s=False)
 
     passes = 0
     t0 = time.perf_counter()
@@ -567,7 +600,7 @@ def cpu_baseline(host, weight_bytes_per_step, seconds, log):
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": "%d full pass(es) of the step's workload (every kernel once, same inputs) through the "
+        "sample": "%d full pass(es) of the M=1 step's workload (every kernel once, same inputs) through the "
                   "single-threaded fp64 C oracle, %.1f s; weight-block bytes / time" % (passes, el),
         "seconds_per_step": round(el / passes, 3),
         "cpu": cpu_description(),
@@ -601,7 +634,7 @@ def cpu_baseline_threads(host, weight_bytes_per_step, seconds, log):
 
     import oracle
 
-    c2, c3, c4, c5 = host["c2"], host["c3"], host["c4"], host["c5"]
+    c2, c3, c4 = host["c2"], host["c3"], host["c4"]
     Q4, Q8 = oracle.TYPE_Q4_0, oracle.TYPE_Q8_0
     T = max(1, min(os.cpu_count() or 1, 16))
     pool = ThreadPoolExecutor(T)
@@ -623,9 +656,6 @@ def cpu_baseline_threads(host, weight_bytes_per_step, seconds, log):
         h = np.concatenate(hs)
         rows(lambda w, n, k: oracle.matvec(Q4, w, n, k, h), c3["wd"], 2048, 8192)
         rows(lambda w, n, k: oracle.matvec(Q8, w, n, k, c4["x"]), c4["w"], 262144, 2048)
-        for m in (8, 16, 32):
-            rows(lambda w, n, k: oracle.blockdots(Q4, w, n, k, c5["acts"][m][0], c5["acts"][m][1], want_s=False),
-                 c5["w"], 8192, 2048)
 
     passes = 0
     t0 = time.perf_counter()
@@ -685,11 +715,13 @@ def pmc_step_mode(args, log):
     torch.cuda.synchronize()
     for i in range(3):
         step.run(i)
+        step.run(i, tiles=True)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"step_launches": [[n, w, o] for n, _, _, w, o in step.sets[0]], "steps": 3}), flush=True)
-    log("pmc pass done: 3 steps of %d launches, 3 x copy of %d bytes" % (len(step.names), COPY_BYTES))
+    launches = step.sets[0] + step.tile_sets[0]
+    print(json.dumps({"step_launches": [[n, w, o] for n, _, _, w, o in launches], "steps": 3}), flush=True)
+    log("pmc pass done: 3 steps of %d launches, 3 x copy of %d bytes" % (len(launches), COPY_BYTES))
 
 
 STEP_TRAFFIC_FILE = os.path.join(PROFILES, "decode_step_hbm_traffic.txt")
@@ -1095,6 +1127,7 @@ def main():
     step = Step(args.sets, log)
     for i in range(args.warmup):
         step.run(i)
+        step.run(i, tiles=True)
     torch.cuda.synchronize()
 
     # timed region: exactly K steps, synchronised on both sides
@@ -1108,19 +1141,35 @@ def main():
     ms_per_step = elapsed / args.steps * 1e3
     value = step.step_weight_bytes * args.steps / elapsed / 1e9
 
+    # the prefill tiles, timed the same way in a loop of their own
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step.run(i, tiles=True)
+    torch.cuda.synchronize()
+    tiles_s = (time.perf_counter() - t0) / args.steps
+    prefill_tiles = {
+        "value": round(step.tile_weight_bytes / tiles_s / 1e9, 2), "unit": "GB/s",
+        "ms_per_pass": round(tiles_s * 1e3, 4), "passes_timed": args.steps,
+        "weight_bytes_per_pass": step.tile_weight_bytes,
+        "launches": step.tile_names,
+        "hbm_frac": round(step.tile_weight_bytes / tiles_s / 1e9 / HBM_PEAK_GBPS, 4),
+    }
+
     dom_ms = [a.elapsed_time(b) for a, b in ev[DOMINANT]]
     dom_avg_s = sum(dom_ms) / len(dom_ms) / 1e3
     dom_bytes = step.weight_bytes[DOMINANT] + step.other_bytes[DOMINANT]
     achieved = dom_bytes / dom_avg_s / 1e9
 
     # per-kernel breakdown (separate, untimed pass with events around every launch)
-    bev = {n: [] for n in step.names}
+    bev = {n: [] for n in step.names + step.tile_names}
     nb = min(20, max(4, args.steps // 10))
     for i in range(nb):
         step.run(i, bev)
+        step.run(i, bev, tiles=True)
     torch.cuda.synchronize()
     breakdown = {}
-    for n in step.names:
+    for n in step.names + step.tile_names:
         us = sorted(a.elapsed_time(b) * 1e3 for a, b in bev[n])
         med = us[len(us) // 2]
         wb = step.weight_bytes[n]
@@ -1189,9 +1238,9 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": "decode step over distinct weights: q4_0 2048x2048 (fp32 x; and q8_0 x quantised in "
-                        "the kernel), ffn q4_0 gate+up 8192x2048 + down 2048x8192, q8_0 vocab 262144x2048, "
-                        "prefill tile q4_0 8192x2048 at M=8,16,32",
+            "workload": "M=1 decode step over distinct weights: q4_0 2048x2048 (fp32 x; and q8_0 x quantised in "
+                        "the kernel), ffn q4_0 gate+up 8192x2048 + down 2048x8192, q8_0 vocab 262144x2048 "
+                        "(the prefill tile q4_0 8192x2048 at M=8,16,32 is timed apart: prefill_tiles)",
             "weight_bytes_per_step": step.step_weight_bytes,
             "weight_sets_rotated": args.sets,
             "launches_per_step": len(step.names),
@@ -1210,6 +1259,7 @@ def main():
             "avg_launch_us": round(dom_avg_s * 1e6, 2),
             "launches_timed": len(dom_ms),
         },
+        "prefill_tiles": prefill_tiles,
         "cpu_baseline": cpu,
         "cpu_baseline_threads": cpu_threads,
         "chained": chained,
