@@ -248,7 +248,7 @@ class Step:
                 res2 = up(rng.standard_normal(2048).astype(np.float32))
                 y2c = torch.empty(2048, dtype=torch.float32, device=dev)
                 logits = torch.empty(262144, dtype=torch.float32, device=dev)
-                ws = torch.empty(gq.argmax_workspace_bytes(), dtype=torch.uint8, device=dev)
+                ws = torch.zeros(gq.argmax_workspace_bytes(), dtype=torch.uint8, device=dev)
                 idx = torch.empty(1, dtype=torch.int32, device=dev)
                 val = torch.empty(1, dtype=torch.float32, device=dev)
                 xq4, xd4 = (up(c5["acts"][8][0][:4].copy()), up(c5["acts"][8][1][:4].copy()))

@@ -36,11 +36,18 @@
 #include "gq_device.hpp"
 #include "gq_launch.hpp"
 
+// Measured on MI355X (fp32 x, k = 2048; 262144 / 8192 rows, and 2048 x 8192):
+// 4 rows per step with up to 2048 workgroups: Q4_K 62-64 / 5.3-5.4 / 5.6 us,
+// Q6_K 84-88 / 6.0-6.1 / 5.7-5.8 us; 2 rows at 1024 workgroups: 73 / 5.7 /
+// 5.8 and 92 / 6.6 / 6.9 us. Two row groups in flight per wave (a second
+// register set) measured no better: the loop is bound by its VALU work
+// (about 2.1 instructions per element for the exact nibble dot), not by
+// load latency.
 #ifndef GQ_KQ_R
-#define GQ_KQ_R 2            // rows per wave step
+#define GQ_KQ_R 4            // rows per wave step
 #endif
 #ifndef GQ_KQ_MAX_GRID
-#define GQ_KQ_MAX_GRID 1024  // workgroups of 4 waves at most
+#define GQ_KQ_MAX_GRID 2048  // workgroups of 4 waves at most
 #endif
 
 namespace gq {

@@ -162,3 +162,20 @@ def test_argmax_stays_inside_its_workspace(qtype, n, k):
     assert torch.all(buf[wsb:] == 0xAB).item()
     lg = down(logits)
     assert int(down(idx)[0]) == oracle.argmax_f32(lg)
+
+
+@pytest.mark.parametrize("qtype,n,k", [(Q8, 262144, 2048), (Q4, 5000, 1024), (Q8, 7, 64)])
+def test_argmax_calls_in_a_row_share_one_workspace(qtype, n, k):
+    """One workspace, many calls in a row with new activations: every call's
+    index and value are those of its own logits, never a stale partial."""
+    rng = np.random.default_rng(3 * n + k)
+    w = synth.weights(rng, qtype, n, k)
+    qs, d = packed(gq, qtype, w, n, k)
+    ws = torch.full((gq.argmax_workspace_bytes(),), 0xFF, dtype=torch.uint8, device="cuda")
+    for call in range(6):
+        x = synth.activations(rng, k)
+        idx, val, logits = _argmax(qtype)(qs, d, n, k, up(x), softcap=30.0 if call % 2 else 0.0, workspace=ws)
+        lg = down(logits)
+        i = int(down(idx)[0])
+        assert i == oracle.argmax_f32(lg), call
+        assert down(val).view(np.uint32)[0] == lg.view(np.uint32)[i]
