@@ -79,10 +79,10 @@ DOMINANT = "qmv_q8_0 262144x2048 (vocab)"
 COPY_BYTES = 512 * 1024 * 1024        # calibration copy for the HBM counters
 
 
-def kernel_source_hash() -> str:
-    """Hash of the sources the dominant kernel is built from."""
+def kernel_source_hash(names=("gq_qmv.hip", "gq_device.hpp", "gq_launch.hpp")) -> str:
+    """Hash of the sources a kernel is built from (default: the dominant one's)."""
     h = hashlib.sha256()
-    for name in ("gq_qmv.hip", "gq_device.hpp", "gq_launch.hpp"):
+    for name in names:
         with open(os.path.join(ROOT, "gguf_block_quant_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -724,6 +724,100 @@ def pmc_step_mode(args, log):
     log("pmc pass done: 3 steps of %d launches, 3 x copy of %d bytes" % (len(launches), COPY_BYTES))
 
 
+def pmc_kq_mode(args, log):
+    """The K-quant matvecs at 262144 x 2048 (3 launches each, Q4_K then
+    Q6_K), then a calibration copy of known size (3 launches), for the
+    rocprofv3 --pmc passes of the K-quant kernels. Prints the launches with
+    their algorithmic bytes as one JSON line."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import gguf_block_quant_amd as gq
+    import synth
+
+    L = gq.raw()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    n, k = 262144, 2048
+    x = torch.from_numpy(synth.activations(np.random.default_rng(5), k)).cuda()
+    launches, work = [], []
+    for qtype, tname, fn, sb in ((gq.TYPE_Q4_K, "q4_k", L.gq_qmv_q4_k, 144), (gq.TYPE_Q6_K, "q6_k", L.gq_qmv_q6_k, 210)):
+        raw = torch.from_numpy(synth.as_bytes(synth.weights(np.random.default_rng(n + qtype), qtype, n, k))
+                               .reshape(-1)).cuda()
+        pk = gq.kq_pack(qtype, raw, n, k)
+        y = torch.empty(n, dtype=torch.float32, device="cuda")
+        work.append((fn, pk, y))
+        launches.append(["qmv_%s %dx%d" % (tname, n, k), n * (k // 256) * sb, k * 4 + n * 4])
+        del raw
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for fn, pk, y in work:
+        for _ in range(3):
+            if fn(P(pk), n, k, P(x), P(y), None) != 0:
+                raise RuntimeError("launch failed")
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"kq_launches": launches, "reps": 3}), flush=True)
+    log("pmc pass done: 3 x each K-quant matvec, 3 x copy of %d bytes" % COPY_BYTES)
+
+
+KQ_TRAFFIC_FILE = os.path.join(PROFILES, "qmv_kquant_262144x2048_hbm_traffic.txt")
+
+
+def kq_traffic_summary(args):
+    """HBM bytes of the K-quant matvecs against their algorithmic bytes, from
+    a FETCH_SIZE and a WRITE_SIZE run of ``--mode pmc-kq``, each counter
+    scaled by its reading for the device copy of known size in the same run."""
+    fetch_dir, write_dir = args.kq_traffic_summary.split(",")
+    run = None
+    for line in open(fetch_dir.rstrip("/") + ".log"):
+        if line.startswith('{"kq_launches"'):
+            run = json.loads(line)
+    if run is None:
+        raise SystemExit("no kq_launches line in %s.log" % fetch_dir.rstrip("/"))
+    launches, reps = run["kq_launches"], run["reps"]
+    per, factors = {}, {}
+    for counter, run_dir in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_dispatches(run_dir, counter)
+        work = [r for r in rows if "qmv_q4_k_kernel" in r[1] or "qmv_q6_k_kernel" in r[1]]
+        if len(work) != reps * len(launches):
+            raise SystemExit("%s: %d K-quant dispatches, expected %d" % (run_dir, len(work), reps * len(launches)))
+        copies = [r for r in rows if "copy" in r[1].lower()]
+        big = max(r[2] for r in copies)
+        cal = [r[3] for r in copies if r[2] == big][-3:]
+        factors[counter] = COPY_BYTES / (1024.0 * (sum(cal) / len(cal)))
+        for i, r in enumerate(work):
+            per.setdefault(launches[i // reps][0], {}).setdefault(counter, []).append(
+                r[3] * 1024.0 * factors[counter])
+    lines = [
+        "# HBM traffic of the K-quant matvecs (fp32 x, 262144 x 2048; bench.py --mode pmc-kq), MI355X",
+        "# commands (repository root R on the GPU host; one counter per run):",
+        "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -d $R/%s -o run \\" % fetch_dir,
+        "#       --output-format csv -- python3 $R/bench.py --mode pmc-kq > $R/%s.log" % fetch_dir.rstrip("/"),
+        "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -d $R/%s -o run \\" % write_dir,
+        "#       --output-format csv -- python3 $R/bench.py --mode pmc-kq > $R/%s.log" % write_dir.rstrip("/"),
+        "#   python3 bench.py --kq-traffic-summary %s,%s --write-profile" % (fetch_dir, write_dir),
+        "# each counter scaled by its reading for a %d-byte device copy in the same run (factors: FETCH_SIZE "
+        "%.4f, WRITE_SIZE %.4f); bytes per launch, mean of %d launches"
+        % (COPY_BYTES, factors["FETCH_SIZE"], factors["WRITE_SIZE"], reps),
+        "# algorithmic = super-block bytes + x read + y written",
+        "# kernel_source_hash = %s" % kernel_source_hash(("gq_kquant.hip", "gq_device.hpp", "gq_launch.hpp")),
+        "%-24s %13s %11s %13s %8s" % ("launch", "fetch_B", "write_B", "algorithmic_B", "ratio"),
+    ]
+    for name, w, o in launches:
+        f = sum(per[name]["FETCH_SIZE"]) / reps
+        wr = sum(per[name]["WRITE_SIZE"]) / reps
+        lines.append("%-24s %13.0f %11.0f %13d %8.3f" % (name, f, wr, w + o, (f + wr) / (w + o)))
+    text = "\n".join(lines) + "\n"
+    print(text)
+    if args.write_profile:
+        with open(KQ_TRAFFIC_FILE, "w") as f:
+            f.write(text)
+
+
 STEP_TRAFFIC_FILE = os.path.join(PROFILES, "decode_step_hbm_traffic.txt")
 
 
@@ -811,7 +905,9 @@ def counters_summary(args):
     csv's GRBM_GUI_ACTIVE is summed over the 8 XCDs and so divided by 8 to get
     the busy cycles of one (the profiler's own derived metrics take the max
     over XCDs)."""
-    dir_a, dir_b = args.counters_summary.split(",")
+    dir_a, dir_b, *rest = args.counters_summary.split(",")
+    out_file = os.path.join(PROFILES, rest[0]) if rest else COUNTERS_FILE
+    mode = "pmc-kq" if rest and "kquant" in rest[0] else "pmc-step"
 
     def per_kernel(run_dir, names):
         out = {}
@@ -825,13 +921,13 @@ def counters_summary(args):
     b = per_kernel(dir_b, ("SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU", "GRBM_GUI_ACTIVE"))
     avg = lambda v: sum(v) / len(v)  # noqa: E731
     lines = [
-        "# VALU and MFMA counters per kernel of one decode step (bench.py --mode pmc-step: 3 steps), MI355X",
+        "# VALU and MFMA counters per kernel (bench.py --mode %s), MI355X" % mode,
         "# commands (repository root R on the GPU host; one pass per run):",
         "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_I8 \\",
-        "#       GRBM_GUI_ACTIVE -d $R/%s -o run --output-format csv -- python3 $R/bench.py --mode pmc-step" % dir_a,
+        "#       GRBM_GUI_ACTIVE -d $R/%s -o run --output-format csv -- python3 $R/bench.py --mode %s" % (dir_a, mode),
         "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc SQ_ACTIVE_INST_VALU SQ_INSTS_VALU GRBM_GUI_ACTIVE \\",
-        "#       -d $R/%s -o run --output-format csv -- python3 $R/bench.py --mode pmc-step" % dir_b,
-        "#   python3 bench.py --counters-summary %s,%s --write-profile" % (dir_a, dir_b),
+        "#       -d $R/%s -o run --output-format csv -- python3 $R/bench.py --mode %s" % (dir_b, mode),
+        "#   python3 bench.py --counters-summary %s --write-profile" % args.counters_summary,
         "# valu_busy = SQ_ACTIVE_INST_VALU / %d CUs / G; mfma_util = SQ_VALU_MFMA_BUSY_CYCLES / (%d SIMDs x G);"
         % (CU_NUM, SIMD_NUM),
         "# G = GRBM_GUI_ACTIVE / %d (the csv sums it over the XCDs); mfma_i8_mops = SQ_INSTS_VALU_MFMA_MOPS_I8"
@@ -854,7 +950,7 @@ def counters_summary(args):
     text = "\n".join(lines) + "\n"
     print(text)
     if args.write_profile:
-        with open(COUNTERS_FILE, "w") as f:
+        with open(out_file, "w") as f:
             f.write(text)
 
 
@@ -923,6 +1019,10 @@ STATS_FILE = os.path.join(PROFILES, "decode_step_kernel_stats.txt")
 
 # what each kernel instantiation is in the default run
 KERNEL_LABELS = [
+    ("qmv_q4_k_kernel<1, 4>", "qmv Q4_K fp32 x: k 2048 (2048, 8192, 262144 rows)"),
+    ("qmv_q6_k_kernel<1, 4>", "qmv Q6_K fp32 x: k 2048 (2048, 8192, 262144 rows)"),
+    ("kq_pack_kernel<12>", "pack Q4_K"),
+    ("kq_pack_kernel<14>", "pack Q6_K"),
     ("qmv_kernel<8, 0, 2, 1, 4, false>", "qmv Q8_0 fp32 x, tall: vocab 262144 (+1/8) x2048"),
     ("qmv_kernel<8, 0, 2, 1, 4, true>", "qmv Q8_0 + rmsnorm + softcap + argmax stage 1: vocab"),
     ("argmax_reduce_kernel", "argmax stage 2 (one workgroup)"),
@@ -1078,10 +1178,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true", help="skip the per-workload throughput pass")
-    ap.add_argument("--mode", choices=["bench", "pmc", "pmc-step"], default="bench")
+    ap.add_argument("--mode", choices=["bench", "pmc", "pmc-step", "pmc-kq"], default="bench")
+    ap.add_argument("--kq-traffic-summary", metavar="FETCH_DIR,WRITE_DIR",
+                    help="FETCH_SIZE and WRITE_SIZE runs of --mode pmc-kq -> HBM bytes of the K-quant matvecs")
     ap.add_argument("--pmc-summary", default=None)
     ap.add_argument("--counters-summary", default=None,
-                    help="A_DIR,B_DIR of the two --mode pmc-step counter runs -> VALU / MFMA table")
+                    help="A_DIR,B_DIR[,FILE] of the two --mode pmc-step (or, with FILE naming 'kquant', pmc-kq) "
+                         "counter runs -> VALU / MFMA table (written to profiles/FILE)")
     ap.add_argument("--step-traffic-summary", metavar="FETCH_DIR,WRITE_DIR",
                     help="FETCH_SIZE and WRITE_SIZE runs of --mode pmc-step -> HBM bytes per kernel of the step")
     ap.add_argument("--stats-summary", default=None,
@@ -1107,6 +1210,9 @@ def main():
     if args.step_traffic_summary:
         step_traffic_summary(args)
         return
+    if args.kq_traffic_summary:
+        kq_traffic_summary(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this path runs on a single MI355X and has no multi-GPU "
@@ -1122,6 +1228,9 @@ def main():
         return
     if args.mode == "pmc-step":
         pmc_step_mode(args, log)
+        return
+    if args.mode == "pmc-kq":
+        pmc_kq_mode(args, log)
         return
 
     step = Step(args.sets, log)
