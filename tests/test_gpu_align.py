@@ -87,3 +87,28 @@ def test_ffn_and_tile_at_minimum_alignment():
     ref = down(gq.qmm_tile_m(qs, d, n, k, m, up(xq), up(xd)))
     got = down(gq.qmm_tile_m(qs, shifted(d), n, k, m, up(xq), shifted(up(xd)), y=out_shifted(m * n)))
     assert np.array_equal(got.reshape(m, n).view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("qtype", [gq.TYPE_Q4_K, gq.TYPE_Q6_K])
+def test_kquant_at_minimum_alignment(qtype):
+    """K-quant matvec with the packed weights and x 16 bytes past a 256-byte
+    boundary and y 4 bytes past one: the same bits as aligned buffers."""
+    rng = np.random.default_rng(13 + qtype)
+    n, k = 1001, 4096
+    w = synth.weights(rng, qtype, n, k)
+    x = rng.standard_normal(k).astype(np.float32)
+    p = gq.kq_pack(qtype, up(synth.as_bytes(w).reshape(-1)), n, k)
+    fn = gq.qmv_q4_k if qtype == gq.TYPE_Q4_K else gq.qmv_q6_k
+    ref = down(fn(p, n, k, up(x)))
+    pb = torch.empty(p.numel() + 16, dtype=torch.uint8, device="cuda")
+    ps = pb[16:]
+    ps.copy_(p)
+    xb = torch.empty(k + 4, dtype=torch.float32, device="cuda")
+    xs = xb[4:]
+    xs.copy_(up(x))
+    assert ps.data_ptr() % 256 == 16 and xs.data_ptr() % 256 == 16
+    y = out_shifted(n)
+    got = down(fn(ps, n, k, xs, y=y))
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    yr, ar = oracle.matvec(qtype, w, n, k, x)
+    check_within(got, yr, oracle.fp32_path_bound(ar), "shifted k-quant")

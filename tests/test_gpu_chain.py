@@ -186,3 +186,46 @@ def test_chain_records_nothing_for_a_rejected_call():
         yr, ar = oracle.matvec(Q4, w, n, k, down(x))
         check_within(down(y), yr, oracle.fp32_path_bound(ar), "chained single matvec")
         chain.close()
+
+
+def test_chained_kquant_matvecs():
+    """Q4_K and Q6_K matvecs recorded in one chain, replayed with new
+    activations: every replay bit-equal to eager calls, and within the bound
+    of the oracle."""
+    rng = np.random.default_rng(12)
+    n, k = 3000, 2304
+    s = torch.cuda.Stream()
+    ws = {}
+    for qtype in (gq.TYPE_Q4_K, gq.TYPE_Q6_K):
+        w = synth.weights(rng, qtype, n, k)
+        ws[qtype] = (w, gq.kq_pack(qtype, up(synth.as_bytes(w).reshape(-1)), n, k))
+    x = torch.zeros(k, dtype=torch.float32, device="cuda:0")
+    y = {q: torch.empty(n, dtype=torch.float32, device="cuda:0") for q in ws}
+    fns = {gq.TYPE_Q4_K: gq.qmv_q4_k, gq.TYPE_Q6_K: gq.qmv_q6_k}
+
+    def enqueue():
+        for q, (_, p) in ws.items():
+            fns[q](p, n, k, x, y=y[q], stream=s)
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        enqueue()
+        s.synchronize()
+        chain = gq.Chain(s)
+        with chain:
+            enqueue()
+        assert chain.launches == 2
+        for rep in range(3):
+            xv = synth.activations(rng, k)
+            x.copy_(up(xv))
+            chain.launch(s)
+            s.synchronize()
+            got = {q: down(y[q]).copy() for q in ws}
+            enqueue()
+            s.synchronize()
+            for q in ws:
+                assert np.array_equal(got[q].view(np.uint32), down(y[q]).view(np.uint32)), (rep, q)
+                if rep == 0:
+                    yr, ar = oracle.matvec(q, ws[q][0], n, k, xv)
+                    check_within(got[q], yr, oracle.fp32_path_bound(ar), "chained k-quant %d" % q)
+        chain.close()

@@ -33,6 +33,11 @@ def test_concurrent_host_threads_match_serial_calls():
     tqs, td = packed(gq, Q4, wt, 1024, 2048)
     txq, txd = synth.q8_0_activations(rng, 8, 2048)
     txq, txd = up(txq), up(txd)
+    kq = {}
+    for qtype in (gq.TYPE_Q4_K, gq.TYPE_Q6_K):
+        wk = synth.weights(rng, qtype, 2048, 4096)
+        kq[qtype] = gq.kq_pack(qtype, up(synth.as_bytes(wk).reshape(-1)), 2048, 4096)
+    kx = up(synth.activations(rng, 4096))
     torch.cuda.synchronize()
 
     def run(case_id, stream, out):
@@ -43,6 +48,8 @@ def test_concurrent_host_threads_match_serial_calls():
             out.append(fn(qs, d, n, k, x, stream=stream))
             out.append(fx(qs, d, n, k, x, stream=stream))
             out.append(gq.qmm_tile_m(tqs, td, 1024, 2048, 8, txq, txd, stream=stream))
+            out.append(gq.qmv_q4_k(kq[gq.TYPE_Q4_K], 2048, 4096, kx, stream=stream))
+            out.append(gq.qmv_q6_k(kq[gq.TYPE_Q6_K], 2048, 4096, kx, stream=stream))
 
     # serial reference on the default stream
     ref = []
