@@ -14,35 +14,41 @@
 //   Q6_K (210 B): ql[128] (low four bits), qh[64] (high two bits), int8
 //     scales[16], binary16 d; element e is d scales[e / 16] (q - 32).
 //
-// Packed layout (gq_kq_pack; byte moves only, sections 256-byte aligned):
+// Packed layout (gq_kq_pack; sections 256-byte aligned). Every value is
+// kept bit for bit; only the places of the scale and high-bit fields change,
+// so that a lane finds its own fields in one load with no unpacking:
 //   Q4_K: qs [n][k/2] (the quant bytes of each super-block in order), then
-//         hdr [n][k/256][16] (d, dmin and the 12 scale bytes).
-//   Q6_K: ql [n][k/2], qh [n][k/4], sc [n][k/16] int8, d [n][k/256] binary16.
-// A row's quants are then contiguous 16-byte units, one per lane: a wave
-// instruction reads 1 KiB of one row, as for Q4_0.
-//
+//         hdr [n][k/256][16]: d, dmin, then for each 64-element chunk g
+//         (sub-blocks 2g and 2g + 1) the 24-bit field sc_2g | sc_2g+1 << 6 |
+//         m_2g << 12 | m_2g+1 << 18 in bytes 4 + 3g .. 6 + 3g.
+//   Q6_K: ql [n][k/2] (as in the super-block); qh [n][k/4]: for each 16-byte
+//         unit of ql (below), 8 bytes holding the high two bits of its 32
+//         elements (layout at qh_fields); sc [n][k/16]: for each unit, its two
+//         int8 scales (low run, high run); d [n][k/256] binary16.
 // Decomposition: lane l of a wave owns unit l of its slice of the row (16
 // bytes = 32 elements, in two runs of 16 that share a sub-block scale each:
 //   Q4_K unit u of a super-block: runs 64(u/2) + 16(u%2) (low nibbles,
 //     sub-block u & 6) and that + 32 (high nibbles, sub-block (u & 6) + 1);
 //   Q6_K unit 4h + j: runs 128h + 16j (scale 8h + j) and that + 64 (scale
-//     8h + j + 4), the high bits from qh bytes 32h + 16(j % 2) ..).
+//     8h + j + 4), the high bits from the unit's own 8 packed qh bytes).
 // The lane's 32 activations stay in VGPRs for every row it streams. Rows
 // longer than 2048 elements are split over WS waves whose partial sums meet
 // in LDS in slice order; waves stream R rows per step; sums over lanes use
-// DPP (wave_sum), fixed order, no atomics.
+// DPP (wave_sum_last_row), fixed order, no atomics.
 #include <atomic>
 
 #include "gq_device.hpp"
 #include "gq_launch.hpp"
 
 // Measured on MI355X (fp32 x, k = 2048; 262144 / 8192 rows, and 2048 x 8192):
-// 4 rows per step with up to 2048 workgroups: Q4_K 62-64 / 5.3-5.4 / 5.6 us,
-// Q6_K 84-88 / 6.0-6.1 / 5.7-5.8 us; 2 rows at 1024 workgroups: 73 / 5.7 /
-// 5.8 and 92 / 6.6 / 6.9 us. Two row groups in flight per wave (a second
+// 4 rows per step with up to 2048 workgroups: Q4_K 58.2-58.5 / 4.9-5.2 /
+// 5.2-5.3 us, Q6_K 74.2-74.3 / 5.6-5.8 / 5.8 us (with the packed fields
+// read directly; the byte-copy layout, unpacking the GGUF fields in the
+// loop, gave 60-62 / 5.3 / 5.6 and 82-84 / 6.0-6.2 / 5.5-5.8 us); 2 rows at
+// 1024 workgroups were slower. Two row groups in flight per wave (a second
 // register set) measured no better: the loop is bound by its VALU work
-// (about 2.1 instructions per element for the exact nibble dot), not by
-// load latency.
+// (about 2.1 instructions per element for the exact nibble dot, 3.0 per
+// element in all for Q4_K and 3.5 for Q6_K), not by load latency.
 #ifndef GQ_KQ_R
 #define GQ_KQ_R 4            // rows per wave step
 #endif
@@ -86,6 +92,18 @@ size_t kq_layout(int type, int64_t n, int64_t k, size_t* offsets) {
 
 namespace {
 
+// qh_fields: the 8 high-bit bytes of a Q6_K unit are two words, one per pair
+// of the unit's 32-bit ql words (2p, 2p + 1). ql word c holds elements
+// 4c .. 4c + 3 of both runs (bytes b = 0..3: low nibble -> low run, high
+// nibble -> high run). Word c's eight 2-bit fields sit where the fp16
+// construction below ORs them in: low-run element 4c + b at bit
+// kq6_lo_pos(b) = 4, 6, 20, 22 and high-run element 4c + b at
+// kq6_hi_pos(b) = 8, 10, 24, 26 (b = 1 and 3 are brought down by a shift of
+// 2, together with their nibbles' shift of 8); word 2p + 1's fields are
+// rotated left by 8 into the free bits of the same 32-bit word.
+__host__ __device__ constexpr int kq6_lo_pos(int b) { return (b & 2) * 8 + (b & 1) * 2 + 4; }
+__host__ __device__ constexpr int kq6_hi_pos(int b) { return kq6_lo_pos(b) + 4; }
+
 // ---------------------------------------------------------------------------
 // Pack: one thread per super-block; byte loads (a GGUF block is only
 // 2-byte aligned at best), 16-byte stores into the aligned sections.
@@ -109,15 +127,66 @@ void kq_pack_kernel(const uint8_t* __restrict__ blocks, int64_t nsb_total, uint8
         uint8_t* qs = out + i * 128;
 #pragma unroll
         for (int c = 0; c < 8; ++c) copy16(16 + 16 * c, qs + 16 * c);
-        copy16(0, out + o1 + i * 16);                       // d, dmin, 12 scale bytes
+        // the GGUF 6-bit scales and minimums (12 bytes q[0..11] after d and
+        // dmin): sub-blocks 0-3 take the low six bits of q[j] (scale) and
+        // q[j + 4] (minimum); sub-blocks 4-7 take the nibbles of q[j + 4]
+        // (low, high) under the top two bits of q[j - 4] and q[j]
+        const uint8_t* q = src + 4;
+        uint32_t sc[8], mn[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            sc[j] = q[j] & 63u;
+            mn[j] = q[j + 4] & 63u;
+            sc[j + 4] = (q[j + 8] & 15u) | ((q[j] >> 6) << 4);
+            mn[j + 4] = (q[j + 8] >> 4) | ((q[j + 4] >> 6) << 4);
+        }
+        uint8_t h[16];
+        h[0] = src[0]; h[1] = src[1]; h[2] = src[2]; h[3] = src[3];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint32_t f = sc[2 * g] | (sc[2 * g + 1] << 6) | (mn[2 * g] << 12) | (mn[2 * g + 1] << 18);
+            h[4 + 3 * g] = static_cast<uint8_t>(f);
+            h[5 + 3 * g] = static_cast<uint8_t>(f >> 8);
+            h[6 + 3 * g] = static_cast<uint8_t>(f >> 16);
+        }
+        uint32_t hw[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            hw[w] = h[4 * w] | (h[4 * w + 1] << 8) | (h[4 * w + 2] << 16) | (static_cast<uint32_t>(h[4 * w + 3]) << 24);
+        *reinterpret_cast<uint4*>(out + o1 + i * 16) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
     } else {
         uint8_t* ql = out + i * 128;
 #pragma unroll
         for (int c = 0; c < 8; ++c) copy16(16 * c, ql + 16 * c);
-        uint8_t* qh = out + o1 + i * 64;
+        // unit u = 4 hh + j covers ql bytes 64 hh + 16 j .. + 15: elements
+        // 128 hh + 16 j + e (low nibbles, the low run) and + 64 (high
+        // nibbles, the high run), e < 16, whose high bits sit in qh byte
+        // 32 hh + 16 (j % 2) + e at bit 2 (j / 2) (low run) and 4 + 2 (j / 2)
+        uint32_t* qh = reinterpret_cast<uint32_t*>(out + o1 + i * 64);
+        uint16_t* scp = reinterpret_cast<uint16_t*>(out + o2 + i * 16);
+        const uint8_t* qhs = src + 128;
+        const int8_t* scs = reinterpret_cast<const int8_t*>(src + 192);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) copy16(128 + 16 * c, qh + 16 * c);
-        copy16(192, out + o2 + i * 16);                     // 16 int8 scales
+        for (int u = 0; u < 8; ++u) {
+            const int hh = u >> 2, j = u & 3;
+            const int sl = 2 * (j >> 1), shi = 4 + 2 * (j >> 1);
+            uint32_t field[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                uint32_t f = 0;
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    const uint32_t qb = qhs[32 * hh + 16 * (j & 1) + 4 * c + bb];
+                    f |= ((qb >> sl) & 3u) << kq6_lo_pos(bb);
+                    f |= ((qb >> shi) & 3u) << kq6_hi_pos(bb);
+                }
+                field[c] = f;
+            }
+            qh[2 * u] = field[0] | ((field[1] << 8) | (field[1] >> 24));
+            qh[2 * u + 1] = field[2] | ((field[3] << 8) | (field[3] >> 24));
+            scp[u] = static_cast<uint16_t>(static_cast<uint8_t>(scs[8 * hh + j]) |
+                                           (static_cast<uint16_t>(static_cast<uint8_t>(scs[8 * hh + j + 4])) << 8));
+        }
         *reinterpret_cast<uint16_t*>(out + o3 + i * 2) =
             static_cast<uint16_t>(src[208] | (src[209] << 8));
     }
@@ -184,9 +253,13 @@ void qmv_q4_k_kernel(const KqParams p) {
         sxa += xr[e];
         sxb += xr[16 + e];
     }
-    // which bytes of the 12 hold this lane's two sub-blocks (a = u & 6, b = a + 1)
-    const uint32_t jsh = 8u * (u & 2u);            // byte (a & 3) of a scale word
-    const bool hi_sub = (u & 4u) != 0;             // sub-blocks 4..7: the split 6-bit encoding
+    // this lane's chunk g = u / 2 (sub-blocks 2g, 2g + 1): its 24-bit field
+    // is bytes 3g .. 3g + 2 of the header's last 12, gathered by one byte
+    // permute from the word pair (y, z) for g < 2, else (z, w)
+    const uint32_t g = u >> 1;
+    const bool first_pair = g < 2u;
+    const uint32_t fb = first_pair ? 3u * g : 3u * g - 4u;
+    const uint32_t psel = fb | ((fb + 1u) << 8) | ((fb + 2u) << 16) | (0x0Cu << 24);    // 0x0C: a zero byte
 
     uint32_t magic = 0x64006400u;
     asm volatile("" : "+v"(magic));
@@ -227,32 +300,33 @@ void qmv_q4_k_kernel(const KqParams p) {
                 pb = fmaf(static_cast<float>(hi13.y), xr[16 + 4 * j + 3], pb);
             }
             pb *= 0.0625f;                              // exact
-            // the two sub-blocks' 6-bit scales and minimums, side by side in
-            // the low two bytes of SC and MN
+            // the two sub-blocks' 6-bit scales and minimums
             uint32_t hx = h[r].x, hy = h[r].y, hz = h[r].z, hw = h[r].w;
             asm volatile("" : "+v"(hx), "+v"(hy), "+v"(hz), "+v"(hw));
-            const uint32_t Y = hy >> jsh, Z = hz >> jsh, W = hw >> jsh;
-            const uint32_t SC = hi_sub ? ((W & 0x0F0Fu) | ((Y >> 2) & 0x3030u)) : (Y & 0x3F3Fu);
-            const uint32_t MN = hi_sub ? (((W >> 4) & 0x0F0Fu) | ((Z >> 2) & 0x3030u)) : (Z & 0x3F3Fu);
-            const float sca = static_cast<float>(SC & 0xFFu), scb = static_cast<float>((SC >> 8) & 0xFFu);
-            const float mna = static_cast<float>(MN & 0xFFu), mnb = static_cast<float>((MN >> 8) & 0xFFu);
-            const float dd = valid ? half_bits_to_float(static_cast<uint16_t>(hx & 0xFFFFu)) : 0.f;
-            const float dm = valid ? half_bits_to_float(static_cast<uint16_t>(hx >> 16)) : 0.f;
+            const uint32_t f = __builtin_amdgcn_perm(first_pair ? hz : hw, first_pair ? hy : hz, psel);
+            const float sca = static_cast<float>(f & 63u), scb = static_cast<float>((f >> 6) & 63u);
+            const float mna = static_cast<float>((f >> 12) & 63u), mnb = static_cast<float>((f >> 18) & 63u);
+            // d and dmin stay binary16: v_fma_mix_f32 takes them as they are
+            // (their products with fp32 values round once, as after a conversion)
+            const half2_t dh = __builtin_bit_cast(half2_t, valid ? hx : 0u);
             const float t1 = fmaf(scb, pb, sca * pa);
             const float t2 = fmaf(mnb, sxb, mna * sxa);
-            acc[r] = fmaf(dd, t1, -(dm * t2));
+            const float pm = fmaf(static_cast<float>(dh.y), t2, 0.f);
+            acc[r] = fmaf(static_cast<float>(dh.x), t1, -pm);
         }
+        // the row sums are complete in lanes 48..63: lane 64 - R + r stores row r
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+        for (int r = 0; r < R; ++r) acc[r] = wave_sum_last_row(acc[r]);
         if constexpr (WS == 1) {
-            if (lane < R) {
+            const int lr = lane - (kWave - R);
+            if (lr >= 0) {
                 float a = acc[0];
 #pragma unroll
-                for (int r = 1; r < R; ++r) a = lane == r ? acc[r] : a;
-                if (r0 + lane < p.n) p.y[r0 + lane] = a;
+                for (int r = 1; r < R; ++r) a = lr == r ? acc[r] : a;
+                if (r0 + lr < p.n) p.y[r0 + lr] = a;
             }
         } else {
-            if (lane == 0) {
+            if (lane == kWave - 1) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) lpart[wave][r] = acc[r];
             }
@@ -294,9 +368,6 @@ void qmv_q6_k_kernel(const KqParams p) {
     }
 #pragma unroll
     for (int e = 0; e < 32; ++e) xr[e] = valid ? xr[e] : 0.f;
-    const uint32_t sh_lo = 2u * (j >> 1);          // bit pair of qh for the low run
-    const uint32_t sh_hi = 4u + sh_lo;             // ... and for the high run
-    const uint32_t ssh = 8u * j;                   // byte of the scale words
 
     uint32_t magic = 0x64006400u;
     asm volatile("" : "+v"(magic));
@@ -307,9 +378,9 @@ void qmv_q6_k_kernel(const KqParams p) {
     __shared__ float lpart[WAVES][R];
     for (int it = blockIdx.x; it * SUBS < p.row_groups; it += gridDim.x) {
         const int r0 = (it * SUBS + sub) * R;
-        uint4 ql[R], qh[R];
-        uint2 scw[R];
-        uint16_t db[R];
+        uint4 ql[R];
+        uint2 qh[R];
+        uint16_t scw[R], db[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const uint32_t row = static_cast<uint32_t>(min(r0 + r, p.n - 1));
@@ -317,32 +388,37 @@ void qmv_q6_k_kernel(const KqParams p) {
             const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
                 p.q + static_cast<uint64_t>(row) * static_cast<uint32_t>(p.k / 2) + uload * 16u));
             ql[r] = make_uint4(t.x, t.y, t.z, t.w);
-            qh[r] = *reinterpret_cast<const uint4*>(p.qh + static_cast<uint64_t>(row) * static_cast<uint32_t>(p.k / 4) +
-                                                    sb * 64u + hh * 32u + (j & 1u) * 16u);
-            scw[r] = *reinterpret_cast<const uint2*>(p.sc + static_cast<uint64_t>(row) * static_cast<uint32_t>(p.k / 16) +
-                                                     sb * 16u + hh * 8u);
+            qh[r] = *reinterpret_cast<const uint2*>(p.qh + static_cast<uint64_t>(row) * static_cast<uint32_t>(p.k / 4) +
+                                                    uload * 8u);
+            scw[r] = *reinterpret_cast<const uint16_t*>(p.sc + static_cast<uint64_t>(row) * static_cast<uint32_t>(p.k / 16) +
+                                                        uload * 2u);
             db[r] = p.d[static_cast<uint64_t>(row) * nsb + sb];
         }
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const uint32_t w[4] = {ql[r].x, ql[r].y, ql[r].z, ql[r].w};
-            const uint32_t b[4] = {qh[r].x, qh[r].y, qh[r].z, qh[r].w};
+            const uint32_t hp[2] = {qh[r].x, qh[r].y};
             float plo = 0.f, phi = 0.f;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const uint32_t v = w[c], v8 = v >> 8;
-                const uint32_t bl = b[c] >> sh_lo, bh = b[c] >> sh_hi;
-                // low run: nibble at bits 0-3 of each 16-bit half, high bits to 4-5
-                const half2_t lo02 = __builtin_bit_cast(half2_t, ((v & 0x000F000Fu) | magic) |
-                                                                     ((bl << 4) & 0x00300030u)) + off_lo;
-                const half2_t lo13 = __builtin_bit_cast(half2_t, ((v8 & 0x000F000Fu) | magic) |
-                                                                     ((bl >> 4) & 0x00300030u)) + off_lo;
-                // high run in place: nibble at bits 4-7, high bits to 8-9
-                const half2_t hi02 = __builtin_bit_cast(half2_t, ((v & 0x00F000F0u) | magic) |
-                                                                     ((bh << 8) & 0x03000300u)) + off_hi;
-                const half2_t hi13 = __builtin_bit_cast(half2_t, ((v8 & 0x00F000F0u) | magic) |
-                                                                     (bh & 0x03000300u)) + off_hi;
+                // the word's high-bit fields: in place for even c, rotated
+                // right by 8 for odd c; elements 4c + 1 and 4c + 3 shifted
+                // down by 2 together with their nibbles' shift of 8
+                const uint32_t hc = (c & 1) ? __builtin_amdgcn_alignbit(hp[c >> 1], hp[c >> 1], 8) : hp[c >> 1];
+                const uint32_t hc2 = hc >> 2;
+                // low run: nibble at bits 0-3 of each 16-bit half, high bits at 4-5;
+                // high run in place: nibble at bits 4-7, high bits at 8-9. The
+                // nibble-and-exponent words pass through an opaque statement, so
+                // each OR-in of high bits is one v_and_or_b32 (not and, and, or3)
+                uint32_t n02 = (v & 0x000F000Fu) | magic, n13 = (v8 & 0x000F000Fu) | magic;
+                uint32_t m02 = (v & 0x00F000F0u) | magic, m13 = (v8 & 0x00F000F0u) | magic;
+                asm volatile("" : "+v"(n02), "+v"(n13), "+v"(m02), "+v"(m13));
+                const half2_t lo02 = __builtin_bit_cast(half2_t, (hc & 0x00300030u) | n02) + off_lo;
+                const half2_t lo13 = __builtin_bit_cast(half2_t, (hc2 & 0x00300030u) | n13) + off_lo;
+                const half2_t hi02 = __builtin_bit_cast(half2_t, (hc & 0x03000300u) | m02) + off_hi;
+                const half2_t hi13 = __builtin_bit_cast(half2_t, (hc2 & 0x03000300u) | m13) + off_hi;
                 plo = fmaf(static_cast<float>(lo02.x), xr[4 * c + 0], plo);
                 phi = fmaf(static_cast<float>(hi02.x), xr[16 + 4 * c + 0], phi);
                 plo = fmaf(static_cast<float>(lo13.x), xr[4 * c + 1], plo);
@@ -352,24 +428,26 @@ void qmv_q6_k_kernel(const KqParams p) {
                 plo = fmaf(static_cast<float>(lo13.y), xr[4 * c + 3], plo);
                 phi = fmaf(static_cast<float>(hi13.y), xr[16 + 4 * c + 3], phi);
             }
-            uint32_t s0 = scw[r].x, s1 = scw[r].y, dbits = db[r];
-            asm volatile("" : "+v"(s0), "+v"(s1), "+v"(dbits));
-            const float sl = static_cast<float>(static_cast<int8_t>(s0 >> ssh));
-            const float sh = static_cast<float>(static_cast<int8_t>(s1 >> ssh));
+            uint32_t s01 = scw[r], dbits = db[r];
+            asm volatile("" : "+v"(s01), "+v"(dbits));
+            const float sl = static_cast<float>(static_cast<int8_t>(s01 & 0xFFu));
+            const float sh = static_cast<float>(static_cast<int8_t>(s01 >> 8));
             const float dd = valid ? half_bits_to_float(static_cast<uint16_t>(dbits)) : 0.f;
             acc[r] = dd * fmaf(sh * 0.0625f, phi, sl * plo);
         }
+        // the row sums are complete in lanes 48..63: lane 64 - R + r stores row r
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+        for (int r = 0; r < R; ++r) acc[r] = wave_sum_last_row(acc[r]);
         if constexpr (WS == 1) {
-            if (lane < R) {
+            const int lr = lane - (kWave - R);
+            if (lr >= 0) {
                 float a = acc[0];
 #pragma unroll
-                for (int r = 1; r < R; ++r) a = lane == r ? acc[r] : a;
-                if (r0 + lane < p.n) p.y[r0 + lane] = a;
+                for (int r = 1; r < R; ++r) a = lr == r ? acc[r] : a;
+                if (r0 + lr < p.n) p.y[r0 + lr] = a;
             }
         } else {
-            if (lane == 0) {
+            if (lane == kWave - 1) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) lpart[wave][r] = acc[r];
             }

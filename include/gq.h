@@ -79,7 +79,7 @@
 extern "C" {
 #endif
 
-#define GQ_ABI_VERSION 6
+#define GQ_ABI_VERSION 7
 
 enum {
     GQ_OK = 0,
@@ -99,7 +99,8 @@ enum {
     GQ_TYPE_Q6_K = 14        /* GGUF type id of Q6_K (256-element super-blocks) */
 };
 
-/* Version of this header's signatures; bumped on any change, so that a
+/* Version of this header's signatures and of the packed layouts the pack
+ * calls write; bumped on any change (7: the K-quant packed layout), so that a
  * caller can probe what the loaded library supports before using it (the
  * capability probe of the TensorSharp Gemma 4 page, batched fused decode
  * section: the managed side queries the native library and keeps older
@@ -334,11 +335,22 @@ int gq_qmm_tile_m(const uint8_t *qs, const uint16_t *d, int64_t n, int64_t k, in
  *
  * gq_kq_pack splits the GGUF super-blocks (device memory, contiguous, any
  * alignment) into ONE packed device buffer of gq_kq_packed_bytes(type, n, k)
- * bytes, 16-byte aligned, holding byte-for-byte copies in 256-byte aligned
- * sections (the load-time kernel-layout pack of gq_pack):
- *  - Q4_K: quants [n][k/2], then headers [n][k/256][16] (d, dmin, the 12
- *    scale bytes);
- *  - Q6_K: ql [n][k/2], qh [n][k/4], scales [n][k/16], d [n][k/256].
+ * bytes, 16-byte aligned, in 256-byte aligned sections (the load-time
+ * kernel-layout pack of gq_pack). Every bit of the super-blocks is kept;
+ * the scale and high-bit fields are rearranged so that each 16-byte quant
+ * unit's own fields can be read with one load and no unpacking:
+ *  - Q4_K: quants [n][k/2] (byte copies), then headers [n][k/256][16]: d,
+ *    dmin, then for each 64-element chunk g (sub-blocks 2g and 2g+1) the
+ *    24-bit field sc_2g | sc_2g+1 << 6 | m_2g << 12 | m_2g+1 << 18 in bytes
+ *    4+3g .. 6+3g;
+ *  - Q6_K: ql [n][k/2] (byte copies); qh [n][k/4]: for each 16-byte ql unit
+ *    u = 4h + j of a super-block (elements 128h + 16j + e, e < 16, and those
+ *    + 64), two little-endian 32-bit words; ql word c of the unit holds
+ *    elements 4c .. 4c+3 of both runs, whose 2-bit high parts sit at bits 4,
+ *    6, 20, 22 (the first run) and 8, 10, 24, 26 (the second) of a field;
+ *    word p holds field 2p as it is and field 2p+1 rotated left by 8;
+ *    scales [n][k/16]: per unit, its two int8 scales (8h + j, 8h + j + 4);
+ *    d [n][k/256] binary16.
  * gq_kq_packed_bytes returns 0 for an unknown type or invalid shape.
  *
  * gq_qmv_q4_k / gq_qmv_q6_k -- decode matvec on a packed K-quant matrix

@@ -40,7 +40,7 @@ def test_header_symbols_all_exported():
 
 
 def test_version_and_status_strings():
-    assert gq.abi_version() == 6
+    assert gq.abi_version() == 7
     for s in range(8):
         assert gq.status_str(s)
     assert gq.status_str(99) == "unknown status"

@@ -1,5 +1,5 @@
 """GPU parity of the K-quant path (Q4_K, Q6_K super-blocks of 256 elements):
-the load-time pack moves bytes exactly, and the fp32-activation matvec
+the load-time pack lays out every byte as specified, and the fp32-activation matvec
 matches the fp64 oracle (which reads the canonical GGUF super-block bytes)
 within |y - y_ref| <= 1e-4 sum|w x| + 1e-6 at every dispatch shape, bit for
 bit on one-hot and exact-arithmetic inputs, with special scale values, and
@@ -9,6 +9,7 @@ import pytest
 
 import oracle
 import synth
+import kq_layout_model as kq_model
 from gpu_util import check_special, check_within, down, packed_kq, up
 
 pytestmark = pytest.mark.gpu
@@ -27,7 +28,9 @@ def _fn(qtype):
 
 
 @pytest.mark.parametrize("qtype,n,k", [(Q4K, 7, 256), (Q4K, 33, 2048), (Q6K, 7, 256), (Q6K, 33, 4352)])
-def test_kq_pack_moves_bytes_exactly(qtype, n, k):
+def test_kq_pack_lays_out_every_byte(qtype, n, k):
+    # the packed sections are the layout's lossless rearrangement of the GGUF
+    # bits (modelled on the host; the model is pinned by test_kq_layout.py)
     w = synth.weights(np.random.default_rng(n + k), qtype, n, k)
     p = down(packed_kq(gq, qtype, w, n, k))
     assert p.size >= gq.kq_packed_bytes(qtype, n, k)
@@ -38,16 +41,16 @@ def test_kq_pack_moves_bytes_exactly(qtype, n, k):
         o1 = r256(n * k // 2)
         hdr = p[o1: o1 + n * nsb * 16].reshape(n, nsb, 16)
         assert np.array_equal(qs, w["qs"])
-        assert np.array_equal(hdr[..., 0:2].copy().view(np.uint16)[..., 0], w["d"])
-        assert np.array_equal(hdr[..., 2:4].copy().view(np.uint16)[..., 0], w["dmin"])
-        assert np.array_equal(hdr[..., 4:16], w["scales"])
+        assert np.array_equal(hdr, kq_model.q4_k_header(w))
     else:
         o1 = r256(n * k // 2)
         o2 = o1 + r256(n * k // 4)
         o3 = o2 + r256(n * k // 16)
         assert np.array_equal(p[: n * k // 2].reshape(n, nsb, 128), w["ql"])
-        assert np.array_equal(p[o1: o1 + n * k // 4].reshape(n, nsb, 64), w["qh"])
-        assert np.array_equal(p[o2: o2 + n * k // 16].view(np.int8).reshape(n, nsb, 16), w["scales"])
+        assert np.array_equal(p[o1: o1 + n * k // 4].copy().view("<u4").reshape(n, nsb, 8, 2),
+                              kq_model.q6_k_high_words(w))
+        assert np.array_equal(p[o2: o2 + n * k // 16].view(np.int8).reshape(n, nsb, 8, 2),
+                              kq_model.q6_k_unit_scales(w))
         assert np.array_equal(p[o3: o3 + n * nsb * 2].view(np.uint16).reshape(n, nsb), w["d"])
 
 
