@@ -56,27 +56,6 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
-// The same sum, complete only in lanes 48..63 (the last row of 16), with
-// two DPP row broadcasts in place of the four lane reads: every row adds
-// lane 15 of the row before it (row 0 adds 0), then rows 2 and 3 add lane 31.
-// Row 3 ends with (s3 + s2) + (s1 + s0) -- the same additions as wave_sum,
-// so the same bits (fp32 addition is commutative); the other rows hold
-// partial sums. (Full row masks and zero for missing source lanes let each
-// step be one v_add_f32_dpp.)
-constexpr int kDppRowBcast15 = 0x142;
-constexpr int kDppRowBcast31 = 0x143;
-__device__ __forceinline__ float wave_sum_last_row(float v) {
-    v += dpp_f32<kDppQuadSwap1>(v);
-    v += dpp_f32<kDppQuadSwap2>(v);
-    v += dpp_f32<kDppRowHalfMirror>(v);
-    v += dpp_f32<kDppRowMirror>(v);
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kDppRowBcast15,
-                                                               0xF, 0xF, true));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kDppRowBcast31,
-                                                               0xF, 0xF, true));
-    return v;
-}
-
 // Sum of a double over the 64 lanes of the wave (xor butterfly: lane i and
 // lane i ^ o add the same two values, so every lane ends with the same bits,
 // and the order is fixed run to run).

@@ -60,6 +60,28 @@ namespace gq {
 
 namespace {
 
+// The sum of v over the 64 lanes of the wave, as wave_sum computes it, but
+// complete only in lanes 48..63 (the last row of 16): two DPP row broadcasts
+// take the place of the four lane reads. Every row adds
+// lane 15 of the row before it (row 0 adds 0), then rows 2 and 3 add lane 31.
+// Row 3 ends with (s3 + s2) + (s1 + s0) -- the same additions as wave_sum,
+// so the same bits (fp32 addition is commutative); the other rows hold
+// partial sums. (Full row masks and zero for missing source lanes let each
+// step be one v_add_f32_dpp.)
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+__device__ __forceinline__ float wave_sum_last_row(float v) {
+    v += dpp_f32<kDppQuadSwap1>(v);
+    v += dpp_f32<kDppQuadSwap2>(v);
+    v += dpp_f32<kDppRowHalfMirror>(v);
+    v += dpp_f32<kDppRowMirror>(v);
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kDppRowBcast15,
+                                                               0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kDppRowBcast31,
+                                                               0xF, 0xF, true));
+    return v;
+}
+
 constexpr int kTypeQ4_K = 12;
 constexpr int kTypeQ6_K = 14;
 
