@@ -764,6 +764,217 @@ def pmc_kq_mode(args, log):
     log("pmc pass done: 3 x each K-quant matvec, 3 x copy of %d bytes" % COPY_BYTES)
 
 
+# ----------------------------------------------------------------------------
+# time against bytes: fixed cost and steady rate of each M = 1 kernel family
+# ----------------------------------------------------------------------------
+
+SWEEP_FILE = os.path.join(PROFILES, "matvec_fixed_cost_sweep.txt")
+SWEEP_WARMUP = 8
+SWEEP_GRAPH = 64
+SWEEP_REPLAYS = 7
+
+# (family, kernel-name key in the trace, shapes): every shape of a family
+# runs the same kernel instantiation (the launch rules pick it by shape)
+SWEEP_FAMILIES = [
+    ("qmv_q4_0 fp32 x, k 2048 (the 2048x2048 kernel)", "qmv_kernel<2, 0, 1, 1, 1, false>",
+     [1024, 2048, 4096, 8192, 12288]),
+    ("qffn_gate_up_gelu, k 2048 (2 x n_ff rows)", "qmv_kernel<2, 2, 1, 1, 2, false>",
+     [2048, 4096, 8192, 16384, 32768]),
+    ("qmv_q4_0 fp32 x, k 8192 (the down projection)", "qmv_kernel<2, 0, 1, 4, 4, false>",
+     [512, 1024, 2048, 4096, 8192]),
+    ("qmv_q8_0 fp32 x, k 2048, tall (the vocab head)", "qmv_kernel<8, 0, 2, 1, 4, false>",
+     [32768, 65536, 131072, 262144]),
+    ("read stream (16-byte loads, 8 KiB per wave, 256 workgroups)", "wave_chunk_kernel",
+     [8 << 20, 32 << 20, 128 << 20, 512 << 20]),
+]
+
+
+def sweep_mode(args, log):
+    """Each M = 1 kernel family of the step at several sizes (one kernel
+    instantiation per family), plus the plain read-stream kernel: per size,
+    rotated copies of random weights covering >= 1 GiB (the 256 MB last-level
+    cache never holds a launch's weights), SWEEP_WARMUP warm-up launches, then
+    64 launches over distinct copies recorded as one chain and replayed
+    1 + SWEEP_REPLAYS times, the last SWEEP_REPLAYS between events: the
+    device's back-to-back time per launch, free of the host's per-call cost
+    (which, at about 4 us through Python, would otherwise bound the short
+    kernels). Prints one JSON line: the launch manifest in order (so a
+    rocprofv3 kernel trace of this run can be cut into shapes) and the
+    per-launch times."""
+    import ctypes
+    import math
+
+    import torch
+
+    import gguf_block_quant_amd as gq
+
+    L = gq.raw()
+    stream = torch.cuda.Stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    bench_lib = ctypes.CDLL(os.path.join(ROOT, "gguf_block_quant_amd", "libgq_bench.so"))
+    bench_lib.gqb_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_void_p]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+
+    def scales(nblocks):
+        return (torch.rand(nblocks, device="cuda", generator=gen) * 9e-3 + 1e-3).half().view(torch.int16)
+
+    def quants(nbytes):
+        return torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=gen)
+
+    manifest, event_us = [], {}
+    read_out = torch.empty(256 * 256, dtype=torch.int32, device="cuda")
+    for fam, _key, sizes in SWEEP_FAMILIES:
+        for n in sizes:
+            if fam.startswith("read stream"):
+                wbytes, obytes = n, 0
+                make = lambda: (quants(n),)  # noqa: E731
+                call = lambda c: bench_lib.gqb_read_stream(P(c[0]), n, P(read_out), 256, 1, sp)  # noqa: E731
+            elif fam.startswith("qffn"):
+                k = 2048
+                wbytes, obytes = 2 * n * k // 32 * 18, k * 4 + n * 4
+                x = torch.randn(k, device="cuda", generator=gen)
+                h = torch.empty(n, device="cuda")
+                make = lambda: (quants(n * k // 2), scales(n * k // 32), quants(n * k // 2), scales(n * k // 32))  # noqa: E731
+                call = lambda c: L.gq_qffn_gate_up_gelu(P(c[0]), P(c[1]), P(c[2]), P(c[3]), n, 2048, P(x), P(h), sp)  # noqa: E731
+            else:
+                q8 = "q8_0" in fam
+                k = 8192 if "k 8192" in fam else 2048
+                wbytes, obytes = n * k // 32 * (34 if q8 else 18), k * 4 + n * 4
+                x = torch.randn(k, device="cuda", generator=gen)
+                y = torch.empty(n, device="cuda")
+                fn = L.gq_qmv_q8_0 if q8 else L.gq_qmv_q4_0
+                make = lambda: (quants(n * k if q8 else n * k // 2), scales(n * k // 32))  # noqa: E731
+                call = lambda c: fn(P(c[0]), P(c[1]), n, k, P(x), P(y), sp)  # noqa: E731
+            ncopies = max(2, math.ceil((1 << 30) / wbytes))
+            copies = [make() for _ in range(ncopies)]
+            torch.cuda.synchronize()
+            for i in range(SWEEP_WARMUP):
+                if call(copies[i % ncopies]) != 0:
+                    raise RuntimeError("launch failed: %s %d" % (fam, n))
+            torch.cuda.synchronize()
+            chain = gq.Chain(stream)
+            with chain:
+                for i in range(SWEEP_GRAPH):
+                    if call(copies[i % ncopies]) != 0:
+                        raise RuntimeError("launch failed: %s %d" % (fam, n))
+            chain.launch(stream)
+            torch.cuda.synchronize()
+            a, b = TimingEvent(), TimingEvent()
+            a.record(stream)
+            for _ in range(SWEEP_REPLAYS):
+                chain.launch(stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            chain.close()
+            launches = SWEEP_WARMUP + SWEEP_GRAPH * (1 + SWEEP_REPLAYS)
+            label = "%s | %d" % (fam, n)
+            manifest.append([fam, n, wbytes, obytes, launches, SWEEP_WARMUP + SWEEP_GRAPH])
+            event_us[label] = a.elapsed_time(b) * 1e3 / (SWEEP_REPLAYS * SWEEP_GRAPH)
+            log("sweep %s: %.2f us per launch back to back (%d copies)" % (label, event_us[label], ncopies))
+            del copies
+            torch.cuda.empty_cache()
+    print(json.dumps({"sweep_manifest": manifest, "event_us": event_us}), flush=True)
+
+
+def _fit(points):
+    """Least-squares fit t = a + bytes / rate over (bytes, t_us) points:
+    (a in us, rate in TB/s)."""
+    n = len(points)
+    mx = sum(b for b, _ in points) / n
+    my = sum(t for _, t in points) / n
+    sxx = sum((b - mx) ** 2 for b, _ in points)
+    sxy = sum((b - mx) * (t - my) for b, t in points)
+    slope = sxy / sxx                      # us per byte
+    return my - slope * mx, 1.0 / slope / 1e6
+
+
+def sweep_summary(args):
+    """Fixed cost and steady rate per kernel family, from a rocprofv3
+    --kernel-trace run of ``--mode sweep`` (kernel durations, median of each
+    shape's timed launches) and from the same run's back-to-back event times."""
+    run_dir, _, plain_log = args.sweep_summary.partition(",")
+    run_dir = run_dir.rstrip("/")
+
+    def sweep_line(path):
+        found = None
+        for line in open(path):
+            if line.startswith('{"sweep_manifest"'):
+                found = json.loads(line)
+        if found is None:
+            raise SystemExit("no sweep_manifest line in %s" % path)
+        return found
+
+    run = sweep_line(run_dir + ".log")
+    # the back-to-back times from the same command without the profiler
+    # (under it, every dispatch waits for its trace record)
+    plain = sweep_line(plain_log) if plain_log else None
+    if plain is not None and [m[:5] for m in plain["sweep_manifest"]] != [m[:5] for m in run["sweep_manifest"]]:
+        raise SystemExit("the plain run's manifest differs from the traced run's")
+    files = glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no kernel_trace.csv under %s" % run_dir)
+    keys = [key for _, key, _ in SWEEP_FAMILIES]
+    rows = []
+    for r in csv.DictReader(open(files[0])):
+        if any(k in r["Kernel_Name"] for k in ("qmv_kernel", "wave_chunk_kernel")):
+            rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"],
+                         (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    rows.sort()
+    pos = 0
+    durations = {}
+    for fam, n, wb, ob, launches, skip in run["sweep_manifest"]:
+        part = rows[pos:pos + launches]
+        pos += launches
+        key = keys[[f for f, _, _ in SWEEP_FAMILIES].index(fam)]
+        if len(part) != launches or any(key not in name for _, name, _ in part):
+            raise SystemExit("trace does not match the manifest at %s %d" % (fam, n))
+        d = sorted(t for _, _, t in part[skip:])
+        durations[(fam, n)] = d[len(d) // 2]
+    if pos != len(rows):
+        raise SystemExit("trace has %d matvec dispatches, the manifest %d" % (len(rows), pos))
+    lines = [
+        "# Time against bytes per M = 1 kernel family (bench.py --mode sweep), MI355X: fixed cost per launch",
+        "# and steady rate from a least-squares fit t = fixed + bytes / rate over the sizes of one kernel",
+        "# instantiation (random weights, >= 1 GiB of rotated copies per size)",
+        "# command (repository root R on the GPU host):",
+        "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d $R/%s -o run \\" % run_dir,
+        "#       --output-format csv -- python3 $R/bench.py --mode sweep > $R/%s.log" % run_dir,
+        "#   cd $R && python3 bench.py --mode sweep > %s" % (plain_log or "(not given)"),
+        "#   python3 bench.py --sweep-summary %s%s --write-profile" % (run_dir, "," + plain_log if plain_log else ""),
+        "# kernel_us: median kernel duration in the trace (dispatch start to end; the replayed launches);",
+        "# launch_us: device time per launch, back to back, in 64-launch graph replays over distinct copies",
+        "# (the gap between dependent dispatches included), from the run without the profiler%s"
+        % ("" if plain else " -- NOT GIVEN: these are the profiled run's, inflated by the tracing"),
+        "# bytes = weight blocks + x + y (the read stream: its buffer)",
+        "# kernel_source_hash = %s" % kernel_source_hash(),
+    ]
+    for fam, key, sizes in SWEEP_FAMILIES:
+        lines.append("")
+        lines.append("%s   [%s]" % (fam, key))
+        lines.append("%10s %14s %10s %10s %9s" % ("size", "bytes", "kernel_us", "launch_us", "GB/s"))
+        kp, lp = [], []
+        for fam2, n, wb, ob, _, _ in run["sweep_manifest"]:
+            if fam2 != fam:
+                continue
+            kt = durations[(fam, n)]
+            lt = (plain or run)["event_us"]["%s | %d" % (fam, n)]
+            kp.append((wb + ob, kt))
+            lp.append((wb + ob, lt))
+            lines.append("%10d %14d %10.2f %10.2f %9.0f" % (n, wb + ob, kt, lt, (wb + ob) / kt / 1e3))
+        ka, kr = _fit(kp)
+        la, lr = _fit(lp)
+        lines.append("fit kernel: fixed %.2f us, steady %.2f TB/s;  back to back: fixed %.2f us, steady %.2f TB/s"
+                     % (ka, kr, la, lr))
+    text = "\n".join(lines) + "\n"
+    print(text)
+    if args.write_profile:
+        with open(SWEEP_FILE, "w") as f:
+            f.write(text)
+
+
 KQ_TRAFFIC_FILE = os.path.join(PROFILES, "qmv_kquant_262144x2048_hbm_traffic.txt")
 
 
@@ -1178,7 +1389,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true", help="skip the per-workload throughput pass")
-    ap.add_argument("--mode", choices=["bench", "pmc", "pmc-step", "pmc-kq"], default="bench")
+    ap.add_argument("--mode", choices=["bench", "pmc", "pmc-step", "pmc-kq", "sweep"], default="bench")
     ap.add_argument("--kq-traffic-summary", metavar="FETCH_DIR,WRITE_DIR",
                     help="FETCH_SIZE and WRITE_SIZE runs of --mode pmc-kq -> HBM bytes of the K-quant matvecs")
     ap.add_argument("--pmc-summary", default=None)
@@ -1191,6 +1402,10 @@ def main():
                     help="DIR[,BENCH_JSON]: rocprofv3 --kernel-trace --stats output dir of the default run "
                          "(its stdout in DIR.log) and optionally the JSON output of the same command run "
                          "without the profiler -> kernel table")
+    ap.add_argument("--sweep-summary", default=None,
+                    help="DIR[,PLAIN_LOG]: rocprofv3 --kernel-trace output dir of --mode sweep (its stdout in "
+                         "DIR.log) and the stdout of the same command without the profiler -> fixed cost and "
+                         "steady rate per kernel family")
     ap.add_argument("--write-profile", action="store_true",
                     help="with --pmc-summary: write the summary under profiles/")
     args = ap.parse_args()
@@ -1213,6 +1428,9 @@ def main():
     if args.kq_traffic_summary:
         kq_traffic_summary(args)
         return
+    if args.sweep_summary:
+        sweep_summary(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this path runs on a single MI355X and has no multi-GPU "
@@ -1231,6 +1449,9 @@ def main():
         return
     if args.mode == "pmc-kq":
         pmc_kq_mode(args, log)
+        return
+    if args.mode == "sweep":
+        sweep_mode(args, log)
         return
 
     step = Step(args.sets, log)
