@@ -56,13 +56,43 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
-// Sum of a double over the 64 lanes of the wave (xor butterfly: lane i and
-// lane i ^ o add the same two values, so every lane ends with the same bits,
-// and the order is fixed run to run).
+// Sum of a double over the 64 lanes of the wave, in every lane: the same
+// pairing and order as wave_sum (each DPP step moves the two 32-bit halves),
+// so the result is reproducible and identical in every lane -- and the same
+// bits as a xor butterfly over the lanes (fp64 addition is commutative).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(b), CTRL, 0xF, 0xF, false));
+    const uint32_t hi =
+        static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), CTRL, 0xF, 0xF, false));
+    return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b), l));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b >> 32), l));
+    return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    v += dpp_f64<kDppQuadSwap1>(v);
+    v += dpp_f64<kDppQuadSwap2>(v);
+    v += dpp_f64<kDppRowHalfMirror>(v);
+    v += dpp_f64<kDppRowMirror>(v);
+    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+// Largest of v over the 64 lanes, in every lane (max is exact in any order).
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_f32<kDppQuadSwap1>(v));
+    v = fmaxf(v, dpp_f32<kDppQuadSwap2>(v));
+    v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v));
+    v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 // Exact int8x4 dot product with int32 accumulate (v_dot4_i32_i8).

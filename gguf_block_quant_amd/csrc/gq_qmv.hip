@@ -266,6 +266,7 @@ void qmv_kernel(const QmvParams p) {
     __shared__ uint32_t qx_s[kQxWords];
     __shared__ uint16_t qd_s[kQuantX ? kQxWords / 8 : 1];
     __shared__ double nss[WAVES];
+    __shared__ float nmx[WAVES];
 
     // ---- this lane's units ------------------------------------------------
     int unit[NI];
@@ -435,6 +436,18 @@ void qmv_kernel(const QmvParams p) {
         return 1.0 / sqrt(sum / static_cast<double>(p.k) + static_cast<double>(p.norm_eps));
     };
     auto scaled = [](float v, double s) { return static_cast<float>(static_cast<double>(v) * s); };
+    // RMSNorm: when every |x_i w_i| lies in [2^-40, 2^40] (the usual case;
+    // uniform over the launch), the dots run on x w as staged and each
+    // finished row is multiplied by inv in fp64 (rounded once) -- no dot can
+    // overflow or lose precision to underflow there (|y| <= k 65504 127 2^40),
+    // and the prologue's fp64 work no longer delays the first dot. Outside
+    // that range the activations are scaled by inv before the dots, as an
+    // fp64 product rounded once, which keeps every dot in range for any
+    // finite x.
+    float mxl = 0.f;                 // this thread's max |x w|
+    bool post = false;               // scale the finished rows by post_inv
+    double post_inv = 1.0;
+    constexpr float kPostLo = 0x1p-40f, kPostHi = 0x1p40f;
     if constexpr (kStage) {
         // Un-split rows: every wave of the workgroup needs all of x, so the
         // workgroup reads it (and w) from memory once into LDS, padded to a
@@ -464,6 +477,9 @@ void qmv_kernel(const QmvParams p) {
                     if constexpr (kZeroPass) ss += j < nf4 ? q : 0.0;
                     else ss += q;                // t is zero past k
                     t.x *= g.x; t.y *= g.y; t.z *= g.z; t.w *= g.w;
+                    const float m4 = fmaxf(fmaxf(fabsf(t.x), fabsf(t.y)), fmaxf(fabsf(t.z), fabsf(t.w)));
+                    if constexpr (kZeroPass) mxl = j < nf4 ? fmaxf(mxl, m4) : mxl;
+                    else mxl = fmaxf(mxl, m4);
                 }
             }
             const int e = j << 2;
@@ -481,7 +497,11 @@ void qmv_kernel(const QmvParams p) {
         if constexpr (FOLD) {
             if (norm) {
                 ss = wave_sum_f64(ss);
-                if (lane == 0) nss[wave] = ss;
+                mxl = wave_max(mxl);
+                if (lane == 0) {
+                    nss[wave] = ss;
+                    nmx[wave] = mxl;
+                }
             }
         }
         __syncthreads();
@@ -489,9 +509,18 @@ void qmv_kernel(const QmvParams p) {
         if constexpr (FOLD) {
             if (norm) {
                 double t = nss[0];
+                float mx = nmx[0];
 #pragma unroll
-                for (int w = 1; w < WAVES; ++w) t += nss[w];
+                for (int w = 1; w < WAVES; ++w) {
+                    t += nss[w];
+                    mx = fmaxf(mx, nmx[w]);
+                }
                 inv = norm_scale(t);
+                post = mx >= kPostLo && mx <= kPostHi;
+                if (post) {
+                    post_inv = inv;
+                    inv = 1.0;
+                }
             }
         }
 #pragma unroll
@@ -503,8 +532,10 @@ void qmv_kernel(const QmvParams p) {
             for (int v = 0; v < EPU / 4; ++v) {
                 float4 t = *reinterpret_cast<const float4*>(xs + 4 * v);
                 if constexpr (FOLD) {
-                    t.x = scaled(t.x, inv); t.y = scaled(t.y, inv);
-                    t.z = scaled(t.z, inv); t.w = scaled(t.w, inv);
+                    if (norm && !post) {
+                        t.x = scaled(t.x, inv); t.y = scaled(t.y, inv);
+                        t.z = scaled(t.z, inv); t.w = scaled(t.w, inv);
+                    }
                 }
                 xr[i][4 * v + 0] = t.x; xr[i][4 * v + 1] = t.y;
                 xr[i][4 * v + 2] = t.z; xr[i][4 * v + 3] = t.w;
@@ -586,28 +617,57 @@ void qmv_kernel(const QmvParams p) {
                             ss = fma(static_cast<double>(xr[i][4 * v + c]), static_cast<double>(xr[i][4 * v + c]), ss);
                         xr[i][4 * v + 0] *= g.x; xr[i][4 * v + 1] *= g.y;
                         xr[i][4 * v + 2] *= g.z; xr[i][4 * v + 3] *= g.w;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) mxl = fmaxf(mxl, fabsf(xr[i][4 * v + c]));   // zero past k
                     }
                 }
                 ss = wave_sum_f64(ss);
-                if (lane == 0) nss[wave] = ss;
+                mxl = wave_max(mxl);
+                if (lane == 0) {
+                    nss[wave] = ss;
+                    nmx[wave] = mxl;
+                }
                 __syncthreads();
                 double t = nss[sub * WS];
+                float mx = nmx[sub * WS];
 #pragma unroll
-                for (int sl = 1; sl < WS; ++sl) t += nss[sub * WS + sl];
+                for (int sl = 1; sl < WS; ++sl) {
+                    t += nss[sub * WS + sl];
+                    mx = fmaxf(mx, nmx[sub * WS + sl]);
+                }
                 const double inv = norm_scale(t);
+                post = mx >= kPostLo && mx <= kPostHi;
+                if (post) {
+                    post_inv = inv;
+                } else {
 #pragma unroll
-                for (int i = 0; i < NI; ++i)
+                    for (int i = 0; i < NI; ++i)
 #pragma unroll
-                    for (int e = 0; e < EPU; ++e) xr[i][e] = scaled(xr[i][e], inv);
+                        for (int e = 0; e < EPU; ++e) xr[i][e] = scaled(xr[i][e], inv);
+                }
             }
         }
     }
 
     // ---- epilogue of one finished row: residual, soft cap, store, argmax --
     unsigned long long best = 0ull;
+    // the residual of the row this lane finishes (lane r of the row group
+    // holds row r), loaded when its group's dot starts -- in flight during the
+    // dot rather than a memory round trip after it
+    float resv = 0.f;
+    auto load_res = [&](int r0) {
+        if constexpr (FOLD) {
+            if (p.residual != nullptr) resv = p.residual[min(r0 + lane % R, p.n - 1)];
+        }
+    };
+    auto post_scale = [&](float v) {
+        if constexpr (FOLD) return post ? scaled(v, post_inv) : v;
+        else return v;
+    };
     auto emit = [&](int row, float v) {
         if constexpr (FOLD) {
-            if (p.residual != nullptr) v += p.residual[row];
+            (void)row;
+            if (p.residual != nullptr) v += resv;
             if (p.softcap > 0.0f) v = p.softcap * tanhf(v / p.softcap);
         }
         p.y[row] = v;
@@ -679,6 +739,8 @@ void qmv_kernel(const QmvParams p) {
                         a0 = lane == r ? acc[0][r] : a0;
                         a1 = lane == r ? acc[NMAT - 1][r] : a1;
                     }
+                    a0 = post_scale(a0);
+                    a1 = post_scale(a1);
                     const int row = r0 + lane;
                     if (row < p.n) {
                         if constexpr (MODE == kFFN)
@@ -710,7 +772,7 @@ void qmv_kernel(const QmvParams p) {
                     float t = lpart[wave][m][lane];
 #pragma unroll
                     for (int s = 1; s < WS; ++s) t += lpart[wave + s][m][lane];
-                    tot[m] = t;
+                    tot[m] = post_scale(t);
                 }
                 if (row < p.n) {
                     if constexpr (MODE == kFFN)
@@ -734,6 +796,7 @@ void qmv_kernel(const QmvParams p) {
             const int r0 = (it * SUBS + sub) * R;
             const int itn = it + gridDim.x;
             const bool more = itn * SUBS < p.row_groups;
+            load_res(r0);
             float acc[NMAT][R];
             dot_group(q, db, r0, acc);
             // pin the order: the dot is finished (its results pass through
@@ -755,6 +818,7 @@ void qmv_kernel(const QmvParams p) {
         for (; it * SUBS < p.row_groups; it += gridDim.x) {
             const int r0 = (it * SUBS + sub) * R;
             const int itn = it + gridDim.x;
+            load_res(r0);
             float acc[NMAT][R];
             dot_group(q, db, r0, acc);
             if (itn * SUBS < p.row_groups) load_group(q, db, (itn * SUBS + sub) * R);
