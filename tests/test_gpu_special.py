@@ -196,6 +196,48 @@ def test_rmsnorm_fold_full_fp32_range(qtype, n, k):
         check_within(y, yr, oracle.fp32_path_bound(ar), "rmsnorm %s type %d %dx%d" % (name, qtype, n, k))
 
 
+def _boundary_cases(rng, k):
+    """x and g whose largest |x g| sits exactly on, or one ulp outside, the
+    ends of the range where the fold scales the finished rows (2^-40, 2^40);
+    outside it the activations are scaled first. Both must match the oracle."""
+    out = []
+    j = k // 5
+    for edge in (2.0 ** 40, 2.0 ** -40):
+        for name, v in (("at", edge), ("outside", np.nextafter(np.float32(edge), np.float32(np.inf if edge > 1 else 0)))):
+            g = rng.uniform(0.5, 1.0, k).astype(np.float32)
+            g[j] = 1.0
+            base = synth.activations(rng, k)
+            x = (base * np.float32(edge / 2 / np.abs(base).max())).astype(np.float32)   # |x g| <= edge / 2
+            x[j] = np.float32(v)
+            out.append(("%s %g" % (name, edge), x, g))
+    return out
+
+
+@pytest.mark.parametrize("qtype,n,k", [(Q4, 2048, 2048), (Q8, 515, 8192), (Q4, 64, 32768)])
+def test_rmsnorm_fold_scaling_path_boundary(qtype, n, k):
+    rng = np.random.default_rng(7 * n + k)
+    w = synth.weights(rng, qtype, n, k)
+    qs, d = packed(gq, qtype, w, n, k)
+    fn = gq.qmv_q8_0_ex if qtype == Q8 else gq.qmv_q4_0_ex
+    for name, x, g in _boundary_cases(rng, k):
+        y = down(fn(qs, d, n, k, up(x), norm_weight=up(g), norm_eps=1e-6))
+        yr, ar = oracle.matvec(qtype, w, n, k, oracle.rmsnorm(x, g, 1e-6))
+        check_within(y, yr, oracle.fp32_path_bound(ar), "rmsnorm boundary %s type %d %dx%d" % (name, qtype, n, k))
+
+
+def test_rmsnorm_fold_ffn_scaling_path_boundary():
+    n_ff, k = 1024, 2048
+    rng = np.random.default_rng(17)
+    wg, wu = synth.q4_0_weights(rng, n_ff, k), synth.q4_0_weights(rng, n_ff, k)
+    gw, uw = packed(gq, Q4, wg, n_ff, k), packed(gq, Q4, wu, n_ff, k)
+    for name, x, g in _boundary_cases(rng, k):
+        h = down(gq.qffn_gate_up_gelu_ex(gw[0], gw[1], uw[0], uw[1], n_ff, k, up(x), norm_weight=up(g),
+                                         norm_eps=1e-6))
+        ref = oracle.ffn_gate_up(Q4, wg, wu, n_ff, k, oracle.rmsnorm(x, g, 1e-6))
+        check_within(h, ref["h"], oracle.ffn_h_bound(ref["g"], ref["u"], ref["ag"], ref["au"], ref["h"]),
+                     "ffn rmsnorm boundary " + name)
+
+
 @pytest.mark.parametrize("n_ff,k", [(1024, 2048), (300, 8192)])
 def test_rmsnorm_fold_ffn_and_vocab_head_full_range(n_ff, k):
     rng = np.random.default_rng(3 * n_ff + k)
