@@ -136,8 +136,13 @@ class TimingEvent:
         return ms.value
 
     def __del__(self):
-        if self.ev:
-            _hip_runtime().hipEventDestroy(self.ev)
+        # (at interpreter exit the module globals may already be gone; the
+        # runtime frees its events with the process then)
+        try:
+            if self.ev and _hip is not None:
+                _hip.hipEventDestroy(self.ev)
+        except Exception:
+            pass
 
 
 # ----------------------------------------------------------------------------
