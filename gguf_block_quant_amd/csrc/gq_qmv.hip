@@ -109,6 +109,7 @@ struct QmvParams {
     int8_t* xq_out;         // integer path quantising x itself: optional codes out [k]
     uint16_t* xd_out;       // ... and scales out [k/32] (written by workgroup 0)
     float norm_eps;
+    double inv_k;           // 1 / k (the RMSNorm mean's divisor)
     float softcap;          // > 0: output = softcap * tanh(output / softcap)
     int n;
     int k;
@@ -432,8 +433,20 @@ void qmv_kernel(const QmvParams p) {
     float dxr[NI];
     int sxr[NI];
     double ss = 0.0;
+    // inv = (sum / k + eps)^(-1/2): the hardware reciprocal square root (good
+    // to about 2^-24) and one Newton step in fp64 (to about 2^-47; the
+    // callers round to fp32). The divide and correctly rounded square root
+    // of 1/sqrt(sum/k + eps) cost every wave a long fp64 sequence, about a
+    // microsecond for the 2 x 8192 x 2048 FFN's 16 waves per CU. The mean is
+    // 0 (x all zero with eps 0: inv = +Inf, as 1/sqrt(0)) or at least 2^-313
+    // (the square of the smallest fp32 subnormal over k <= 32768), far from
+    // the fp64 subnormals where the approximation weakens.
     auto norm_scale = [&](double sum) {
-        return 1.0 / sqrt(sum / static_cast<double>(p.k) + static_cast<double>(p.norm_eps));
+        const double a = fma(sum, p.inv_k, static_cast<double>(p.norm_eps));
+        const double y0 = __builtin_amdgcn_rsq(a);
+        const double h = a * y0;
+        const double y1 = fma(0.5 * y0, fma(-h, y0, 1.0), y0);
+        return (a > 0.0 && a < __builtin_inf()) ? y1 : y0;
     };
     auto scaled = [](float v, double s) { return static_cast<float>(static_cast<double>(v) * s); };
     // RMSNorm: when every |x_i w_i| lies in [2^-40, 2^40] (the usual case;
@@ -990,6 +1003,7 @@ QmvParams base_params(const void* qs, const uint16_t* d, int64_t n, int64_t k, i
     p.units = static_cast<int>(k / 32 * bytes_per_32 / 16);
     p.nb = static_cast<int>(k / 32);
     p.k = static_cast<int>(k);
+    p.inv_k = 1.0 / static_cast<double>(k);
     return p;
 }
 
