@@ -177,7 +177,8 @@ int gq_qmv_q4_0(const uint8_t *qs, const uint16_t *d, int64_t n, int64_t k,
  *    applied directly (SafeC Gemma 4 DESIGN_NOTES page, "RMSNorm"; Gemma 4
  *    uses norm_eps = 1e-6); norm_weight fp32 [k], 16-byte aligned;
  *    norm_eps >= 0 and finite, else GQ_ERR_VALUE. The sum of squares is
- *    taken in fp64; the scale is applied to each finished row (an fp64
+ *    taken in fp64, and the scale (mean + norm_eps)^(-1/2) in fp64 to
+ *    within about 1e-14 relative; the scale is applied to each finished row (an fp64
  *    product) when every |x[c] * norm_weight[c]| lies in [2^-40, 2^40],
  *    and otherwise to the activations before the products, so any finite
  *    x is supported as long as every product x[c] * norm_weight[c] is
