@@ -56,6 +56,55 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
+// gfx950 lane swaps: v_permlane32_swap_b32 exchanges the upper 32 lanes of
+// a with the lower 32 lanes of b, v_permlane16_swap_b32 the odd 16-lane rows
+// of a with the even rows of b; each returns both registers. The returned
+// pair is reinterpreted as a whole: a bit cast of one element of the
+// returned integer vector has compiled to a read of its first element.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x2_t swap_halves(float a, float b) {
+    return __builtin_bit_cast(f32x2_t, __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a),
+                                                                         __builtin_bit_cast(uint32_t, b), false, false));
+}
+__device__ __forceinline__ f32x2_t swap_rows(float a, float b) {
+    return __builtin_bit_cast(f32x2_t, __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a),
+                                                                         __builtin_bit_cast(uint32_t, b), false, false));
+}
+// Lane i plus lane i + 32: lanes 0..31 receive a's sums, lanes 32..63 b's.
+__device__ __forceinline__ float fold_halves(float a, float b) {
+    const f32x2_t t = swap_halves(a, b);
+    return t.x + t.y;
+}
+// Row 2j plus row 2j + 1 (rows of 16 lanes): rows 0 and 2 receive a's sums
+// (of rows 0 + 1 and 2 + 3), rows 1 and 3 b's.
+__device__ __forceinline__ float fold_rows(float a, float b) {
+    const f32x2_t t = swap_rows(a, b);
+    return t.x + t.y;
+}
+// Sum over the 16 lanes of each row, identical in every lane of the row.
+__device__ __forceinline__ float row_sum(float v) {
+    v += dpp_f32<kDppQuadSwap1>(v);
+    v += dpp_f32<kDppQuadSwap2>(v);
+    v += dpp_f32<kDppRowHalfMirror>(v);
+    v += dpp_f32<kDppRowMirror>(v);
+    return v;
+}
+// Four sums over the 64 lanes at once, transposed: every lane of row q
+// receives the sum of value ((q & 1) << 1) | (q >> 1) of (a0, a1, a2, a3),
+// i.e. rows 0..3 hold the sums of a0, a2, a1, a3 -- two lane-half swaps,
+// one row swap and four DPP adds where four separate sums take 16 DPP adds
+// and 16 lane reads. Every value is summed in the same fixed order (lanes
+// i + i+32, then rows 0+1 / 2+3, then the butterfly in the row), so the
+// result is reproducible.
+__device__ __forceinline__ float wave_sum4_rows(float a0, float a1, float a2, float a3) {
+    return row_sum(fold_rows(fold_halves(a0, a1), fold_halves(a2, a3)));
+}
+// One sum over the 64 lanes in the same order, in every lane.
+__device__ __forceinline__ float wave_sum_swapped(float a) {
+    const float h = fold_halves(a, a);
+    return row_sum(fold_rows(h, h));
+}
+
 // Sum of a double over the 64 lanes of the wave, in every lane: the same
 // pairing and order as wave_sum (each DPP step moves the two 32-bit halves),
 // so the result is reproducible and identical in every lane -- and the same

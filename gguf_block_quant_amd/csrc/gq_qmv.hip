@@ -11,7 +11,8 @@
 //    workgroup first stages all of x in LDS (one read of x per workgroup).
 //  * A wave streams R rows per step (R x NI independent 16-byte loads in
 //    flight per lane), dequantises and dot-reduces in registers, and sums
-//    the lanes with DPP (wave_sum), fixed order, no atomics. The next row
+//    the lanes of all the group's rows at once with lane-half and row swaps
+//    and DPP (wave_sum4_rows), fixed order, no atomics. The next row
 //    group's loads go out after the current group's dot, into the same
 //    registers.
 //  * Long rows (large k) are split over WS waves of the workgroup; their
@@ -668,9 +669,25 @@ void qmv_kernel(const QmvParams p) {
     // holds row r), loaded when its group's dot starts -- in flight during the
     // dot rather than a memory round trip after it
     float resv = 0.f;
+    // The row group's NMAT * R sums are reduced over the wave together
+    // (wave_sum4_rows): four of them leave 16-lane row q holding value
+    // ((q & 1) << 1) | (q >> 1), value v being acc[v / R][v % R]. So the
+    // lane that finishes a row is lane 16 q for four rows (and for the
+    // gate+up pass at 4 row pairs, which reduces gates and ups separately);
+    // lane 32 r for the gate+up pass at 2 row pairs (a row swap pairs each
+    // gate with its up); lane 0 for one row; and lane r of slice 0 for split
+    // rows, which add the slices' sums in LDS.
+    constexpr int kV = NMAT * R;
+    static_assert(kV == 1 || kV == 4 || (kV == 8 && NMAT == 2), "1, 4 or 2 x 4 sums per row group");
+    auto lane_row = [&](int l) -> int {
+        if constexpr (WS > 1) return l % R;
+        else if constexpr (kV == 1) return 0;
+        else if constexpr (kV == 4 && NMAT == 2) return l >> 5;
+        else return (((l >> 4) & 1) << 1) | (l >> 5);
+    };
     auto load_res = [&](int r0) {
         if constexpr (FOLD) {
-            if (p.residual != nullptr) resv = p.residual[min(r0 + lane % R, p.n - 1)];
+            if (p.residual != nullptr) resv = p.residual[min(r0 + lane_row(lane), p.n - 1)];
         }
     };
     auto post_scale = [&](float v) {
@@ -731,50 +748,48 @@ void qmv_kernel(const QmvParams p) {
     // ---- cross-lane and cross-wave reduction, epilogue and store --------
     __shared__ float lpart[WAVES][NMAT][R];
     auto finish_group = [&](float (&acc)[NMAT][R], int r0) {
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-            for (int r = 0; r < R; ++r) acc[m][r] = wave_sum(acc[m][r]);
+        float t0, t1 = 0.f;
+        if constexpr (kV == 1) {
+            t0 = wave_sum_swapped(acc[0][0]);
+        } else if constexpr (kV == 4) {
+            t0 = wave_sum4_rows(acc[0][0], acc[1 / R][1 % R], acc[2 / R][2 % R], acc[3 / R][3 % R]);
+        } else {
+            t0 = wave_sum4_rows(acc[0][0], acc[0][1 % R], acc[0][2 % R], acc[0][3 % R]);
+            t1 = wave_sum4_rows(acc[NMAT - 1][0], acc[NMAT - 1][1 % R], acc[NMAT - 1][2 % R], acc[NMAT - 1][3 % R]);
+        }
+        const int q = lane >> 4;
+        const int vq = ((q & 1) << 1) | (q >> 1);     // the value row q holds
 
         if constexpr (WS == 1) {
-            // The gate+up pass and the folded variants: lane r finishes row
-            // r of the group (the reduced sums are wave-uniform), so the R
-            // rows' epilogues -- GELU, soft cap, argmax key -- run side by
-            // side (measured: gate+up 5.91 -> 5.63 us, the fused vocab head
-            // 90.8 -> 88.9 us). The plain matvec keeps one lane storing its
-            // R rows (85.4 vs 86.0 us for the vocab head).
-            constexpr bool kLaneRows = MODE == kFFN || FOLD;
-            if constexpr (kLaneRows) {
-                if (lane < R) {
-                    float a0 = acc[0][0], a1 = acc[NMAT - 1][0];
-#pragma unroll
-                    for (int r = 1; r < R; ++r) {
-                        a0 = lane == r ? acc[0][r] : a0;
-                        a1 = lane == r ? acc[NMAT - 1][r] : a1;
-                    }
-                    a0 = post_scale(a0);
-                    a1 = post_scale(a1);
-                    const int row = r0 + lane;
-                    if (row < p.n) {
-                        if constexpr (MODE == kFFN)
-                            emit(row, gelu_tanh(a0) * a1);
-                        else
-                            emit(row, a0);
-                    }
+            // The rows' epilogues -- GELU, soft cap, argmax key -- run side
+            // by side in their finishing lanes.
+            if constexpr (kV == 4 && NMAT == 2) {
+                // rows hold g0, u0, g1, u1: one row swap gives lanes 0..31
+                // (g0, u0) and lanes 32..63 (g1, u1)
+                const f32x2_t gu = swap_rows(t0, t0);
+                if ((lane & 31) == 0) {
+                    const int row = r0 + (lane >> 5);
+                    if (row < p.n) emit(row, gelu_tanh(post_scale(gu.x)) * post_scale(gu.y));
                 }
-            } else if (lane == 0) {
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int row = r0 + r;
-                    if (row < p.n) emit(row, acc[0][r]);
+            } else if constexpr (kV == 8) {
+                if ((lane & 15) == 0) {
+                    const int row = r0 + vq;
+                    if (row < p.n) emit(row, gelu_tanh(post_scale(t0)) * post_scale(t1));
                 }
+            } else if ((lane & 15) == 0 && (kV == 4 || lane == 0)) {
+                const int row = r0 + (kV == 1 ? 0 : vq);
+                if (row < p.n) emit(row, post_scale(t0));
             }
         } else {
-            if (lane == 0) {
-#pragma unroll
-                for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                    for (int r = 0; r < R; ++r) lpart[wave][m][r] = acc[m][r];
+            if ((lane & 15) == 0 && (kV != 1 || lane == 0)) {
+                if constexpr (kV == 1) {
+                    lpart[wave][0][0] = t0;
+                } else if constexpr (kV == 4) {
+                    lpart[wave][vq / R][vq % R] = t0;
+                } else {
+                    lpart[wave][0][vq] = t0;
+                    lpart[wave][NMAT - 1][vq] = t1;
+                }
             }
             __syncthreads();
             if (slice == 0 && lane < R) {

@@ -70,16 +70,18 @@ def test_residual_epilogue_and_in_place(qtype, n, k):
                           down(_ex(qtype)(qs, d, n, k, up(x))).view(np.uint32))
 
 
-@pytest.mark.parametrize("n_ff,k", [(8192, 2048), (1056, 8192)])
+@pytest.mark.parametrize("n_ff,k", [(8192, 2048), (1056, 8192), (65539, 2048)])   # the last: tall shape
 def test_ffn_rmsnorm_prologue(n_ff, k):
-    wl = synth.workload_ffn(seed=5, n_ff=n_ff, k=k)
-    rng = np.random.default_rng(6)
-    gw = rng.uniform(0.5, 1.5, k).astype(np.float32)
-    gt = packed(gq, Q4, wl["wg"], n_ff, k)
-    ut = packed(gq, Q4, wl["wu"], n_ff, k)
-    h = down(gq.qffn_gate_up_gelu_ex(gt[0], gt[1], ut[0], ut[1], n_ff, k, up(wl["x"]),
-                                     norm_weight=up(gw), norm_eps=EPS))
-    ref = oracle.ffn_gate_up(Q4, wl["wg"], wl["wu"], n_ff, k, oracle.rmsnorm(wl["x"], gw, EPS))
+    # gate, up and x only (no down matrix: n_ff need not be a whole number of blocks)
+    rng = np.random.default_rng(5)
+    wg = synth.q4_0_weights(rng, n_ff, k)
+    wu = synth.q4_0_weights(rng, n_ff, k)
+    x = synth.activations(rng, k)
+    gw = np.random.default_rng(6).uniform(0.5, 1.5, k).astype(np.float32)
+    gt = packed(gq, Q4, wg, n_ff, k)
+    ut = packed(gq, Q4, wu, n_ff, k)
+    h = down(gq.qffn_gate_up_gelu_ex(gt[0], gt[1], ut[0], ut[1], n_ff, k, up(x), norm_weight=up(gw), norm_eps=EPS))
+    ref = oracle.ffn_gate_up(Q4, wg, wu, n_ff, k, oracle.rmsnorm(x, gw, EPS))
     check_within(h, ref["h"], oracle.ffn_h_bound(ref["g"], ref["u"], ref["ag"], ref["au"], ref["h"]), "ffn norm")
 
 

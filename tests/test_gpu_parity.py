@@ -300,10 +300,12 @@ def test_ffn_stage_by_stage(n_ff, k):
     check_within(y, ye, Wd @ hb + oracle.fp32_path_bound(ae), "end to end")
 
 
-@pytest.mark.parametrize("n_ff,k", [(1001, 2048), (77, 8192), (45, 16384), (3, 32768)])
+@pytest.mark.parametrize("n_ff,k", [(1001, 2048), (77, 8192), (45, 16384), (3, 32768), (65539, 2048)])
 def test_ffn_gate_up_ragged_rows(n_ff, k):
     """Gate+up alone at row counts that leave row groups (and, for split
-    rows, the second row group of a workgroup) partly or wholly past the end."""
+    rows, the second row group of a workgroup) partly or wholly past the end;
+    65539 rows take the tall shape (four row pairs per wave step, their gate
+    and up sums reduced as two transposed sets of four)."""
     rng = np.random.default_rng(n_ff + k)
     wg = synth.q4_0_weights(rng, n_ff, k)
     wu = synth.q4_0_weights(rng, n_ff, k)
