@@ -34,7 +34,8 @@
 // The lane's 32 activations stay in VGPRs for every row it streams. Rows
 // longer than 2048 elements are split over WS waves whose partial sums meet
 // in LDS in slice order; waves stream R rows per step; sums over lanes use
-// DPP (wave_sum_last_row), fixed order, no atomics.
+// lane-half and row swaps and DPP (wave_sum4_rows; at other step sizes
+// wave_sum_last_row), fixed order, no atomics.
 #include <atomic>
 
 #include "gq_device.hpp"
@@ -292,6 +293,27 @@ void qmv_q4_k_kernel(const KqParams p) {
     const half2_t off_lo = {static_cast<_Float16>(-1024.0f), static_cast<_Float16>(-1024.0f)};
 
     __shared__ float lpart[WAVES][R];
+    // four rows per step: their sums reduced over the wave together
+    // (wave_sum4_rows), 16-lane row q finishing row ((q & 1) << 1) | (q >> 1)
+    // of the step
+    auto finish4 = [&](const float (&acc)[R], int r0) {
+        const float t = wave_sum4_rows(acc[0], acc[1 % R], acc[2 % R], acc[3 % R]);
+        const int q = lane >> 4;
+        const int vq = ((q & 1) << 1) | (q >> 1);
+        if constexpr (WS == 1) {
+            if ((lane & 15) == 0 && r0 + vq < p.n) p.y[r0 + vq] = t;
+        } else {
+            if ((lane & 15) == 0) lpart[wave][vq % R] = t;
+            __syncthreads();
+            if (slice == 0 && lane < R) {
+                float tt = lpart[wave][lane];
+#pragma unroll
+                for (int sl = 1; sl < WS; ++sl) tt += lpart[wave + sl][lane];
+                if (r0 + lane < p.n) p.y[r0 + lane] = tt;
+            }
+            __syncthreads();
+        }
+    };
     for (int it = blockIdx.x; it * SUBS < p.row_groups; it += gridDim.x) {
         const int r0 = (it * SUBS + sub) * R;
         uint4 q[R], h[R];
@@ -339,6 +361,10 @@ void qmv_q4_k_kernel(const KqParams p) {
             const float t2 = fmaf(mnb, sxb, mna * sxa);
             const float pm = fmaf(static_cast<float>(dh.y), t2, 0.f);
             acc[r] = fmaf(static_cast<float>(dh.x), t1, -pm);
+        }
+        if constexpr (R == 4) {
+            finish4(acc, r0);
+            continue;
         }
         // the row sums are complete in lanes 48..63: lane 64 - R + r stores row r
 #pragma unroll
@@ -402,6 +428,27 @@ void qmv_q6_k_kernel(const KqParams p) {
     const half2_t off_hi = {static_cast<_Float16>(-1536.0f), static_cast<_Float16>(-1536.0f)};
 
     __shared__ float lpart[WAVES][R];
+    // four rows per step: their sums reduced over the wave together
+    // (wave_sum4_rows), 16-lane row q finishing row ((q & 1) << 1) | (q >> 1)
+    // of the step
+    auto finish4 = [&](const float (&acc)[R], int r0) {
+        const float t = wave_sum4_rows(acc[0], acc[1 % R], acc[2 % R], acc[3 % R]);
+        const int q = lane >> 4;
+        const int vq = ((q & 1) << 1) | (q >> 1);
+        if constexpr (WS == 1) {
+            if ((lane & 15) == 0 && r0 + vq < p.n) p.y[r0 + vq] = t;
+        } else {
+            if ((lane & 15) == 0) lpart[wave][vq % R] = t;
+            __syncthreads();
+            if (slice == 0 && lane < R) {
+                float tt = lpart[wave][lane];
+#pragma unroll
+                for (int sl = 1; sl < WS; ++sl) tt += lpart[wave + sl][lane];
+                if (r0 + lane < p.n) p.y[r0 + lane] = tt;
+            }
+            __syncthreads();
+        }
+    };
     for (int it = blockIdx.x; it * SUBS < p.row_groups; it += gridDim.x) {
         const int r0 = (it * SUBS + sub) * R;
         uint4 ql[R];
@@ -460,6 +507,10 @@ void qmv_q6_k_kernel(const KqParams p) {
             const float sh = static_cast<float>(static_cast<int8_t>(s01 >> 8));
             const float dd = valid ? half_bits_to_float(static_cast<uint16_t>(dbits)) : 0.f;
             acc[r] = dd * fmaf(sh * 0.0625f, phi, sl * plo);
+        }
+        if constexpr (R == 4) {
+            finish4(acc, r0);
+            continue;
         }
         // the row sums are complete in lanes 48..63: lane 64 - R + r stores row r
 #pragma unroll
