@@ -725,10 +725,16 @@ void qmv_kernel(const QmvParams p) {
                     // right after the staging, waiting there for every load
                     uint32_t dbits = dd[i][m][r];
                     asm volatile("" : "+v"(dbits));
-                    const float dw = uvalid[i] ? half_bits_to_float(static_cast<uint16_t>(dbits)) : 0.f;
                     if constexpr (MODE != kQ8X) {
-                        acc[m][r] = fmaf(dw, unit_dot_f32<TYPE>(qd[i][m][r], xr[i]), acc[m][r]);
+                        // the binary16 scale enters the FMA as it is
+                        // (v_fma_mix_f32: the same single rounding as after
+                        // an exact conversion); lanes past the row take +0
+                        uint32_t hb = uvalid[i] ? dbits : 0u;
+                        asm volatile("" : "+v"(hb));     // keeps the select on the bits
+                        acc[m][r] = fmaf(half_bits_to_float(static_cast<uint16_t>(hb)),
+                                         unit_dot_f32<TYPE>(qd[i][m][r], xr[i]), acc[m][r]);
                     } else {
+                        const float dw = uvalid[i] ? half_bits_to_float(static_cast<uint16_t>(dbits)) : 0.f;
                         int s = unit_dot_q8<TYPE>(qd[i][m][r], xqr[i], sxr[i]);
                         if constexpr (TYPE == kTypeQ8_0) {
                             // a block is two adjacent lanes' units: S_b = s(2t) + s(2t+1)
