@@ -243,7 +243,13 @@ void qmv_kernel(const QmvParams p) {
     // the pinned loop, the un-split one-group matvecs (2048 x 2048) do not.
     constexpr bool kManyGroups = (WS == 1 && R == GQ_QMV_R_TALL);
     constexpr bool kPinned = kManyGroups || MODE == kFFN || WS > 1;
-    const int wave = kManyGroups ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave)
+    // The plain split-row kernels (2 to 8 waves per row) take the scalar wave
+    // index too (measured: down projection 2048 x 8192 4.25 -> 4.07 us,
+    // 2048 x 16384 7.77 -> 7.64 us); the 16-wave split, the folded variants
+    // and the un-split gate+up pass measured slower with it (11.6 -> 11.75,
+    // 2048 x 2048 RMSNorm 3.18 -> 3.36, gate+up 5.3 -> 5.5 us).
+    constexpr bool kScalarWave = kManyGroups || (WS > 1 && WS < 16 && !FOLD);
+    const int wave = kScalarWave ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave)
                                  : static_cast<int>(threadIdx.x) / kWave;
     const int slice = wave % WS;
     const int sub = wave / WS;
