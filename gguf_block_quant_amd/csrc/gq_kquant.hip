@@ -42,8 +42,10 @@
 #include "gq_launch.hpp"
 
 // Measured on MI355X (fp32 x, k = 2048; 262144 / 8192 rows, and 2048 x 8192):
-// 4 rows per step with up to 2048 workgroups: Q4_K 58.2-58.5 / 4.9-5.2 /
-// 5.2-5.3 us, Q6_K 74.2-74.3 / 5.6-5.8 / 5.8 us (with the packed fields
+// 4 rows per step with up to 2048 workgroups: Q4_K 56.5-57.6 / 4.6-5.0 /
+// 5.0-5.1 us, Q6_K 73.6-74.9 / 5.4-5.6 / 5.7-5.8 us with the four rows
+// summed over the lanes together (58.2-58.5 / 4.9-5.2 / 5.2-5.3 and
+// 74.2-74.3 / 5.6-5.8 / 5.8 us one row at a time; with the packed fields
 // read directly; the byte-copy layout, unpacking the GGUF fields in the
 // loop, gave 60-62 / 5.3 / 5.6 and 82-84 / 6.0-6.2 / 5.5-5.8 us); 2 rows at
 // 1024 workgroups were slower. Two row groups in flight per wave (a second
