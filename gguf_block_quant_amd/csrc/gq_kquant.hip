@@ -368,7 +368,8 @@ void qmv_q4_k_kernel(const KqParams p) {
             finish4(acc, r0);
             continue;
         }
-        // the row sums are complete in lanes 48..63: lane 64 - R + r stores row r
+        // (other step sizes) the row sums are complete in lanes 48..63:
+        // lane 64 - R + r stores row r
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = wave_sum_last_row(acc[r]);
         if constexpr (WS == 1) {
@@ -514,7 +515,8 @@ void qmv_q6_k_kernel(const KqParams p) {
             finish4(acc, r0);
             continue;
         }
-        // the row sums are complete in lanes 48..63: lane 64 - R + r stores row r
+        // (other step sizes) the row sums are complete in lanes 48..63:
+        // lane 64 - R + r stores row r
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = wave_sum_last_row(acc[r]);
         if constexpr (WS == 1) {

@@ -671,9 +671,9 @@ void qmv_kernel(const QmvParams p) {
 
     // ---- epilogue of one finished row: residual, soft cap, store, argmax --
     unsigned long long best = 0ull;
-    // the residual of the row this lane finishes (lane r of the row group
-    // holds row r), loaded when its group's dot starts -- in flight during the
-    // dot rather than a memory round trip after it
+    // the residual of the row this lane finishes (lane_row below), loaded
+    // when its group's dot starts -- in flight during the dot rather than a
+    // memory round trip after it
     float resv = 0.f;
     // The row group's NMAT * R sums are reduced over the wave together
     // (wave_sum4_rows): four of them leave 16-lane row q holding value
