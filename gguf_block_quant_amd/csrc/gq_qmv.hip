@@ -550,17 +550,21 @@ void qmv_kernel(const QmvParams p) {
             const float* xs = &xstage[unit[i] * kPitch];
 #pragma unroll
             for (int v = 0; v < EPU / 4; ++v) {
-                float4 t = *reinterpret_cast<const float4*>(xs + 4 * v);
-                if constexpr (FOLD) {
-                    if (norm && !post) {
-                        t.x = scaled(t.x, inv); t.y = scaled(t.y, inv);
-                        t.z = scaled(t.z, inv); t.w = scaled(t.w, inv);
-                    }
-                }
+                const float4 t = *reinterpret_cast<const float4*>(xs + 4 * v);
                 xr[i][4 * v + 0] = t.x; xr[i][4 * v + 1] = t.y;
                 xr[i][4 * v + 2] = t.z; xr[i][4 * v + 3] = t.w;
             }
             dxr[i] = 0.f; sxr[i] = 0;
+        }
+        // the scale on the activations (the rare path) after all the LDS
+        // reads: a branch per read made each wait for its own LDS round trip
+        if constexpr (FOLD) {
+            if (norm && !post) {
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+#pragma unroll
+                    for (int e = 0; e < EPU; ++e) xr[i][e] = scaled(xr[i][e], inv);
+            }
         }
     } else {
         if constexpr (kQuantX) {
