@@ -420,8 +420,43 @@ void qmv_kernel(const QmvParams p) {
     // activation waits above exact)
     // keep the scheduler from hoisting the weight loads above the activation
     // loads (the point of the order above)
+    // The row group's NMAT * R sums are reduced over the wave together
+    // (wave_sum4_rows): four of them leave 16-lane row q holding value
+    // ((q & 1) << 1) | (q >> 1), value v being acc[v / R][v % R]. So the
+    // lane that finishes a row is lane 16 q for four rows (and for the
+    // gate+up pass at 4 row pairs, which reduces gates and ups separately);
+    // lane 32 r for the gate+up pass at 2 row pairs (a row swap pairs each
+    // gate with its up); lane 0 for one row; and lane r of slice 0 for split
+    // rows, which add the slices' sums in LDS.
+    constexpr int kV = NMAT * R;
+    static_assert(kV == 1 || kV == 4 || (kV == 8 && NMAT == 2), "1, 4 or 2 x 4 sums per row group");
+    auto lane_row = [&](int l) -> int {
+        if constexpr (WS > 1) return l % R;
+        else if constexpr (kV == 1) return 0;
+        else if constexpr (kV == 4 && NMAT == 2) return l >> 5;
+        else return (((l >> 4) & 1) << 1) | (l >> 5);
+    };
+    // The residual of the row this lane finishes goes out just before its
+    // row group's weights: loads complete in issue order, so the wait for
+    // the weights covers it (issued after them, it had held up every dot).
+    // The load is unconditional -- without a residual it reads (and ignores)
+    // x[0], which every workgroup reads anyway (y[0] if there were no x): a
+    // load on one path only makes the compiler count the loads before it for
+    // the shorter path, so the prologue's wait for x would also have waited
+    // for the residual (2048 x 2048 RMSNorm + residual 3.12 -> 2.6 us).
+    // (A dummy read of y's own rows measured 0.25 us slower.)
+    float resv = 0.f, resv_next = 0.f;
+    auto load_res = [&](float& dst, int r0) {
+        if constexpr (FOLD) {
+            const float* src = p.residual != nullptr ? p.residual + min(r0 + lane_row(lane), p.n - 1)
+                                                     : (p.x != nullptr ? p.x : p.y);
+            dst = *src;
+        }
+    };
+
     __builtin_amdgcn_sched_barrier(0);
     int it = blockIdx.x;
+    load_res(resv, (it * SUBS + sub) * R);
     load_group(q, db, (it * SUBS + sub) * R);
 
     // ---- activation registers for this lane's units ----------------------
@@ -675,31 +710,6 @@ void qmv_kernel(const QmvParams p) {
 
     // ---- epilogue of one finished row: residual, soft cap, store, argmax --
     unsigned long long best = 0ull;
-    // the residual of the row this lane finishes (lane_row below), loaded
-    // when its group's dot starts -- in flight during the dot rather than a
-    // memory round trip after it
-    float resv = 0.f;
-    // The row group's NMAT * R sums are reduced over the wave together
-    // (wave_sum4_rows): four of them leave 16-lane row q holding value
-    // ((q & 1) << 1) | (q >> 1), value v being acc[v / R][v % R]. So the
-    // lane that finishes a row is lane 16 q for four rows (and for the
-    // gate+up pass at 4 row pairs, which reduces gates and ups separately);
-    // lane 32 r for the gate+up pass at 2 row pairs (a row swap pairs each
-    // gate with its up); lane 0 for one row; and lane r of slice 0 for split
-    // rows, which add the slices' sums in LDS.
-    constexpr int kV = NMAT * R;
-    static_assert(kV == 1 || kV == 4 || (kV == 8 && NMAT == 2), "1, 4 or 2 x 4 sums per row group");
-    auto lane_row = [&](int l) -> int {
-        if constexpr (WS > 1) return l % R;
-        else if constexpr (kV == 1) return 0;
-        else if constexpr (kV == 4 && NMAT == 2) return l >> 5;
-        else return (((l >> 4) & 1) << 1) | (l >> 5);
-    };
-    auto load_res = [&](int r0) {
-        if constexpr (FOLD) {
-            if (p.residual != nullptr) resv = p.residual[min(r0 + lane_row(lane), p.n - 1)];
-        }
-    };
     auto post_scale = [&](float v) {
         if constexpr (FOLD) return post ? scaled(v, post_inv) : v;
         else return v;
@@ -840,7 +850,6 @@ void qmv_kernel(const QmvParams p) {
             const int r0 = (it * SUBS + sub) * R;
             const int itn = it + gridDim.x;
             const bool more = itn * SUBS < p.row_groups;
-            load_res(r0);
             float acc[NMAT][R];
             dot_group(q, db, r0, acc);
             // pin the order: the dot is finished (its results pass through
@@ -852,9 +861,13 @@ void qmv_kernel(const QmvParams p) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) asm volatile("" : "+v"(acc[m][r]));
             asm volatile("" ::: "memory");
-            if (more) load_group(q, db, (itn * SUBS + sub) * R);
+            if (more) {
+                load_res(resv_next, (itn * SUBS + sub) * R);
+                load_group(q, db, (itn * SUBS + sub) * R);
+            }
             finish_group(acc, r0);
             if (!more) break;
+            resv = resv_next;
             it = itn;
         }
     } else {
@@ -862,11 +875,14 @@ void qmv_kernel(const QmvParams p) {
         for (; it * SUBS < p.row_groups; it += gridDim.x) {
             const int r0 = (it * SUBS + sub) * R;
             const int itn = it + gridDim.x;
-            load_res(r0);
             float acc[NMAT][R];
             dot_group(q, db, r0, acc);
-            if (itn * SUBS < p.row_groups) load_group(q, db, (itn * SUBS + sub) * R);
+            if (itn * SUBS < p.row_groups) {
+                load_res(resv_next, (itn * SUBS + sub) * R);
+                load_group(q, db, (itn * SUBS + sub) * R);
+            }
             finish_group(acc, r0);
+            resv = resv_next;
         }
     }
 
