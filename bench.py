@@ -417,6 +417,30 @@ def per_config(step, ceiling_gbps, log, rotate_bytes=2 << 30):
         rows.append(("C5 qmm_tile_m 8192x2048 M=%d" % m, 9437184, m * 2176 + m * 8192 * 4,
                      [(L.gq_qmm_tile_m, (P(q), P(d), 8192, 2048, m, P(acts[m][0]), P(acts[m][1]), P(yt[m]), None,
                                          sp)) for q, d in w5]))
+    # the folds around a projection and the fused vocabulary head (RMSNorm
+    # prologue, residual epilogue; soft cap and the two-stage greedy argmax),
+    # on the same rotated weights as their plain rows above
+    rngf = np.random.default_rng(1)
+    gf = up(rngf.uniform(0.5, 1.5, 2048).astype(np.float32))
+    resf = up(rngf.standard_normal(2048).astype(np.float32))
+    y2f, h3f = torch.empty(2048, dtype=torch.float32, device=dev), torch.empty(8192, dtype=torch.float32, device=dev)
+    logitsf = torch.empty(262144, dtype=torch.float32, device=dev)
+    wsf = torch.zeros(gq.argmax_workspace_bytes(), dtype=torch.uint8, device=dev)
+    idxf, valf = torch.empty(1, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.float32, device=dev)
+    eps = ctypes.c_float(1e-6)
+    rows.append(("F1 qmv_q4_0_ex 2048x2048 (rmsnorm + residual)", 2359296, 3 * 8192 + 8192,
+                 [(L.gq_qmv_q4_0_ex, (P(q), P(d), 2048, 2048, P(x2), P(gf), eps, P(resf), P(y2f), sp))
+                  for q, d in w2]))
+    rows.append(("F1 qffn_gate_up_gelu_ex 2x8192x2048 (rmsnorm)", 2 * 9437184, 2 * 8192 + 32768,
+                 [(L.gq_qffn_gate_up_gelu_ex, (P(g[0]), P(g[1]), P(u[0]), P(u[1]), 8192, 2048, P(x3), P(gf), eps,
+                                               P(h3f), sp)) for g, u in zip(wg, wu)]))
+    rows.append(("F2 qmv_q8_0_argmax 262144x2048 (rmsnorm + softcap 30 + argmax, two launches)", 570425344,
+                 2 * 8192 + 4 * 262144,
+                 [(L.gq_qmv_q8_0_argmax, (P(q), P(d), 262144, 2048, P(x4), P(gf), eps, ctypes.c_float(30.0),
+                                          P(logitsf), P(wsf), wsf.numel(), P(idxf), P(valf), sp))
+                  for q, d in step.vocab_sets]))
+    fold_keep = [gf, resf, y2f, h3f, logitsf, wsf, idxf, valf]
+
     # K-quant matvecs (fp32 x, k = 2048): the decode shapes, and a
     # vocabulary-sized matrix that streams from HBM at the steady rate
     def kq_copies(qtype, blocks, n, k, count):
@@ -438,7 +462,7 @@ def per_config(step, ceiling_gbps, log, rotate_bytes=2 << 30):
             rows.append(("K qmv_%s %dx2048" % (tname.lower(), n), wbytes, 8192 + 4 * n,
                          [(fn, (P(pk), n, 2048, P(xk), P(yk), sp)) for pk in kc]))
     keep = [w1, w2, wg, wu, wd, wds, w5, x1, y1, x2, y2, xq2, xd2, x3, h3, y3, x4, y4, y4s, h3s, y3s, acts, yt,
-            kq_keep]
+            kq_keep, fold_keep]
 
     def issue(launch):
         for fn, fargs in (launch if isinstance(launch[0], tuple) else (launch,)):
