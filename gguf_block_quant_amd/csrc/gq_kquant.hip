@@ -42,16 +42,17 @@
 #include "gq_launch.hpp"
 
 // Measured on MI355X (fp32 x, k = 2048; 262144 / 8192 rows, and 2048 x 8192):
-// 4 rows per step with up to 2048 workgroups: Q4_K 56.5-57.6 / 4.6-5.0 /
-// 5.0-5.1 us, Q6_K 73.6-74.9 / 5.4-5.6 / 5.7-5.8 us with the four rows
-// summed over the lanes together (58.2-58.5 / 4.9-5.2 / 5.2-5.3 and
-// 74.2-74.3 / 5.6-5.8 / 5.8 us one row at a time; with the packed fields
-// read directly; the byte-copy layout, unpacking the GGUF fields in the
-// loop, gave 60-62 / 5.3 / 5.6 and 82-84 / 6.0-6.2 / 5.5-5.8 us); 2 rows at
-// 1024 workgroups were slower. Two row groups in flight per wave (a second
-// register set) measured no better: the loop is bound by its VALU work
-// (about 2.1 instructions per element for the exact nibble dot, 3.0 per
-// element in all for Q4_K and 3.5 for Q6_K), not by load latency.
+// 4 rows per step with up to 2048 workgroups: Q4_K 52.2 / 4.5 / 4.7 us with
+// the nibbles read as binary16 subnormals (59.0 / 4.7 / 4.8 with the
+// normal-range form and its packed add), Q6_K 73.6-75.4 / 5.3-5.6 /
+// 5.4-5.8 us, with the four rows summed over the lanes together (one row
+// at a time was 2-3 % slower; with the packed fields read directly; the
+// byte-copy layout, unpacking the GGUF fields in the loop, gave 60-62 /
+// 5.3 / 5.6 and 82-84 / 6.0-6.2 / 5.5-5.8 us); 2 rows at 1024 workgroups
+// were slower. Two row groups in flight per wave (a second register set)
+// measured no better: the loop is bound by its VALU work (for the exact
+// nibble dot about 1.6 instructions per element in Q4_K and 2.8 in Q6_K;
+// 2.7 and 3.5 per element in all), not by load latency.
 #ifndef GQ_KQ_R
 #define GQ_KQ_R 4            // rows per wave step
 #endif
@@ -236,13 +237,18 @@ template <int WS> struct KqWaves { static constexpr int value = WS < 4 ? 4 : WS;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
-// Exact dequantisation of two 4-bit fields of a 32-bit word, held in the
-// low bits of its 16-bit halves (mask selects them), through the binary16
-// number 1024 + v built by OR-ing them under the exponent pattern in `magic`,
-// then one packed add of `off` (exact: every value involved is an integer
-// below 2048).
-__device__ __forceinline__ half2_t nib2(uint32_t w, uint32_t mask, uint32_t magic, half2_t off) {
-    return __builtin_bit_cast(half2_t, (w & mask) | magic) + off;
+constexpr float kTwoM24 = 5.9604644775390625e-08f;   // 2^-24
+constexpr float kTwo24 = 16777216.0f;               // 2^24
+
+// Two 4-bit fields of a 32-bit word, held in the low bits of its 16-bit
+// halves (mask selects them), read as binary16 numbers with a zero exponent
+// field: the subnormals v * 2^-24, exact, with no offset to take out.
+// v_fma_mix_f32 multiplies such a half by an fp32 activation with a single
+// rounding, as it does a normal one, so each product is the fp32 FMA of
+// (float) v scaled by 2^-24 (exact while the result stays above 2^-126; the
+// row sums are scaled back by 2^24 at the end).
+__device__ __forceinline__ half2_t sub2(uint32_t w, uint32_t mask) {
+    return __builtin_bit_cast(half2_t, w & mask);
 }
 
 // Five waves per SIMD: the compiler fits the loop in 88 VGPRs (no spills),
@@ -282,6 +288,9 @@ void qmv_q4_k_kernel(const KqParams p) {
         sxa += xr[e];
         sxb += xr[16 + e];
     }
+    // the whole row sum is kept at the scale 2^-24 of the subnormal quants
+    sxa *= kTwoM24;
+    sxb *= kTwoM24;
     // this lane's chunk g = u / 2 (sub-blocks 2g, 2g + 1): its 24-bit field
     // is bytes 3g .. 3g + 2 of the header's last 12, gathered by one byte
     // permute from the word pair (y, z) for g < 2, else (z, w)
@@ -289,10 +298,6 @@ void qmv_q4_k_kernel(const KqParams p) {
     const bool first_pair = g < 2u;
     const uint32_t fb = first_pair ? 3u * g : 3u * g - 4u;
     const uint32_t psel = fb | ((fb + 1u) << 8) | ((fb + 2u) << 16) | (0x0Cu << 24);    // 0x0C: a zero byte
-
-    uint32_t magic = 0x64006400u;
-    asm volatile("" : "+v"(magic));
-    const half2_t off_lo = {static_cast<_Float16>(-1024.0f), static_cast<_Float16>(-1024.0f)};
 
     __shared__ float lpart[WAVES][R];
     // four rows per step: their sums reduced over the wave together
@@ -303,7 +308,7 @@ void qmv_q4_k_kernel(const KqParams p) {
         const int q = lane >> 4;
         const int vq = ((q & 1) << 1) | (q >> 1);
         if constexpr (WS == 1) {
-            if ((lane & 15) == 0 && r0 + vq < p.n) p.y[r0 + vq] = t;
+            if ((lane & 15) == 0 && r0 + vq < p.n) p.y[r0 + vq] = t * kTwo24;
         } else {
             if ((lane & 15) == 0) lpart[wave][vq % R] = t;
             __syncthreads();
@@ -311,7 +316,7 @@ void qmv_q4_k_kernel(const KqParams p) {
                 float tt = lpart[wave][lane];
 #pragma unroll
                 for (int sl = 1; sl < WS; ++sl) tt += lpart[wave + sl][lane];
-                if (r0 + lane < p.n) p.y[r0 + lane] = tt;
+                if (r0 + lane < p.n) p.y[r0 + lane] = tt * kTwo24;
             }
             __syncthreads();
         }
@@ -336,10 +341,10 @@ void qmv_q4_k_kernel(const KqParams p) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t v = w[j], v8 = v >> 8;
-                const half2_t lo02 = nib2(v, 0x000F000Fu, magic, off_lo);
-                const half2_t lo13 = nib2(v8, 0x000F000Fu, magic, off_lo);
-                const half2_t hi02 = nib2(v, 0x00F000F0u, magic, off_lo);     // 16 q
-                const half2_t hi13 = nib2(v8, 0x00F000F0u, magic, off_lo);
+                const half2_t lo02 = sub2(v, 0x000F000Fu);
+                const half2_t lo13 = sub2(v8, 0x000F000Fu);
+                const half2_t hi02 = sub2(v, 0x00F000F0u);     // 16 q
+                const half2_t hi13 = sub2(v8, 0x00F000F0u);
                 pa = fmaf(static_cast<float>(lo02.x), xr[4 * j + 0], pa);
                 pb = fmaf(static_cast<float>(hi02.x), xr[16 + 4 * j + 0], pb);
                 pa = fmaf(static_cast<float>(lo13.x), xr[4 * j + 1], pa);
@@ -378,7 +383,7 @@ void qmv_q4_k_kernel(const KqParams p) {
                 float a = acc[0];
 #pragma unroll
                 for (int r = 1; r < R; ++r) a = lr == r ? acc[r] : a;
-                if (r0 + lr < p.n) p.y[r0 + lr] = a;
+                if (r0 + lr < p.n) p.y[r0 + lr] = a * kTwo24;
             }
         } else {
             if (lane == kWave - 1) {
@@ -390,7 +395,7 @@ void qmv_q4_k_kernel(const KqParams p) {
                 float t = lpart[wave][lane];
 #pragma unroll
                 for (int s = 1; s < WS; ++s) t += lpart[wave + s][lane];
-                if (r0 + lane < p.n) p.y[r0 + lane] = t;
+                if (r0 + lane < p.n) p.y[r0 + lane] = t * kTwo24;
             }
             __syncthreads();
         }

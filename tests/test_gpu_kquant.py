@@ -141,6 +141,22 @@ def test_qmv_kq_deterministic_and_large_x(qtype):
     check_within(y1, yr, oracle.fp32_path_bound(ar), "large x")
 
 
+@pytest.mark.parametrize("qtype", [Q4K, Q6K])
+@pytest.mark.parametrize("scale", [1e-30, 1e-36])
+def test_qmv_kq_tiny_x(qtype, scale):
+    """Activations near the bottom of the fp32 range (products below 2^-126
+    at 1e-36): the contract still holds and nothing turns non-finite."""
+    rng = np.random.default_rng(80 + qtype)
+    n, k = 512, 2048
+    w = synth.weights(rng, qtype, n, k)
+    p = packed_kq(gq, qtype, w, n, k)
+    x = (synth.activations(rng, k).astype(np.float64) * scale).astype(np.float32)
+    y = down(_fn(qtype)(p, n, k, up(x)))
+    assert np.isfinite(y).all()
+    yr, ar = oracle.matvec(qtype, w, n, k, x)
+    check_within(y, yr, oracle.fp32_path_bound(ar), "tiny x %g" % scale)
+
+
 def test_kq_binding_errors():
     x = torch.zeros(256, dtype=torch.float32, device="cuda")
     p = torch.zeros(gq.kq_packed_bytes(Q4K, 4, 256), dtype=torch.uint8, device="cuda")
