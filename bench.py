@@ -27,13 +27,15 @@ wall time of the timed steps.
 
 The roofline object is for the dominant kernel (the Q8_0 vocab matvec,
 about 90 % of the step's bytes): algorithmic bytes per launch (weight
-blocks + x + y) / its average duration from HIP events recorded around each
-of its launches on the launch stream inside the timed region.
+blocks + x + y) / its average duration from HIP events recorded on the
+launch stream around its launch in every EVENT_EVERY-th step of the timed
+region (launches_timed of them).
 
 Also reported beside ``value`` (none of them replaces it):
   prefill_tiles        the three tiles per pass, timed like the steps
-  chained              the same step recorded once per weight set with
-                       gq_chain_* and replayed (one submission per step)
+  chained              the steps recorded with gq_chain_*, CHAIN_STEPS
+                       consecutive steps per chain (one graph launch), and
+                       (one_step_per_replay) one step per chain
   read_stream_ceiling  best bandwidth of a plain 16-byte read-and-XOR kernel
                        (libgq_bench.so) over the 512 MiB vocab buffers;
                        breakdown rows give their % of it
@@ -76,6 +78,8 @@ HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "qmv_q8_0_vocab_262144x2048_hbm_traffic.txt")
 DOMINANT = "qmv_q8_0 262144x2048 (vocab)"
+EVENT_EVERY = 4          # timed steps per event-bracketed dominant launch
+CHAIN_STEPS = 8          # decode steps recorded per chain (one graph launch)
 COPY_BYTES = 512 * 1024 * 1024        # calibration copy for the HBM counters
 
 
@@ -287,14 +291,24 @@ class Step:
         self.step_weight_bytes = sum(self.weight_bytes[n] for n in self.names)
         self.tile_weight_bytes = sum(self.weight_bytes[n] for n in self.tile_names)
 
-    def record_chains(self):
-        """One recorded chain per weight set: the whole step as one graph."""
+    def record_chains(self, steps_per_chain=1):
+        """Recorded chains of steps_per_chain consecutive steps each (every
+        weight set's steps in turn, as the eager loop runs them), enough
+        chains for each to start on a different set when the count divides
+        evenly; one chain is one graph launch."""
         self.chains = []
-        for i in range(len(self.sets)):
+        n = len(self.sets) if steps_per_chain % len(self.sets) else 1
+        for c0 in range(n):
             c = self.gq.Chain(self.stream)
             with c:
-                self.run(i)
+                for j in range(steps_per_chain):
+                    self.run(c0 * steps_per_chain + j)
             self.chains.append(c)
+
+    def close_chains(self):
+        for c in self.chains:
+            c.close()
+        self.chains = []
 
     def replay(self, i):
         self.chains[i % len(self.chains)].launch(self.stream)
@@ -1315,7 +1329,9 @@ def _timed_trace_average(run_dir, run):
     sel = [d for _, d in durs[w:w + k]]
     if len(sel) != k:
         return None
-    return sum(sel) / len(sel) / 1e3
+    every = run["roofline"].get("event_every", 1)
+    bracketed = sel[::every]
+    return sum(sel) / len(sel) / 1e3, sum(bracketed) / len(bracketed) / 1e3, every
 
 
 def stats_summary(args):
@@ -1353,7 +1369,8 @@ def stats_summary(args):
             dom = float(r["AverageNs"]) / 1e3
     log_file = run_dir.rstrip("/") + ".log"
     run = _bench_line(log_file)
-    timed = _timed_trace_average(run_dir, run)
+    trace = _timed_trace_average(run_dir, run)
+    timed, timed_ev = (trace[0], trace[1]) if trace else (None, None)
     if dom is not None:
         alg = 262144 * 64 * 34 + 2048 * 4 + 262144 * 4
         lines.append("")
@@ -1363,6 +1380,9 @@ def stats_summary(args):
             lines.append("# dominant kernel (vocab), rocprof average over the timed region's launches (the kernel's "
                          "dispatches W+1..W+K in the trace): %d B / %.2f us = %.2f TB/s = %.1f%% of 8 TB/s"
                          % (alg, timed, alg / timed / 1e6, alg / timed / 1e6 / 8.0 * 100))
+            if trace[2] > 1:
+                lines.append("# over the event-bracketed ones only (one in %d of them, the launches the HIP events "
+                             "time): %.2f us" % (trace[2], timed_ev))
         else:
             lines.append("# dominant kernel (vocab), rocprof average over all of the kernel's launches (no trace): "
                          "%d B / %.2f us = %.2f TB/s = %.1f%% of 8 TB/s"
@@ -1371,14 +1391,14 @@ def stats_summary(args):
             ev = run["roofline"]["avg_launch_us"]
             lines.append("# the profiled run's live HIP-event average over the same launches: %.2f us (the events "
                          "bracket each launch, and under the profiler each dispatch waits for its trace record; "
-                         "difference %.1f%%)" % (ev, (ev / (timed or dom) - 1) * 100))
+                         "difference %.1f%%)" % (ev, (ev / (timed_ev or dom) - 1) * 100))
         plain = _bench_line(bench_json) if bench_json else None
         if plain is not None:
             ev = plain["roofline"]["avg_launch_us"]
             lines.append("# the same command without the profiler (%s): HIP-event average %.2f us, "
                          "roofline frac %.3f (difference %.1f%%)"
                          % (os.path.basename(bench_json), ev, plain["roofline"]["frac"],
-                            (ev / (timed or dom) - 1) * 100))
+                            (ev / (timed_ev or dom) - 1) * 100))
     text = "\n".join(lines) + "\n"
     print(text)
     if args.write_profile:
@@ -1489,12 +1509,15 @@ def main():
         step.run(i, tiles=True)
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps, synchronised on both sides
+    # timed region: exactly K steps, synchronised on both sides; an event
+    # pair brackets the dominant launch of every EVENT_EVERY-th step (each
+    # pair costs the step about 1.7 us of device time, so bracketing every
+    # launch would add that much instrumentation to every step)
     ev = {DOMINANT: []}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step.run(i, ev)
+        step.run(i, ev if i % EVENT_EVERY == 0 else None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed / args.steps * 1e3
@@ -1556,20 +1579,29 @@ def main():
         extras[name] = {"median_us": round(med, 2), "weight_bytes": wb,
                         "weight_GBps": round(wb / med / 1e3, 1), "total_GBps": round((wb + ob) / med / 1e3, 1)}
 
-    # the same step recorded as one chain per weight set and replayed
-    # (decode-step chaining: one submission per step instead of 9 launches)
-    step.record_chains()
-    for i in range(args.warmup):
-        step.replay(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step.replay(i)
-    torch.cuda.synchronize()
-    chained_s = (time.perf_counter() - t0) / args.steps
-    chained = {"ms_per_step": round(chained_s * 1e3, 4),
-               "value": round(step.step_weight_bytes / chained_s / 1e9, 2), "unit": "GB/s",
-               "launches_per_replay": step.chains[0].launches, "replays_timed": args.steps}
+    # the step recorded as chains and replayed: CHAIN_STEPS consecutive
+    # steps per chain (one graph launch per CHAIN_STEPS steps), and one step
+    # per chain (one graph launch per step)
+    def time_chains(steps_per_chain):
+        step.record_chains(steps_per_chain)
+        replays = max(1, args.steps // steps_per_chain)
+        for i in range(max(1, args.warmup // steps_per_chain)):
+            step.replay(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(replays):
+            step.replay(i)
+        torch.cuda.synchronize()
+        per_step = (time.perf_counter() - t0) / (replays * steps_per_chain)
+        out = {"ms_per_step": round(per_step * 1e3, 4),
+               "value": round(step.step_weight_bytes / per_step / 1e9, 2), "unit": "GB/s",
+               "steps_per_replay": steps_per_chain, "launches_per_replay": step.chains[0].launches,
+               "replays_timed": replays}
+        step.close_chains()
+        return out
+
+    chained = time_chains(CHAIN_STEPS)
+    chained["one_step_per_replay"] = time_chains(1)
 
     ceiling = read_stream_ceiling(step, log)
     for n, b in breakdown.items():
@@ -1617,6 +1649,7 @@ def main():
             "algorithmic_bytes_per_launch": dom_bytes,
             "avg_launch_us": round(dom_avg_s * 1e6, 2),
             "launches_timed": len(dom_ms),
+            "event_every": EVENT_EVERY,
         },
         "prefill_tiles": prefill_tiles,
         "cpu_baseline": cpu,

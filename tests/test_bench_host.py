@@ -130,6 +130,30 @@ def test_stats_summary_averages_the_timed_region_from_the_trace(tmp_path, capsys
     assert "87.72 us" in out and "difference 2.0%" in out and "0.810" in out
 
 
+def test_stats_summary_compares_events_with_the_bracketed_launches(tmp_path, capsys):
+    # 1 warm-up and 4 timed vocab launches; the events bracket every 2nd timed
+    # one (launches 1 and 3 of the region: 86 us each, the others 96 us)
+    d = tmp_path / "prof"
+    d.mkdir()
+    with open(d / "run_kernel_stats.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"])
+        w.writerow([VOCAB, 5, 500000, 100000.0, 90.0, 86000, 136000, 1.0])
+    durs = [136000, 86000, 96000, 86000, 96000]
+    with open(d / "run_kernel_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        for i, dur in enumerate(durs):
+            w.writerow([10 + i, VOCAB, 1000000 * i, 1000000 * i + dur])
+    (tmp_path / "prof.log").write_text('{"warmup": 1, "steps": 4, "roofline": {"avg_launch_us": 87.72, '
+                                       '"event_every": 2}}\n')
+    bench.stats_summary(argparse.Namespace(stats_summary=str(d), write_profile=False))
+    out = capsys.readouterr().out
+    assert "B / 91.00 us" in out                       # every timed launch
+    assert "one in 2 of them" in out and "86.00 us" in out
+    assert "87.72 us" in out and "difference 2.0%" in out
+
+
 def test_step_traffic_summary_matches_launches_and_calibrates(tmp_path, capsys):
     # a step of two launches, run twice, then the calibration copy; the copy
     # reads 2x its bytes on FETCH_SIZE (factor 0.5) and 1x on WRITE_SIZE
