@@ -49,12 +49,19 @@
 // at a time was 2-3 % slower; with the packed fields read directly; the
 // byte-copy layout, unpacking the GGUF fields in the loop, gave 60-62 /
 // 5.3 / 5.6 and 82-84 / 6.0-6.2 / 5.5-5.8 us); 2 rows at 1024 workgroups
-// were slower. Two row groups in flight per wave (a second register set)
+// were slower; matrices with fewer 4-row groups than the device has SIMDs
+// take 2 rows per step instead, so that every SIMD gets a wave (2048 x 2048:
+// Q4_K 3.14 -> 2.92 us, Q6_K 3.88 -> 3.27 us; 1 row per step was slower, and
+// at 8192 rows and on split rows 4 rows stay faster). Two row groups in
+// flight per wave (a second register set)
 // measured no better: the loop is bound by its VALU work (for the exact
 // nibble dot about 1.6 instructions per element in Q4_K and 2.8 in Q6_K;
 // 2.7 and 3.5 per element in all), not by load latency.
 #ifndef GQ_KQ_R
 #define GQ_KQ_R 4            // rows per wave step
+#endif
+#ifndef GQ_KQ_R_SHORT
+#define GQ_KQ_R_SHORT 2      // rows per wave step for matrices with few rows (below)
 #endif
 #ifndef GQ_KQ_MAX_GRID
 #define GQ_KQ_MAX_GRID 2048  // workgroups of 4 waves at most
@@ -84,6 +91,14 @@ __device__ __forceinline__ float wave_sum_last_row(float v) {
     v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kDppRowBcast31,
                                                                0xF, 0xF, true));
     return v;
+}
+
+// The sums of a and b over the 64 lanes, complete in lanes 0..31 (a) and
+// 32..63 (b): one lane-half swap adds the halves of both, one row swap the
+// two rows of each half, four DPP steps the 16 lanes of a row.
+__device__ __forceinline__ float wave_sum2_rows(float a, float b) {
+    const float h = fold_halves(a, b);
+    return row_sum(fold_rows(h, h));
 }
 
 constexpr int kTypeQ4_K = 12;
@@ -373,6 +388,12 @@ void qmv_q4_k_kernel(const KqParams p) {
             finish4(acc, r0);
             continue;
         }
+        if constexpr (R == 2 && WS == 1) {
+            // two rows: lanes 0 and 32 finish rows r0 and r0 + 1
+            const float t = wave_sum2_rows(acc[0], acc[1 % R]);
+            if ((lane & 31) == 0 && r0 + (lane >> 5) < p.n) p.y[r0 + (lane >> 5)] = t * kTwo24;
+            continue;
+        }
         // (other step sizes) the row sums are complete in lanes 48..63:
         // lane 64 - R + r stores row r
 #pragma unroll
@@ -520,6 +541,12 @@ void qmv_q6_k_kernel(const KqParams p) {
             finish4(acc, r0);
             continue;
         }
+        if constexpr (R == 2 && WS == 1) {
+            // two rows: lanes 0 and 32 finish rows r0 and r0 + 1
+            const float t = wave_sum2_rows(acc[0], acc[1 % R]);
+            if ((lane & 31) == 0 && r0 + (lane >> 5) < p.n) p.y[r0 + (lane >> 5)] = t;
+            continue;
+        }
         // (other step sizes) the row sums are complete in lanes 48..63:
         // lane 64 - R + r stores row r
 #pragma unroll
@@ -565,9 +592,8 @@ int kq_device_cus() {
     return cus;
 }
 
-template <int TYPE, int WS>
+template <int TYPE, int WS, int R>
 hipError_t launch_ws(KqParams p, hipStream_t stream) {
-    constexpr int R = GQ_KQ_R;
     constexpr int WAVES = KqWaves<WS>::value;
     constexpr int SUBS = WAVES / WS;
     p.row_groups = (p.n + R - 1) / R;
@@ -615,18 +641,23 @@ hipError_t launch_qmv_kq(int type, const uint8_t* packed, int64_t n, int64_t k, 
     p.k = static_cast<int>(k);
     p.units = static_cast<int>(k / 32);
     const int ws = (p.units + kWave - 1) / kWave;          // waves a row is split over
+    // un-split rows take GQ_KQ_R_SHORT rows per step when GQ_KQ_R would give
+    // fewer row groups (one wave each) than the device has SIMDs
+    const bool short_rows = (static_cast<int64_t>(p.n) + GQ_KQ_R - 1) / GQ_KQ_R < 4 * kq_device_cus();
     if (type == kTypeQ4_K) {
-        if (ws <= 1) return launch_ws<kTypeQ4_K, 1>(p, stream);
-        if (ws <= 2) return launch_ws<kTypeQ4_K, 2>(p, stream);
-        if (ws <= 4) return launch_ws<kTypeQ4_K, 4>(p, stream);
-        if (ws <= 8) return launch_ws<kTypeQ4_K, 8>(p, stream);
-        if (ws <= 16) return launch_ws<kTypeQ4_K, 16>(p, stream);
+        if (ws <= 1) return short_rows ? launch_ws<kTypeQ4_K, 1, GQ_KQ_R_SHORT>(p, stream)
+                                       : launch_ws<kTypeQ4_K, 1, GQ_KQ_R>(p, stream);
+        if (ws <= 2) return launch_ws<kTypeQ4_K, 2, GQ_KQ_R>(p, stream);
+        if (ws <= 4) return launch_ws<kTypeQ4_K, 4, GQ_KQ_R>(p, stream);
+        if (ws <= 8) return launch_ws<kTypeQ4_K, 8, GQ_KQ_R>(p, stream);
+        if (ws <= 16) return launch_ws<kTypeQ4_K, 16, GQ_KQ_R>(p, stream);
     } else {
-        if (ws <= 1) return launch_ws<kTypeQ6_K, 1>(p, stream);
-        if (ws <= 2) return launch_ws<kTypeQ6_K, 2>(p, stream);
-        if (ws <= 4) return launch_ws<kTypeQ6_K, 4>(p, stream);
-        if (ws <= 8) return launch_ws<kTypeQ6_K, 8>(p, stream);
-        if (ws <= 16) return launch_ws<kTypeQ6_K, 16>(p, stream);
+        if (ws <= 1) return short_rows ? launch_ws<kTypeQ6_K, 1, GQ_KQ_R_SHORT>(p, stream)
+                                       : launch_ws<kTypeQ6_K, 1, GQ_KQ_R>(p, stream);
+        if (ws <= 2) return launch_ws<kTypeQ6_K, 2, GQ_KQ_R>(p, stream);
+        if (ws <= 4) return launch_ws<kTypeQ6_K, 4, GQ_KQ_R>(p, stream);
+        if (ws <= 8) return launch_ws<kTypeQ6_K, 8, GQ_KQ_R>(p, stream);
+        if (ws <= 16) return launch_ws<kTypeQ6_K, 16, GQ_KQ_R>(p, stream);
     }
     return hipErrorInvalidValue;    // beyond the documented maximum k (32768)
 }

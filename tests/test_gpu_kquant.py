@@ -58,7 +58,7 @@ def test_kq_pack_lays_out_every_byte(qtype, n, k):
 # 2, 4, 8 and 16 waves (a last partial wave), ragged row counts (two rows per
 # wave step), the 2048 x 2048 and 8192 x 2048 decode shapes
 SHAPES = [(2048, 2048), (8192, 2048), (1, 256), (3, 768), (1001, 1536), (515, 2304), (300, 4096),
-          (77, 8192), (45, 11776), (64, 16384), (17, 32768), (4096, 2048)]
+          (77, 8192), (45, 11776), (64, 16384), (17, 32768), (4096, 2048), (4099, 1792)]
 
 
 @pytest.mark.parametrize("qtype", [Q4K, Q6K])
