@@ -132,6 +132,19 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 }
 
 // Largest of v over the 64 lanes, in every lane (max is exact in any order).
+// The largest of v over the 64 lanes, in every lane (64-bit keys, moved as
+// two 32-bit halves per step).
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, kWave);
+        const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, kWave);
+        const unsigned long long o = (static_cast<unsigned long long>(hi) << 32) | lo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, dpp_f32<kDppQuadSwap1>(v));
     v = fmaxf(v, dpp_f32<kDppQuadSwap2>(v));

@@ -886,40 +886,45 @@ void qmv_kernel(const QmvParams p) {
         }
     }
 
-    // ---- argmax partial of this workgroup (fixed-shape tree, exact) --------
+    // ---- argmax partial of this workgroup (a maximum: exact in any order) --
     if (FOLD && p.part != nullptr) {
-        __shared__ unsigned long long keys[WAVES * kWave];
-        keys[threadIdx.x] = best;
+        __shared__ unsigned long long keys[WAVES];
+        const unsigned long long wb = wave_max_u64(best);
+        if (lane == 0) keys[threadIdx.x / kWave] = wb;
         __syncthreads();
-        for (int st = WAVES * kWave / 2; st > 0; st >>= 1) {
-            if (static_cast<int>(threadIdx.x) < st) {
-                const unsigned long long o = keys[threadIdx.x + st];
-                keys[threadIdx.x] = o > keys[threadIdx.x] ? o : keys[threadIdx.x];
-            }
-            __syncthreads();
+        if (threadIdx.x == 0) {
+            unsigned long long b = keys[0];
+#pragma unroll
+            for (int w = 1; w < WAVES; ++w) b = keys[w] > b ? keys[w] : b;
+            p.part[blockIdx.x] = b;
         }
-        if (threadIdx.x == 0) p.part[blockIdx.x] = keys[0];
     }
 }
 
-// Second stage of the argmax: one workgroup folds the per-workgroup keys.
-__global__ __launch_bounds__(1024)
+// Second stage of the argmax: one workgroup folds the per-workgroup keys
+// (1 <= nparts <= kArgmaxParts). Each thread issues all of its loads before
+// it waits (indexes past nparts re-read the last key, which changes no
+// maximum), then the waves fold their lanes and thread 0 the waves.
+constexpr int kArgmaxThreads = 256;
+constexpr int kArgmaxParts = static_cast<int>(kArgmaxWorkspaceBytes / sizeof(unsigned long long));
+constexpr int kArgmaxPer = (kArgmaxParts + kArgmaxThreads - 1) / kArgmaxThreads;
+__global__ __launch_bounds__(kArgmaxThreads)
 void argmax_reduce_kernel(const unsigned long long* __restrict__ part, int nparts, int32_t* __restrict__ index,
                           float* __restrict__ value) {
-    __shared__ unsigned long long keys[1024];
-    unsigned long long b = 0ull;
-    for (int i = threadIdx.x; i < nparts; i += 1024) b = part[i] > b ? part[i] : b;
-    keys[threadIdx.x] = b;
+    unsigned long long kv[kArgmaxPer];
+#pragma unroll
+    for (int j = 0; j < kArgmaxPer; ++j) kv[j] = part[min(static_cast<int>(threadIdx.x) + j * kArgmaxThreads, nparts - 1)];
+    unsigned long long b = kv[0];
+#pragma unroll
+    for (int j = 1; j < kArgmaxPer; ++j) b = kv[j] > b ? kv[j] : b;
+    b = wave_max_u64(b);
+    __shared__ unsigned long long keys[kArgmaxThreads / kWave];
+    if ((threadIdx.x & (kWave - 1)) == 0) keys[threadIdx.x / kWave] = b;
     __syncthreads();
-    for (int st = 512; st > 0; st >>= 1) {
-        if (static_cast<int>(threadIdx.x) < st) {
-            const unsigned long long o = keys[threadIdx.x + st];
-            keys[threadIdx.x] = o > keys[threadIdx.x] ? o : keys[threadIdx.x];
-        }
-        __syncthreads();
-    }
     if (threadIdx.x == 0) {
-        const unsigned long long k = keys[0];
+#pragma unroll
+        for (int w = 1; w < kArgmaxThreads / kWave; ++w) b = keys[w] > b ? keys[w] : b;
+        const unsigned long long k = b;
         const uint32_t hi = static_cast<uint32_t>(k >> 32);
         const uint32_t u = (hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi;
         *index = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(k & 0xFFFFFFFFull));
@@ -1074,7 +1079,7 @@ hipError_t launch_qmv_argmax(int type, const void* qs, const uint16_t* d, int64_
     hipError_t e = type == kTypeQ8_0 ? dispatch<kTypeQ8_0, kF32>(p, stream, &grid)
                                      : dispatch<kTypeQ4_0, kF32>(p, stream, &grid);
     if (e != hipSuccess) return e;
-    return launch_kernel(argmax_reduce_kernel, dim3(1), dim3(1024), stream,
+    return launch_kernel(argmax_reduce_kernel, dim3(1), dim3(kArgmaxThreads), stream,
                          static_cast<const unsigned long long*>(workspace), grid, index, value);
 }
 
