@@ -22,6 +22,7 @@ CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast
 TYPE_Q4_0 = 2
 TYPE_Q8_0 = 8
 TYPE_Q4_K = 12
+TYPE_Q5_K = 13
 TYPE_Q6_K = 14
 
 

@@ -47,6 +47,12 @@
  *      byte 32g + l (g < 4, l < 32) holds element 64g + l in its low nibble
  *      and element 64g + 32 + l in its high nibble. Element e belongs to
  *      sub-block e / 32 and is d sc_j q_e - dmin m_j.
+ *      Q5_K, 176 bytes: binary16 d, binary16 dmin, the same 12 scale and
+ *      minimum bytes as Q4_K, 32 bytes qh, then 128 quant bytes laid out as
+ *      Q4_K's (low four bits). The fifth bit of element 64g + l (l < 32) is
+ *      bit 2g of qh byte l, that of element 64g + 32 + l bit 2g + 1. Element
+ *      e belongs to sub-block e / 32 and is d sc_j q_e - dmin m_j, with q_e
+ *      in 0..31 (the page's "one high bit per element").
  *      Q6_K, 210 bytes: 128 bytes ql (low four bits), 64 bytes qh (high two
  *      bits), 16 int8 scales, binary16 d. In half h (elements 128h ..
  *      128h + 127; ql bytes 64h.., qh bytes 32h..), for l < 32: ql byte l
@@ -71,6 +77,7 @@
 #define OR_TYPE_Q4_0 2
 #define OR_TYPE_Q8_0 8
 #define OR_TYPE_Q4_K 12
+#define OR_TYPE_Q5_K 13
 #define OR_TYPE_Q6_K 14
 
 /* ------------------------------------------------------------------------ */
@@ -132,6 +139,7 @@ size_t or_block_bytes(int type)
     if (type == OR_TYPE_Q8_0) return 34;
     if (type == OR_TYPE_Q4_0) return 18;
     if (type == OR_TYPE_Q4_K) return 144;
+    if (type == OR_TYPE_Q5_K) return 176;
     if (type == OR_TYPE_Q6_K) return 210;
     return 0;
 }
@@ -139,12 +147,12 @@ size_t or_block_bytes(int type)
 /* Elements per block: 32, or 256 for the K-quant super-blocks. */
 int64_t or_block_elems(int type)
 {
-    return (type == OR_TYPE_Q4_K || type == OR_TYPE_Q6_K) ? OR_QK_K : OR_QK;
+    return (type == OR_TYPE_Q4_K || type == OR_TYPE_Q5_K || type == OR_TYPE_Q6_K) ? OR_QK_K : OR_QK;
 }
 
 static int is_kquant(int type)
 {
-    return type == OR_TYPE_Q4_K || type == OR_TYPE_Q6_K;
+    return type == OR_TYPE_Q4_K || type == OR_TYPE_Q5_K || type == OR_TYPE_Q6_K;
 }
 
 /* The 6-bit scale and minimum of Q4_K sub-block j from the 12 packed bytes. */
@@ -171,6 +179,21 @@ static void kblock_values(int type, const uint8_t *blk, double w[OR_QK_K])
             for (int l = 0; l < 32; ++l) {
                 q[64 * g + l] = qs[32 * g + l] & 15;
                 q[64 * g + 32 + l] = qs[32 * g + l] >> 4;
+            }
+        for (int e = 0; e < OR_QK_K; ++e) {
+            int sc, m;
+            q4_k_scale_min(s12, e / 32, &sc, &m);
+            w[e] = d * (double)sc * (double)q[e] - dmin * (double)m;
+        }
+    } else if (type == OR_TYPE_Q5_K) {
+        double d = or_fp16_to_f64((uint16_t)(blk[0] | (blk[1] << 8)));
+        double dmin = or_fp16_to_f64((uint16_t)(blk[2] | (blk[3] << 8)));
+        const uint8_t *s12 = blk + 4, *qh = blk + 16, *qs = blk + 48;
+        int q[OR_QK_K];
+        for (int g = 0; g < 4; ++g)
+            for (int l = 0; l < 32; ++l) {
+                q[64 * g + l] = (qs[32 * g + l] & 15) | (((qh[l] >> (2 * g)) & 1) << 4);
+                q[64 * g + 32 + l] = (qs[32 * g + l] >> 4) | (((qh[l] >> (2 * g + 1)) & 1) << 4);
             }
         for (int e = 0; e < OR_QK_K; ++e) {
             int sc, m;

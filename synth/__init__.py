@@ -32,16 +32,21 @@ assert Q8_0_BLOCK.itemsize == 34 and Q4_0_BLOCK.itemsize == 18
 # K-quant super-blocks of 256 elements (GGUF layout; the pages give only the
 # arithmetic, see the oracle's header): Q4_K = binary16 d, binary16 dmin,
 # 12 bytes of packed 6-bit sub-block scales and minimums, 128 quant bytes;
+# Q5_K = the same header, 32 bytes of fifth quant bits, 128 quant bytes;
 # Q6_K = 128 bytes of low quant bits, 64 bytes of high bits, 16 int8 scales,
 # binary16 d.
 QK_K = 256
 TYPE_Q4_K = 12
+TYPE_Q5_K = 13
 TYPE_Q6_K = 14
 Q4_K_BLOCK = np.dtype([("d", "<u2"), ("dmin", "<u2"), ("scales", "u1", (12,)), ("qs", "u1", (128,))])
+Q5_K_BLOCK = np.dtype([("d", "<u2"), ("dmin", "<u2"), ("scales", "u1", (12,)), ("qh", "u1", (32,)),
+                       ("qs", "u1", (128,))])
 Q6_K_BLOCK = np.dtype([("ql", "u1", (128,)), ("qh", "u1", (64,)), ("scales", "i1", (16,)), ("d", "<u2")])
-assert Q4_K_BLOCK.itemsize == 144 and Q6_K_BLOCK.itemsize == 210
+assert Q4_K_BLOCK.itemsize == 144 and Q5_K_BLOCK.itemsize == 176 and Q6_K_BLOCK.itemsize == 210
 
-BLOCK_DTYPE = {TYPE_Q8_0: Q8_0_BLOCK, TYPE_Q4_0: Q4_0_BLOCK, TYPE_Q4_K: Q4_K_BLOCK, TYPE_Q6_K: Q6_K_BLOCK}
+BLOCK_DTYPE = {TYPE_Q8_0: Q8_0_BLOCK, TYPE_Q4_0: Q4_0_BLOCK, TYPE_Q4_K: Q4_K_BLOCK, TYPE_Q5_K: Q5_K_BLOCK,
+               TYPE_Q6_K: Q6_K_BLOCK}
 
 
 def block_dtype(qtype: int) -> np.dtype:
@@ -109,6 +114,22 @@ def q4_k_weights(rng, n: int, k: int, scale_lo=1e-4, scale_hi=3e-4) -> np.ndarra
     return blocks
 
 
+def q5_k_weights(rng, n: int, k: int, scale_lo=1e-4, scale_hi=2e-4) -> np.ndarray:
+    """(n, k/256) Q5_K super-blocks: uniform quant bytes and fifth-bit bytes
+    (every 5-bit quant uniform on 0..31), uniform bytes for the 12 packed
+    scale/min bytes, then binary16 d and dmin uniform in [scale_lo,
+    scale_hi]."""
+    assert k % QK_K == 0
+    nsb = k // QK_K
+    blocks = np.empty((n, nsb), dtype=Q5_K_BLOCK)
+    blocks["qs"] = rng.integers(0, 256, size=(n, nsb, 128), dtype=np.uint8)
+    blocks["qh"] = rng.integers(0, 256, size=(n, nsb, 32), dtype=np.uint8)
+    blocks["scales"] = rng.integers(0, 256, size=(n, nsb, 12), dtype=np.uint8)
+    blocks["d"] = fp16_scales(rng, (n, nsb), scale_lo, scale_hi)
+    blocks["dmin"] = fp16_scales(rng, (n, nsb), scale_lo, scale_hi)
+    return blocks
+
+
 def q6_k_weights(rng, n: int, k: int, scale_lo=1e-5, scale_hi=1e-4) -> np.ndarray:
     """(n, k/256) Q6_K super-blocks: uniform low-bit and high-bit bytes (every
     6-bit quant uniform on 0..63), int8 scales uniform on [-128, 127], then
@@ -130,6 +151,8 @@ def weights(rng, qtype: int, n: int, k: int, **kw) -> np.ndarray:
         return q4_0_weights(rng, n, k, **kw)
     if qtype == TYPE_Q4_K:
         return q4_k_weights(rng, n, k, **kw)
+    if qtype == TYPE_Q5_K:
+        return q5_k_weights(rng, n, k, **kw)
     if qtype == TYPE_Q6_K:
         return q6_k_weights(rng, n, k, **kw)
     raise ValueError(qtype)

@@ -1,18 +1,19 @@
-"""Pins for the oracle's K-quant super-block decoders (Q4_K, Q6_K). CPU only.
+"""Pins for the oracle's K-quant super-block decoders (Q4_K, Q5_K, Q6_K). CPU only.
 
 The pages give the arithmetic of these formats (jouleclaw-loader-gguf
 BENCHMARKS page: "Q4_K matmul" with 32-element sub-blocks and the split
-d_sub * sum(a q) - m_sub * sum(a); "Q5_K + Q6_K matmul": two high bits per
-element and a signed -32 offset) but not the byte layout, which is taken from
+d_sub * sum(a q) - m_sub * sum(a); "Q5_K + Q6_K matmul": one high bit per
+element for Q5_K, two and a signed -32 offset for Q6_K) but not the byte
+layout, which is taken from
 the GGUF format (the oracle's header states it). These tests pin the
 oracle's decoder to that layout without reusing its code:
 
 * an encoder written here in the opposite direction -- for every element,
   where its bits go -- builds super-blocks from chosen (scales, minimums,
-  quants); the oracle must decode them to d sc q - dmin m (Q4_K) or
+  quants); the oracle must decode them to d sc q - dmin m (Q4_K, Q5_K) or
   d sc (q - 32) (Q6_K) exactly, computed here from the chosen integers;
-* brute force over every 6-bit scale/minimum pair of every Q4_K sub-block
-  and every 6-bit Q6_K quant at every position;
+* brute force over every 6-bit scale/minimum pair of every Q4_K sub-block,
+  every 5-bit Q5_K quant and every 6-bit Q6_K quant at every position;
 * closed forms (all-zero quants leave only the minimums; q = 32 gives 0);
 * a second decoder written with numpy array operations, and the pages'
   algebraic split of the sub-block sum, against the oracle's matvec.
@@ -25,7 +26,7 @@ import pytest
 import oracle
 import synth
 
-Q4K, Q6K = synth.TYPE_Q4_K, synth.TYPE_Q6_K
+Q4K, Q5K, Q6K = synth.TYPE_Q4_K, synth.TYPE_Q5_K, synth.TYPE_Q6_K
 
 
 def f16(v):
@@ -58,6 +59,20 @@ def enc_q4_k(d_bits, dmin_bits, sc, m, q):
         else:
             b[16 + 32 * g + r - 32] |= q[e] << 4
     return bytes(b)
+
+
+def enc_q5_k(d_bits, dmin_bits, sc, m, q):
+    """Q5_K super-block bytes from 8 scales, 8 minimums (0..63) and 256
+    quants (0..31): the Q4_K header and low nibbles, and each quant's fifth
+    bit in the 32 qh bytes (element 64g + r: byte r % 32, bit 2g for r < 32,
+    2g + 1 otherwise)."""
+    q = np.asarray(q)
+    b = bytearray(enc_q4_k(d_bits, dmin_bits, sc, m, q & 15))
+    qh = bytearray(32)
+    for e in range(256):
+        g, r = divmod(e, 64)
+        qh[r % 32] |= (int(q[e]) >> 4) << (2 * g + r // 32)
+    return bytes(b[:16] + qh + b[16:])
 
 
 def enc_q6_k(d_bits, sc, q):
@@ -103,6 +118,37 @@ def test_q6_k_encoder_roundtrip_random():
         expect.append(d * sc[np.arange(256) // 16] * (q - 32))
     W = oracle.dequantize(Q6K, blocks_from(raws), 40, 256)
     assert np.array_equal(W, np.array(expect, dtype=np.float64))
+
+
+def test_q5_k_encoder_roundtrip_random():
+    rng = np.random.default_rng(7)
+    raws, expect = [], []
+    for _ in range(40):
+        d, dmin = rng.choice([0.5, 0.25, 1.0, 2.0, 0.125]), rng.choice([0.5, 0.25, 1.0, 0.0625])
+        sc, m = rng.integers(0, 64, 8), rng.integers(0, 64, 8)
+        q = rng.integers(0, 32, 256)
+        raws.append(enc_q5_k(f16(d), f16(dmin), sc, m, q))
+        expect.append(d * sc[np.arange(256) // 32] * q - dmin * m[np.arange(256) // 32])
+    W = oracle.dequantize(Q5K, blocks_from(raws), 40, 256)
+    assert np.array_equal(W, np.array(expect, dtype=np.float64))
+
+
+def test_q5_k_every_value_at_every_position():
+    """Each element takes each 5-bit value in turn, all others 0; sub-block
+    scales j + 1 and minimums 0, d = 1: exactly that element reads
+    (j + 1) v (a wrong fifth-bit position or sub-block index shows)."""
+    sc = np.arange(1, 9)
+    for v in range(1, 32):
+        raws, expect = [], []
+        for e in range(256):
+            q = np.zeros(256, int)
+            q[e] = v
+            raws.append(enc_q5_k(f16(1.0), f16(1.0), sc, np.zeros(8, int), q))
+            row = np.zeros(256)
+            row[e] = (e // 32 + 1) * v
+            expect.append(row)
+        W = oracle.dequantize(Q5K, blocks_from(raws), 256, 256)
+        assert np.array_equal(W, np.array(expect)), v
 
 
 def test_q4_k_every_scale_min_pair_of_every_sub_block():
@@ -171,6 +217,16 @@ def test_closed_forms():
     raw = blocks_from([enc_q4_k(f16(1.0), f16(3.0), np.ones(8, int), np.zeros(8, int), np.full(256, 15))] * 2)
     y, _ = oracle.matvec(Q4K, raw, 1, k, np.ones(k))
     assert y[0] == 15 * k
+    # Q5_K, all quants 0: the same minimum-only sum as Q4_K (same header)
+    raw = blocks_from([enc_q5_k(f16(0.5), f16(0.25), sc[i], m[i], np.zeros(256, int)) for i in range(2)])
+    y, _ = oracle.matvec(Q5K, raw, 1, k, x)
+    assert y[0] == pytest.approx(-0.25 * float((m.reshape(-1) * xs).sum()), rel=1e-13)
+    # Q5_K, q = 31, scale 1, minimum 0, d = 1, x = 1: y = 31 k; q = 16 (fifth
+    # bit alone) gives 16 k
+    for v in (31, 16):
+        raw = blocks_from([enc_q5_k(f16(1.0), f16(3.0), np.ones(8, int), np.zeros(8, int), np.full(256, v))] * 2)
+        y, _ = oracle.matvec(Q5K, raw, 1, k, np.ones(k))
+        assert y[0] == v * k
     # Q6_K, q = 32 everywhere: w = 0 whatever the scales
     raw = blocks_from([enc_q6_k(f16(2.0), rng.integers(-128, 128, 16), np.full(256, 32))] * 2)
     y, a = oracle.matvec(Q6K, raw, 1, k, x)
@@ -199,6 +255,24 @@ def _numpy_dequant_q4_k(w):
     return vals.reshape(w.shape[0], -1)
 
 
+def _numpy_dequant_q5_k(w):
+    """A second Q5_K decoder: the Q4_K one on the low nibbles, plus 16 times
+    each element's fifth bit taken by whole-array shifts."""
+    base = w[["d", "dmin", "scales", "qs"]]
+    w4 = np.empty(w.shape, dtype=synth.Q4_K_BLOCK)
+    for f in ("d", "dmin", "scales", "qs"):
+        w4[f] = base[f]
+    d = w["d"].view(np.float16).astype(np.float64)[..., None]
+    s = w["scales"].astype(np.int64)
+    sc = np.concatenate([s[..., 0:4] & 63, (s[..., 8:12] & 15) | ((s[..., 0:4] >> 6) << 4)], axis=-1)
+    qh = w["qh"].astype(np.int64)                                   # (..., 32): byte l
+    bits = (qh[..., None, :] >> np.arange(8).reshape(8, 1)) & 1      # (..., 8 bits, 32 l): bit 2g + t
+    fifth = bits.reshape(w.shape + (256,))                          # element 64g + 32t + l
+    sub = np.arange(256) // 32
+    extra = (d * sc[..., sub] * 16 * fifth).reshape(w.shape[0], -1)
+    return _numpy_dequant_q4_k(w4) + extra
+
+
 def _numpy_dequant_q6_k(w):
     d = w["d"].view(np.float16).astype(np.float64)[..., None]
     ql = w["ql"].astype(np.int64).reshape(w.shape + (2, 2, 32))     # half, ql run, l
@@ -210,7 +284,8 @@ def _numpy_dequant_q6_k(w):
     return (d * sc * (q - 32)).reshape(w.shape[0], -1)
 
 
-@pytest.mark.parametrize("qtype,dec", [(Q4K, _numpy_dequant_q4_k), (Q6K, _numpy_dequant_q6_k)])
+@pytest.mark.parametrize("qtype,dec", [(Q4K, _numpy_dequant_q4_k), (Q5K, _numpy_dequant_q5_k),
+                                       (Q6K, _numpy_dequant_q6_k)])
 def test_numpy_second_decoder_and_matvec(qtype, dec):
     rng = np.random.default_rng(4 + qtype)
     n, k = 37, 1024
