@@ -47,7 +47,7 @@ Also reported beside ``value`` (none of them replaces it):
                        host's issue time per launch, and 64-launch graph
                        figures over distinct copies and over one copy
                        (MALL-hot); the 64x256 Q8_0 config is a launch-latency
-                       point, not a roofline point; Q4_K / Q6_K matvecs at
+                       point, not a roofline point; Q4_K / Q5_K / Q6_K matvecs at
                        the 2048 x 2048, 8192 x 2048 and 262144 x 2048 shapes
 
 Modes:
@@ -466,6 +466,7 @@ def per_config(step, ceiling_gbps, log, rotate_bytes=2 << 30):
     xk = up(synth.activations(np.random.default_rng(5), 2048))
     kq_keep = [xk]
     for qtype, tname, fn, sb_bytes in ((gq.TYPE_Q4_K, "Q4_K", L.gq_qmv_q4_k, 144),
+                                      (gq.TYPE_Q5_K, "Q5_K", L.gq_qmv_q5_k, 176),
                                       (gq.TYPE_Q6_K, "Q6_K", L.gq_qmv_q6_k, 210)):
         for n in (2048, 8192, 262144):
             wbytes = n * 8 * sb_bytes
@@ -768,8 +769,8 @@ def pmc_step_mode(args, log):
 
 
 def pmc_kq_mode(args, log):
-    """The K-quant matvecs at 262144 x 2048 (3 launches each, Q4_K then
-    Q6_K), then a calibration copy of known size (3 launches), for the
+    """The K-quant matvecs at 262144 x 2048 (3 launches each, Q4_K, Q5_K,
+    then Q6_K), then a calibration copy of known size (3 launches), for the
     rocprofv3 --pmc passes of the K-quant kernels. Prints the launches with
     their algorithmic bytes as one JSON line."""
     import ctypes
@@ -785,7 +786,8 @@ def pmc_kq_mode(args, log):
     n, k = 262144, 2048
     x = torch.from_numpy(synth.activations(np.random.default_rng(5), k)).cuda()
     launches, work = [], []
-    for qtype, tname, fn, sb in ((gq.TYPE_Q4_K, "q4_k", L.gq_qmv_q4_k, 144), (gq.TYPE_Q6_K, "q6_k", L.gq_qmv_q6_k, 210)):
+    for qtype, tname, fn, sb in ((gq.TYPE_Q4_K, "q4_k", L.gq_qmv_q4_k, 144), (gq.TYPE_Q5_K, "q5_k", L.gq_qmv_q5_k, 176),
+                                 (gq.TYPE_Q6_K, "q6_k", L.gq_qmv_q6_k, 210)):
         raw = torch.from_numpy(synth.as_bytes(synth.weights(np.random.default_rng(n + qtype), qtype, n, k))
                                .reshape(-1)).cuda()
         pk = gq.kq_pack(qtype, raw, n, k)
@@ -1273,9 +1275,14 @@ STATS_FILE = os.path.join(PROFILES, "decode_step_kernel_stats.txt")
 
 # what each kernel instantiation is in the default run
 KERNEL_LABELS = [
-    ("qmv_q4_k_kernel<1, 4>", "qmv Q4_K fp32 x: k 2048 (2048, 8192, 262144 rows)"),
-    ("qmv_q6_k_kernel<1, 4>", "qmv Q6_K fp32 x: k 2048 (2048, 8192, 262144 rows)"),
+    ("qmv_q4_k_kernel<1, 4, false>", "qmv Q4_K fp32 x: k 2048 (8192, 262144 rows)"),
+    ("qmv_q4_k_kernel<1, 2, false>", "qmv Q4_K fp32 x, 2 rows per step: 2048x2048"),
+    ("qmv_q4_k_kernel<1, 4, true>", "qmv Q5_K fp32 x: k 2048 (8192, 262144 rows)"),
+    ("qmv_q4_k_kernel<1, 2, true>", "qmv Q5_K fp32 x, 2 rows per step: 2048x2048"),
+    ("qmv_q6_k_kernel<1, 4>", "qmv Q6_K fp32 x: k 2048 (8192, 262144 rows)"),
+    ("qmv_q6_k_kernel<1, 2>", "qmv Q6_K fp32 x, 2 rows per step: 2048x2048"),
     ("kq_pack_kernel<12>", "pack Q4_K"),
+    ("kq_pack_kernel<13>", "pack Q5_K"),
     ("kq_pack_kernel<14>", "pack Q6_K"),
     ("qmv_kernel<8, 0, 2, 1, 4, false>", "qmv Q8_0 fp32 x, tall: vocab 262144 (+1/8) x2048"),
     ("qmv_kernel<8, 0, 2, 1, 4, true>", "qmv Q8_0 + rmsnorm + softcap + argmax stage 1: vocab"),

@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libgq.so")
 TYPE_Q4_0 = 2
 TYPE_Q8_0 = 8
 TYPE_Q4_K = 12
+TYPE_Q5_K = 13
 TYPE_Q6_K = 14
 
 GQ_OK = 0
@@ -62,6 +63,7 @@ _SIGS = {
     "gq_kq_packed_bytes": ([_I, _I64, _I64], ctypes.c_size_t),
     "gq_kq_pack": ([_I, _P, _I64, _I64, _P, _P], _I),
     "gq_qmv_q4_k": ([_P, _I64, _I64, _P, _P, _P], _I),
+    "gq_qmv_q5_k": ([_P, _I64, _I64, _P, _P, _P], _I),
     "gq_qmv_q6_k": ([_P, _I64, _I64, _P, _P, _P], _I),
     "gq_qmm_tile_m": ([_P, _P, _I64, _I64, _I, _P, _P, _P, _P, _P], _I),
     "gq_chain_begin": ([_P], _I),
@@ -397,7 +399,7 @@ def _kq_dims(n, k):
 
 
 def kq_pack(qtype, blocks, n, k, packed=None, stream=None):
-    """GGUF Q4_K / Q6_K super-blocks (device uint8) -> one packed uint8 buffer."""
+    """GGUF Q4_K / Q5_K / Q6_K super-blocks (device uint8) -> one packed uint8 buffer."""
     torch = _torch()
     n_, k_ = _kq_dims(n, k)
     need = kq_packed_bytes(qtype, n_, k_) if n_ else 0
@@ -421,6 +423,10 @@ def _qmv_kq(fn, qtype, packed, n, k, x, y, stream):
 
 def qmv_q4_k(packed, n, k, x, y=None, stream=None):
     return _qmv_kq("gq_qmv_q4_k", TYPE_Q4_K, packed, n, k, x, y, stream)
+
+
+def qmv_q5_k(packed, n, k, x, y=None, stream=None):
+    return _qmv_kq("gq_qmv_q5_k", TYPE_Q5_K, packed, n, k, x, y, stream)
 
 
 def qmv_q6_k(packed, n, k, x, y=None, stream=None):

@@ -43,7 +43,7 @@ bool any_alias(const Range (&outs)[NO], const Range (&ins)[NI]) {
 }
 
 inline bool type_ok(int type) { return type == GQ_TYPE_Q4_0 || type == GQ_TYPE_Q8_0; }
-inline bool kq_type_ok(int type) { return type == GQ_TYPE_Q4_K || type == GQ_TYPE_Q6_K; }
+inline bool kq_type_ok(int type) { return type == GQ_TYPE_Q4_K || type == GQ_TYPE_Q5_K || type == GQ_TYPE_Q6_K; }
 
 // n x k shape check of the K-quant entry points (whole 256-element super-blocks).
 inline int check_kq_shape(int64_t n, int64_t k) {
@@ -208,6 +208,7 @@ size_t gq_block_bytes(int type) {
     if (type == GQ_TYPE_Q8_0) return 34;
     if (type == GQ_TYPE_Q4_0) return 18;
     if (type == GQ_TYPE_Q4_K) return 144;
+    if (type == GQ_TYPE_Q5_K) return 176;
     if (type == GQ_TYPE_Q6_K) return 210;
     return 0;
 }
@@ -361,7 +362,7 @@ int gq_kq_pack(int type, const void* blocks, int64_t n, int64_t k, void* packed,
     int st = check_kq_shape(n, k);
     if (st != GQ_OK) return st;
     if (!aligned(packed, 16)) return GQ_ERR_ALIGN;
-    const size_t bb = type == GQ_TYPE_Q4_K ? 144 : 210;
+    const size_t bb = gq_block_bytes(type);
     const Range outs[] = {{packed, gq::kq_layout(type, n, k, nullptr)}};
     const Range ins[] = {{blocks, static_cast<size_t>(n) * static_cast<size_t>(k / 256) * bb}};
     if (any_alias(outs, ins)) return GQ_ERR_ALIAS;
@@ -388,6 +389,10 @@ extern "C" {
 
 int gq_qmv_q4_k(const void* packed, int64_t n, int64_t k, const float* x, float* y, void* stream) {
     return qmv_kq(GQ_TYPE_Q4_K, packed, n, k, x, y, stream);
+}
+
+int gq_qmv_q5_k(const void* packed, int64_t n, int64_t k, const float* x, float* y, void* stream) {
+    return qmv_kq(GQ_TYPE_Q5_K, packed, n, k, x, y, stream);
 }
 
 int gq_qmv_q6_k(const void* packed, int64_t n, int64_t k, const float* x, float* y, void* stream) {

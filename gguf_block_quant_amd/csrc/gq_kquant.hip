@@ -1,16 +1,20 @@
-// gq_kquant.hip -- M = 1 decode matvec over K-quant super-blocks (Q4_K and
-// Q6_K, 256 elements each) with fp32 activations, and their load-time pack.
+// gq_kquant.hip -- M = 1 decode matvec over K-quant super-blocks (Q4_K, Q5_K
+// and Q6_K, 256 elements each) with fp32 activations, and their load-time
+// pack.
 //
 // What is computed follows the jouleclaw-loader-gguf BENCHMARKS page: "Q4_K
 // matmul" works on 32-element sub-blocks, each with a scale and a minimum,
 // w = d_sub q - m_sub, and splits the sum as d_sub sum(a q) - m_sub sum(a);
-// "Q5_K + Q6_K matmul" takes two high bits per element and a signed -32
-// offset for Q6_K. The super-block byte layout (not printed on the pages) is
-// the GGUF one:
+// "Q5_K + Q6_K matmul" takes one high bit per element for Q5_K, and two high
+// bits and a signed -32 offset for Q6_K. The super-block byte layout (not
+// printed on the pages) is the GGUF one:
 //   Q4_K (144 B): binary16 d, binary16 dmin, 12 bytes of packed 6-bit
 //     sub-block scales sc_j and minimums m_j, 128 quant bytes; quant byte
 //     32g + l holds element 64g + l (low nibble) and 64g + 32 + l (high);
 //     element e of sub-block j = e / 32 is d sc_j q - dmin m_j.
+//   Q5_K (176 B): d, dmin and the 12 scale bytes as Q4_K, qh[32], 128 quant
+//     bytes as Q4_K; the fifth bit of element 64g + l is bit 2g of qh byte
+//     l (l < 32), that of 64g + 32 + l bit 2g + 1; q in 0..31.
 //   Q6_K (210 B): ql[128] (low four bits), qh[64] (high two bits), int8
 //     scales[16], binary16 d; element e is d scales[e / 16] (q - 32).
 //
@@ -21,14 +25,18 @@
 //         hdr [n][k/256][16]: d, dmin, then for each 64-element chunk g
 //         (sub-blocks 2g and 2g + 1) the 24-bit field sc_2g | sc_2g+1 << 6 |
 //         m_2g << 12 | m_2g+1 << 18 in bytes 4 + 3g .. 6 + 3g.
+//   Q5_K: qs and hdr as Q4_K, then fifth [n][k/32]: one 32-bit word per
+//         16-byte quant unit holding the fifth bits of its 32 elements
+//         (layout at kq5_lo_pos).
 //   Q6_K: ql [n][k/2] (as in the super-block); qh [n][k/4]: for each 16-byte
 //         unit of ql (below), 8 bytes holding the high two bits of its 32
 //         elements (layout at qh_fields); sc [n][k/16]: for each unit, its two
 //         int8 scales (low run, high run); d [n][k/256] binary16.
 // Decomposition: lane l of a wave owns unit l of its slice of the row (16
 // bytes = 32 elements, in two runs of 16 that share a sub-block scale each:
-//   Q4_K unit u of a super-block: runs 64(u/2) + 16(u%2) (low nibbles,
-//     sub-block u & 6) and that + 32 (high nibbles, sub-block (u & 6) + 1);
+//   Q4_K / Q5_K unit u of a super-block: runs 64(u/2) + 16(u%2) (low
+//     nibbles, sub-block u & 6) and that + 32 (high nibbles, sub-block
+//     (u & 6) + 1);
 //   Q6_K unit 4h + j: runs 128h + 16j (scale 8h + j) and that + 64 (scale
 //     8h + j + 4), the high bits from the unit's own 8 packed qh bytes).
 // The lane's 32 activations stay in VGPRs for every row it streams. Rows
@@ -102,6 +110,7 @@ __device__ __forceinline__ float wave_sum2_rows(float a, float b) {
 }
 
 constexpr int kTypeQ4_K = 12;
+constexpr int kTypeQ5_K = 13;
 constexpr int kTypeQ6_K = 14;
 
 inline size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
@@ -120,6 +129,10 @@ size_t kq_layout(int type, int64_t n, int64_t k, size_t* offsets) {
     if (type == kTypeQ4_K) {
         o[1] = round256(nn * kk / 2);
         total = o[1] + nn * (kk / 256) * 16;
+    } else if (type == kTypeQ5_K) {
+        o[1] = round256(nn * kk / 2);
+        o[2] = o[1] + round256(nn * (kk / 256) * 16);
+        total = o[2] + nn * (kk / 32) * 4;
     } else {
         o[1] = round256(nn * kk / 2);
         o[2] = o[1] + round256(nn * kk / 4);
@@ -145,6 +158,17 @@ namespace {
 __host__ __device__ constexpr int kq6_lo_pos(int b) { return (b & 2) * 8 + (b & 1) * 2 + 4; }
 __host__ __device__ constexpr int kq6_hi_pos(int b) { return kq6_lo_pos(b) + 4; }
 
+// Q5_K fifth bits: one 32-bit word per 16-byte quant unit. Quant word c of
+// the unit holds elements 4c .. 4c + 3 of both runs; its eight bits sit
+// where the binary16 construction ORs them in -- low-run element 4c + b at
+// kq5_lo_pos(b) = 4, 5, 20, 21 and high-run element 4c + b at
+// kq5_hi_pos(b) = 8, 9, 24, 25 (b = 1 and 3 brought down by a shift of 1) --
+// rotated left by kq5_rot(c) = 0, 2, 8, 10: the four rotated sets are
+// disjoint and fill the word, so one rotate gives word c its bits in place.
+__host__ __device__ constexpr int kq5_lo_pos(int b) { return (b & 2) * 8 + (b & 1) + 4; }
+__host__ __device__ constexpr int kq5_hi_pos(int b) { return kq5_lo_pos(b) + 4; }
+__host__ __device__ constexpr int kq5_rot(int c) { return (c & 1) * 2 + (c & 2) * 4; }
+
 // ---------------------------------------------------------------------------
 // Pack: one thread per super-block; byte loads (a GGUF block is only
 // 2-byte aligned at best), 16-byte stores into the aligned sections.
@@ -153,7 +177,7 @@ template <int TYPE>
 __global__ __launch_bounds__(kBlockThreads)
 void kq_pack_kernel(const uint8_t* __restrict__ blocks, int64_t nsb_total, uint8_t* __restrict__ out,
                     size_t o1, size_t o2, size_t o3) {
-    constexpr int BB = TYPE == kTypeQ4_K ? 144 : 210;
+    constexpr int BB = TYPE == kTypeQ4_K ? 144 : (TYPE == kTypeQ5_K ? 176 : 210);
     const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i >= nsb_total) return;
     const uint8_t* src = blocks + i * BB;
@@ -164,10 +188,13 @@ void kq_pack_kernel(const uint8_t* __restrict__ blocks, int64_t nsb_total, uint8
     auto copy16 = [&](int off, uint8_t* dst) {
         *reinterpret_cast<uint4*>(dst) = make_uint4(word(off), word(off + 4), word(off + 8), word(off + 12));
     };
-    if constexpr (TYPE == kTypeQ4_K) {
+    if constexpr (TYPE == kTypeQ4_K || TYPE == kTypeQ5_K) {
+        // Q5_K: the same header and quant bytes, the quants after its 32
+        // fifth-bit bytes
+        constexpr int kQs = TYPE == kTypeQ4_K ? 16 : 48;
         uint8_t* qs = out + i * 128;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) copy16(16 + 16 * c, qs + 16 * c);
+        for (int c = 0; c < 8; ++c) copy16(kQs + 16 * c, qs + 16 * c);
         // the GGUF 6-bit scales and minimums (12 bytes q[0..11] after d and
         // dmin): sub-blocks 0-3 take the low six bits of q[j] (scale) and
         // q[j + 4] (minimum); sub-blocks 4-7 take the nibbles of q[j + 4]
@@ -195,6 +222,31 @@ void kq_pack_kernel(const uint8_t* __restrict__ blocks, int64_t nsb_total, uint8
         for (int w = 0; w < 4; ++w)
             hw[w] = h[4 * w] | (h[4 * w + 1] << 8) | (h[4 * w + 2] << 16) | (static_cast<uint32_t>(h[4 * w + 3]) << 24);
         *reinterpret_cast<uint4*>(out + o1 + i * 16) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        if constexpr (TYPE == kTypeQ5_K) {
+            // unit u = 2 g + t covers quant bytes 32 g + 16 t .. + 15:
+            // elements 64 g + 16 t + e (low nibbles) and + 32 (high nibbles),
+            // e < 16, whose fifth bits are bits 2 g and 2 g + 1 of GGUF qh
+            // byte 16 t + e
+            const uint8_t* qhs = src + 16;
+            uint32_t* fw = reinterpret_cast<uint32_t*>(out + o2 + i * 32);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int g = u >> 1, t = u & 1;
+                uint32_t word = 0;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    uint32_t f = 0;
+#pragma unroll
+                    for (int bb = 0; bb < 4; ++bb) {
+                        const uint32_t qb = qhs[16 * t + 4 * c + bb];
+                        f |= ((qb >> (2 * g)) & 1u) << kq5_lo_pos(bb);
+                        f |= ((qb >> (2 * g + 1)) & 1u) << kq5_hi_pos(bb);
+                    }
+                    word |= kq5_rot(c) == 0 ? f : ((f << kq5_rot(c)) | (f >> (32 - kq5_rot(c))));
+                }
+                fw[u] = word;
+            }
+        }
     } else {
         uint8_t* ql = out + i * 128;
 #pragma unroll
@@ -235,7 +287,7 @@ void kq_pack_kernel(const uint8_t* __restrict__ blocks, int64_t nsb_total, uint8
 
 struct KqParams {
     const uint8_t* q;       // quant bytes [n][k/2] (Q4_K qs, Q6_K ql)
-    const uint8_t* hdr;     // Q4_K: [n][k/256][16] headers
+    const uint8_t* hdr;     // Q4_K, Q5_K: [n][k/256][16] headers
     const uint8_t* qh;      // Q6_K: [n][k/4]
     const int8_t* sc;       // Q6_K: [n][k/16]
     const uint16_t* d;      // Q6_K: [n][k/256]
@@ -245,6 +297,10 @@ struct KqParams {
     int k;
     int units;              // 16-byte quant units per row (k / 32)
     int row_groups;         // ceil(n / R)
+    // (last: placed after hdr it moved the fields the Q4_K kernel reads, and
+    // the 8192 x 2048 and 2048 x 8192 Q4_K matvecs took 4.78 / 4.91 us
+    // instead of 4.55 / 4.67 with identical kernel code)
+    const uint32_t* fifth;  // Q5_K: [n][k/32] fifth-bit words
 };
 
 // Waves per workgroup: 4, or WS when a row is split over more waves.
@@ -270,7 +326,9 @@ __device__ __forceinline__ half2_t sub2(uint32_t w, uint32_t mask) {
 // where it would otherwise take 101 and run four (measured: 262144 x 2048
 // 58.5 -> 56.5 us, 8192 x 2048 and 2048 x 8192 5.3 -> 5.1 us; six waves
 // spill and are slower; Q6_K spills at five and keeps its default).
-template <int WS, int R>
+// Q5 (Q5_K): the same kernel with each quant's fifth bit OR-ed in from the
+// unit's fifth-bit word (q in 0..31, still a subnormal with no offset).
+template <int WS, int R, bool Q5>
 __global__ __launch_bounds__(KqWaves<WS>::value * kWave) __attribute__((amdgpu_waves_per_eu(5)))
 void qmv_q4_k_kernel(const KqParams p) {
     constexpr int WAVES = KqWaves<WS>::value;
@@ -339,6 +397,7 @@ void qmv_q4_k_kernel(const KqParams p) {
     for (int it = blockIdx.x; it * SUBS < p.row_groups; it += gridDim.x) {
         const int r0 = (it * SUBS + sub) * R;
         uint4 q[R], h[R];
+        uint32_t fh[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const uint32_t row = static_cast<uint32_t>(min(r0 + r, p.n - 1));
@@ -347,6 +406,11 @@ void qmv_q4_k_kernel(const KqParams p) {
                 p.q + static_cast<uint64_t>(row) * static_cast<uint32_t>(p.k / 2) + uload * 16u));
             q[r] = make_uint4(t.x, t.y, t.z, t.w);
             h[r] = *reinterpret_cast<const uint4*>(p.hdr + (static_cast<uint64_t>(row) * nsb + sb) * 16u);
+            if constexpr (Q5)
+                fh[r] = __builtin_nontemporal_load(p.fifth + static_cast<uint64_t>(row) * static_cast<uint32_t>(p.units) +
+                                                   uload);
+            else
+                fh[r] = 0u;
         }
         float acc[R];
 #pragma unroll
@@ -356,10 +420,23 @@ void qmv_q4_k_kernel(const KqParams p) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t v = w[j], v8 = v >> 8;
-                const half2_t lo02 = sub2(v, 0x000F000Fu);
-                const half2_t lo13 = sub2(v8, 0x000F000Fu);
-                const half2_t hi02 = sub2(v, 0x00F000F0u);     // 16 q
-                const half2_t hi13 = sub2(v8, 0x00F000F0u);
+                half2_t lo02, lo13, hi02, hi13;
+                if constexpr (Q5) {
+                    // word j's fifth bits, rotated into place: bits 4 and 20
+                    // (elements 4j, 4j + 2 of the low run) and 8, 24 (the
+                    // high run, nibbles in place); odd elements one bit up
+                    const uint32_t hc = kq5_rot(j) == 0 ? fh[r] : __builtin_amdgcn_alignbit(fh[r], fh[r], kq5_rot(j));
+                    const uint32_t hc1 = hc >> 1;
+                    lo02 = __builtin_bit_cast(half2_t, (hc & 0x00100010u) | (v & 0x000F000Fu));
+                    lo13 = __builtin_bit_cast(half2_t, (hc1 & 0x00100010u) | (v8 & 0x000F000Fu));
+                    hi02 = __builtin_bit_cast(half2_t, (hc & 0x01000100u) | (v & 0x00F000F0u));     // 16 q
+                    hi13 = __builtin_bit_cast(half2_t, (hc1 & 0x01000100u) | (v8 & 0x00F000F0u));
+                } else {
+                    lo02 = sub2(v, 0x000F000Fu);
+                    lo13 = sub2(v8, 0x000F000Fu);
+                    hi02 = sub2(v, 0x00F000F0u);     // 16 q
+                    hi13 = sub2(v8, 0x00F000F0u);
+                }
                 pa = fmaf(static_cast<float>(lo02.x), xr[4 * j + 0], pa);
                 pb = fmaf(static_cast<float>(hi02.x), xr[16 + 4 * j + 0], pb);
                 pa = fmaf(static_cast<float>(lo13.x), xr[4 * j + 1], pa);
@@ -597,7 +674,8 @@ hipError_t launch_ws(KqParams p, hipStream_t stream) {
     constexpr int WAVES = KqWaves<WS>::value;
     constexpr int SUBS = WAVES / WS;
     p.row_groups = (p.n + R - 1) / R;
-    const auto kernel = TYPE == kTypeQ4_K ? qmv_q4_k_kernel<WS, R> : qmv_q6_k_kernel<WS, R>;
+    const auto kernel = TYPE == kTypeQ4_K ? qmv_q4_k_kernel<WS, R, false>
+                        : (TYPE == kTypeQ5_K ? qmv_q4_k_kernel<WS, R, true> : qmv_q6_k_kernel<WS, R>);
     // resident workgroups (one query per kernel variant): the grid strides
     // over the row groups and never needs a second dispatch round
     static const int per_cu = [&] {
@@ -613,6 +691,18 @@ hipError_t launch_ws(KqParams p, hipStream_t stream) {
     return launch_kernel(kernel, dim3(grid), dim3(WAVES * kWave), stream, p);
 }
 
+// The split of a row over ws waves (<= 16, k <= 32768), and for un-split
+// short matrices GQ_KQ_R_SHORT rows per step.
+template <int TYPE>
+hipError_t launch_type(KqParams p, int ws, bool short_rows, hipStream_t stream) {
+    if (ws <= 1) return short_rows ? launch_ws<TYPE, 1, GQ_KQ_R_SHORT>(p, stream) : launch_ws<TYPE, 1, GQ_KQ_R>(p, stream);
+    if (ws <= 2) return launch_ws<TYPE, 2, GQ_KQ_R>(p, stream);
+    if (ws <= 4) return launch_ws<TYPE, 4, GQ_KQ_R>(p, stream);
+    if (ws <= 8) return launch_ws<TYPE, 8, GQ_KQ_R>(p, stream);
+    if (ws <= 16) return launch_ws<TYPE, 16, GQ_KQ_R>(p, stream);
+    return hipErrorInvalidValue;    // beyond the documented maximum k (32768)
+}
+
 }  // namespace
 
 hipError_t launch_kq_pack(int type, const uint8_t* blocks, int64_t n, int64_t k, uint8_t* packed,
@@ -622,6 +712,7 @@ hipError_t launch_kq_pack(int type, const uint8_t* blocks, int64_t n, int64_t k,
     const int64_t nsb = n * (k / 256);
     const dim3 g(static_cast<unsigned>((nsb + kBlockThreads - 1) / kBlockThreads)), b(kBlockThreads);
     if (type == kTypeQ4_K) return launch_kernel(kq_pack_kernel<kTypeQ4_K>, g, b, stream, blocks, nsb, packed, o[1], o[2], o[3]);
+    if (type == kTypeQ5_K) return launch_kernel(kq_pack_kernel<kTypeQ5_K>, g, b, stream, blocks, nsb, packed, o[1], o[2], o[3]);
     return launch_kernel(kq_pack_kernel<kTypeQ6_K>, g, b, stream, blocks, nsb, packed, o[1], o[2], o[3]);
 }
 
@@ -631,10 +722,14 @@ hipError_t launch_qmv_kq(int type, const uint8_t* packed, int64_t n, int64_t k, 
     kq_layout(type, n, k, o);
     KqParams p{};
     p.q = packed;
-    p.hdr = packed + o[1];
-    p.qh = packed + o[1];
-    p.sc = reinterpret_cast<const int8_t*>(packed + o[2]);
-    p.d = reinterpret_cast<const uint16_t*>(packed + o[3]);
+    if (type == kTypeQ6_K) {
+        p.qh = packed + o[1];
+        p.sc = reinterpret_cast<const int8_t*>(packed + o[2]);
+        p.d = reinterpret_cast<const uint16_t*>(packed + o[3]);
+    } else {
+        p.hdr = packed + o[1];
+        if (type == kTypeQ5_K) p.fifth = reinterpret_cast<const uint32_t*>(packed + o[2]);
+    }
     p.x = x;
     p.y = y;
     p.n = static_cast<int>(n);
@@ -644,22 +739,9 @@ hipError_t launch_qmv_kq(int type, const uint8_t* packed, int64_t n, int64_t k, 
     // un-split rows take GQ_KQ_R_SHORT rows per step when GQ_KQ_R would give
     // fewer row groups (one wave each) than the device has SIMDs
     const bool short_rows = (static_cast<int64_t>(p.n) + GQ_KQ_R - 1) / GQ_KQ_R < 4 * kq_device_cus();
-    if (type == kTypeQ4_K) {
-        if (ws <= 1) return short_rows ? launch_ws<kTypeQ4_K, 1, GQ_KQ_R_SHORT>(p, stream)
-                                       : launch_ws<kTypeQ4_K, 1, GQ_KQ_R>(p, stream);
-        if (ws <= 2) return launch_ws<kTypeQ4_K, 2, GQ_KQ_R>(p, stream);
-        if (ws <= 4) return launch_ws<kTypeQ4_K, 4, GQ_KQ_R>(p, stream);
-        if (ws <= 8) return launch_ws<kTypeQ4_K, 8, GQ_KQ_R>(p, stream);
-        if (ws <= 16) return launch_ws<kTypeQ4_K, 16, GQ_KQ_R>(p, stream);
-    } else {
-        if (ws <= 1) return short_rows ? launch_ws<kTypeQ6_K, 1, GQ_KQ_R_SHORT>(p, stream)
-                                       : launch_ws<kTypeQ6_K, 1, GQ_KQ_R>(p, stream);
-        if (ws <= 2) return launch_ws<kTypeQ6_K, 2, GQ_KQ_R>(p, stream);
-        if (ws <= 4) return launch_ws<kTypeQ6_K, 4, GQ_KQ_R>(p, stream);
-        if (ws <= 8) return launch_ws<kTypeQ6_K, 8, GQ_KQ_R>(p, stream);
-        if (ws <= 16) return launch_ws<kTypeQ6_K, 16, GQ_KQ_R>(p, stream);
-    }
-    return hipErrorInvalidValue;    // beyond the documented maximum k (32768)
+    if (type == kTypeQ4_K) return launch_type<kTypeQ4_K>(p, ws, short_rows, stream);
+    if (type == kTypeQ5_K) return launch_type<kTypeQ5_K>(p, ws, short_rows, stream);
+    return launch_type<kTypeQ6_K>(p, ws, short_rows, stream);
 }
 
 }  // namespace gq

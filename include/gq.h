@@ -96,6 +96,7 @@ enum {
     GQ_TYPE_Q4_0 = 2,        /* GGUF type id of Q4_0 */
     GQ_TYPE_Q8_0 = 8,        /* GGUF type id of Q8_0 */
     GQ_TYPE_Q4_K = 12,       /* GGUF type id of Q4_K (256-element super-blocks) */
+    GQ_TYPE_Q5_K = 13,       /* GGUF type id of Q5_K (256-element super-blocks) */
     GQ_TYPE_Q6_K = 14        /* GGUF type id of Q6_K (256-element super-blocks) */
 };
 
@@ -315,19 +316,25 @@ int gq_qmm_tile_m(const uint8_t *qs, const uint16_t *d, int64_t n, int64_t k, in
                   int32_t *blockdots, void *stream);
 
 /*
- * K-quant super-blocks: Q4_K and Q6_K, 256 elements each (distributed Gemma 4
+ * K-quant super-blocks: Q4_K, Q5_K and Q6_K, 256 elements each (distributed Gemma 4
  * GGUF files are mostly Q4_K_M / UD-Q4_K_XL: TensorSharp Gemma 4 page, model
  * table). The arithmetic is the jouleclaw-loader-gguf BENCHMARKS page's
  * ("Q4_K matmul": 32-element sub-blocks with a 6-bit scale and a 6-bit
  * minimum, w = d sc q - dmin m, summed as d sc sum(x q) - dmin m sum(x);
- * "Q5_K + Q6_K matmul": Q6_K has four low bits, two high bits and a signed
- * -32 offset, w = d sc (q - 32) with one int8 scale per 16 elements). The
+ * "Q5_K + Q6_K matmul": Q5_K adds one high bit per element to Q4_K's four,
+ * w = d sc q - dmin m with q in 0..31; Q6_K has four low bits, two high bits
+ * and a signed -32 offset, w = d sc (q - 32) with one int8 scale per 16
+ * elements). The
  * GGUF byte layout the pages do not print:
  *  - Q4_K, 144 B: binary16 d, binary16 dmin, 12 bytes of scales/minimums
  *    (for sub-block j < 4: the low six bits of bytes j and j+4; for j >= 4:
  *    the low and high nibble of byte j+4 and the top two bits of bytes j-4
  *    and j), 128 quant bytes (byte 32g + l: element 64g + l in the low
  *    nibble, element 64g + 32 + l in the high one);
+ *  - Q5_K, 176 B: d, dmin and the 12 scale/minimum bytes as in Q4_K, qh[32],
+ *    then 128 quant bytes as in Q4_K; the fifth bit of element 64g + l
+ *    (l < 32) is bit 2g of qh byte l, that of element 64g + 32 + l bit
+ *    2g + 1;
  *  - Q6_K, 210 B: ql[128], qh[64], int8 scales[16], binary16 d; in half h
  *    and for l < 32, ql byte 64h + l holds the low bits of elements
  *    128h + l (low nibble) and 128h + l + 64 (high), ql byte 64h + l + 32
@@ -346,6 +353,13 @@ int gq_qmm_tile_m(const uint8_t *qs, const uint16_t *d, int64_t n, int64_t k, in
  *    dmin, then for each 64-element chunk g (sub-blocks 2g and 2g+1) the
  *    24-bit field sc_2g | sc_2g+1 << 6 | m_2g << 12 | m_2g+1 << 18 in bytes
  *    4+3g .. 6+3g;
+ *  - Q5_K: quants and headers as Q4_K, then fifth bits [n][k/32]: one
+ *    little-endian 32-bit word per 16-byte quant unit u = 2g + t of a
+ *    super-block (elements 64g + 16t + e, e < 16, and those + 32); quant
+ *    word c of the unit holds elements 4c .. 4c+3 of both runs, whose fifth
+ *    bits sit at bits 4, 5, 20, 21 (the first run) and 8, 9, 24, 25 (the
+ *    second) of a field, rotated left by 0, 2, 8, 10 for c = 0..3 and OR-ed
+ *    into the word (the four rotated fields do not overlap);
  *  - Q6_K: ql [n][k/2] (byte copies); qh [n][k/4]: for each 16-byte ql unit
  *    u = 4h + j of a super-block (elements 128h + 16j + e, e < 16, and those
  *    + 64), two little-endian 32-bit words; ql word c of the unit holds
@@ -356,7 +370,7 @@ int gq_qmm_tile_m(const uint8_t *qs, const uint16_t *d, int64_t n, int64_t k, in
  *    d [n][k/256] binary16.
  * gq_kq_packed_bytes returns 0 for an unknown type or invalid shape.
  *
- * gq_qmv_q4_k / gq_qmv_q6_k -- decode matvec on a packed K-quant matrix
+ * gq_qmv_q4_k / gq_qmv_q5_k / gq_qmv_q6_k -- decode matvec on a packed K-quant matrix
  * with fp32 activations: y[r] = sum_c w[r][c] x[c] accumulated in fp32,
  * |y - y_exact| <= 1e-4 * sum_c |w x| + 1e-6. x fp32 [k] (16-byte aligned),
  * y fp32 [n]. k must be a multiple of 256 (else GQ_ERR_SHAPE), at most
@@ -365,6 +379,7 @@ int gq_qmm_tile_m(const uint8_t *qs, const uint16_t *d, int64_t n, int64_t k, in
 size_t gq_kq_packed_bytes(int type, int64_t n, int64_t k);
 int gq_kq_pack(int type, const void *blocks, int64_t n, int64_t k, void *packed, void *stream);
 int gq_qmv_q4_k(const void *packed, int64_t n, int64_t k, const float *x, float *y, void *stream);
+int gq_qmv_q5_k(const void *packed, int64_t n, int64_t k, const float *x, float *y, void *stream);
 int gq_qmv_q6_k(const void *packed, int64_t n, int64_t k, const float *x, float *y, void *stream);
 
 /*

@@ -7,6 +7,13 @@ Q4_K header (16 bytes per super-block): d, dmin, then for each 64-element
 chunk g (sub-blocks 2g, 2g+1) the 24-bit field
 sc_2g | sc_2g+1 << 6 | m_2g << 12 | m_2g+1 << 18 in bytes 4+3g .. 6+3g.
 
+Q5_K (qs and header as Q4_K) fifth bits (32 bytes per super-block): one
+32-bit word per 16-byte quant unit u (elements 64g + 16t + e, low run, and
++ 32, high run; g = u / 2, t = u % 2, e < 16). Quant word c of the unit
+holds elements 4c..4c+3 of both runs; word c's bits sit at 4, 5, 20, 21
+(low run, b = 0..3) and 8, 9, 24, 25 (high run), rotated left by 0, 2, 8,
+10 for c = 0..3 (the four rotated sets are disjoint and fill the word).
+
 Q6_K high bits (64 bytes per super-block): for each 16-byte ql unit u = 4h+j
 (elements 128h + 16j + e, low run, and + 64, high run; e < 16), two 32-bit
 words. ql word c of the unit holds elements 4c..4c+3 of both runs; word c's
@@ -19,6 +26,9 @@ import numpy as np
 
 LO_POS = (4, 6, 20, 22)
 HI_POS = (8, 10, 24, 26)
+Q5_LO_POS = (4, 5, 20, 21)
+Q5_HI_POS = (8, 9, 24, 25)
+Q5_ROT = (0, 2, 8, 10)
 
 
 def q4_k_scale_min(scales):
@@ -47,6 +57,53 @@ def _rotl8(x):
 
 def _rotr8(x):
     return ((x >> np.uint32(8)) | (x << np.uint32(24))) & np.uint32(0xFFFFFFFF)
+
+
+def _rotl(x, r):
+    r %= 32
+    return ((x << np.uint32(r)) | (x >> np.uint32((32 - r) % 32))) & np.uint32(0xFFFFFFFF) if r else x
+
+
+def _rotr(x, r):
+    return _rotl(x, 32 - r) if r % 32 else x
+
+
+def q5_k_fifth_words(w):
+    """Expected packed Q5_K fifth-bit words, (n, nsb, 8 units) uint32."""
+    qh = w["qh"].astype(np.uint32)
+    out = np.zeros(w.shape + (8,), np.uint32)
+    for u in range(8):
+        g, t = divmod(u, 2)
+        word = np.zeros(w.shape, np.uint32)
+        for c in range(4):
+            f = np.zeros(w.shape, np.uint32)
+            for b in range(4):
+                qb = qh[..., 16 * t + 4 * c + b]
+                f |= ((qb >> np.uint32(2 * g)) & np.uint32(1)) << np.uint32(Q5_LO_POS[b])
+                f |= ((qb >> np.uint32(2 * g + 1)) & np.uint32(1)) << np.uint32(Q5_HI_POS[b])
+            word |= _rotl(f, Q5_ROT[c])
+        out[..., u] = word
+    return out
+
+
+def q5_k_read_back(qs_unit_words, fifth_word):
+    """The kernels' recipe, on one unit: quant words (4,) and its fifth-bit
+    word -> (low run, high run) 5-bit values, 16 each (the bit patterns the
+    kernel reads as binary16 subnormals)."""
+    lo, hi = np.zeros(16, np.int64), np.zeros(16, np.int64)
+    for c in range(4):
+        v = np.uint32(qs_unit_words[c])
+        v8 = v >> np.uint32(8)
+        hc = _rotr(np.uint32(fifth_word), Q5_ROT[c])
+        hc1 = hc >> np.uint32(1)
+        for half, sh in ((0, 0), (1, 16)):
+            lo[4 * c + 2 * half] = int(((v | 0) >> np.uint32(sh) & np.uint32(0xF)) | ((hc >> np.uint32(sh)) & np.uint32(0x10)))
+            lo[4 * c + 2 * half + 1] = int(((v8 >> np.uint32(sh)) & np.uint32(0xF)) | ((hc1 >> np.uint32(sh)) & np.uint32(0x10)))
+            hi[4 * c + 2 * half] = int((((v >> np.uint32(sh)) & np.uint32(0xF0)) |
+                                        ((hc >> np.uint32(sh)) & np.uint32(0x100))) >> np.uint32(4))
+            hi[4 * c + 2 * half + 1] = int((((v8 >> np.uint32(sh)) & np.uint32(0xF0)) |
+                                            ((hc1 >> np.uint32(sh)) & np.uint32(0x100))) >> np.uint32(4))
+    return lo, hi
 
 
 def q6_k_high_words(w):

@@ -196,12 +196,13 @@ def test_argmax_noalloc_validation():
 
 def test_kquant_validation():
     """K-quant entry points: whole 256-element super-blocks, k <= 32768."""
-    Q4K, Q6K = 12, 14
-    assert gq.block_bytes(Q4K) == 144 and gq.block_bytes(Q6K) == 210
+    Q4K, Q5K, Q6K = 12, 13, 14
+    assert gq.block_bytes(Q4K) == 144 and gq.block_bytes(Q5K) == 176 and gq.block_bytes(Q6K) == 210
     assert gq.kq_packed_bytes(Q4K, 4, 256) == 512 + 4 * 16          # quants, then 16-byte headers
+    assert gq.kq_packed_bytes(Q5K, 4, 256) == 512 + 256 + 4 * 32    # + headers padded to 256, fifth-bit words
     assert gq.kq_packed_bytes(Q6K, 4, 256) == 512 + 256 + 256 + 8   # ql, qh, scales (padded to 256), d
     assert gq.kq_packed_bytes(Q4K, 4, 288) == 0 and gq.kq_packed_bytes(Q4_0 := 2, 4, 256) == 0
-    for fn in (L.gq_qmv_q4_k, L.gq_qmv_q6_k):
+    for fn in (L.gq_qmv_q4_k, L.gq_qmv_q5_k, L.gq_qmv_q6_k):
         assert fn(None, 4, 256, C, D, None) == NULL
         assert fn(A, 4, 256, None, D, None) == NULL
         assert fn(A, 4, 288, C, D, None) == SHAPE
@@ -217,6 +218,8 @@ def test_kquant_validation():
     assert f(Q6K, B, 4, 300, A, None) == SHAPE
     assert f(Q6K, B, 4, 256, A + 8, None) == ALIGN
     assert f(Q6K, B, 4, 256, B + 16, None) == ALIAS
+    assert f(Q5K, B, 4, 256, B + 16, None) == ALIAS
+    assert f(15, B, 4, 256, A, None) == UNSUP                                # Q8_K: not a weight format here
 
 
 def test_ffn_ex_validation():

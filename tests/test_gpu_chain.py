@@ -189,19 +189,19 @@ def test_chain_records_nothing_for_a_rejected_call():
 
 
 def test_chained_kquant_matvecs():
-    """Q4_K and Q6_K matvecs recorded in one chain, replayed with new
+    """Q4_K, Q5_K and Q6_K matvecs recorded in one chain, replayed with new
     activations: every replay bit-equal to eager calls, and within the bound
     of the oracle."""
     rng = np.random.default_rng(12)
     n, k = 3000, 2304
     s = torch.cuda.Stream()
     ws = {}
-    for qtype in (gq.TYPE_Q4_K, gq.TYPE_Q6_K):
+    for qtype in (gq.TYPE_Q4_K, gq.TYPE_Q5_K, gq.TYPE_Q6_K):
         w = synth.weights(rng, qtype, n, k)
         ws[qtype] = (w, gq.kq_pack(qtype, up(synth.as_bytes(w).reshape(-1)), n, k))
     x = torch.zeros(k, dtype=torch.float32, device="cuda:0")
     y = {q: torch.empty(n, dtype=torch.float32, device="cuda:0") for q in ws}
-    fns = {gq.TYPE_Q4_K: gq.qmv_q4_k, gq.TYPE_Q6_K: gq.qmv_q6_k}
+    fns = {gq.TYPE_Q4_K: gq.qmv_q4_k, gq.TYPE_Q5_K: gq.qmv_q5_k, gq.TYPE_Q6_K: gq.qmv_q6_k}
 
     def enqueue():
         for q, (_, p) in ws.items():
@@ -214,7 +214,7 @@ def test_chained_kquant_matvecs():
         chain = gq.Chain(s)
         with chain:
             enqueue()
-        assert chain.launches == 2
+        assert chain.launches == 3
         for rep in range(3):
             xv = synth.activations(rng, k)
             x.copy_(up(xv))

@@ -1,4 +1,4 @@
-"""GPU parity of the K-quant path (Q4_K, Q6_K super-blocks of 256 elements):
+"""GPU parity of the K-quant path (Q4_K, Q5_K, Q6_K super-blocks of 256 elements):
 the load-time pack lays out every byte as specified, and the fp32-activation matvec
 matches the fp64 oracle (which reads the canonical GGUF super-block bytes)
 within |y - y_ref| <= 1e-4 sum|w x| + 1e-6 at every dispatch shape, bit for
@@ -20,14 +20,16 @@ if not torch.cuda.is_available():
 
 import gguf_block_quant_amd as gq  # noqa: E402
 
-Q4K, Q6K = gq.TYPE_Q4_K, gq.TYPE_Q6_K
+Q4K, Q5K, Q6K = gq.TYPE_Q4_K, gq.TYPE_Q5_K, gq.TYPE_Q6_K
+KQ = [Q4K, Q5K, Q6K]
 
 
 def _fn(qtype):
-    return gq.qmv_q4_k if qtype == Q4K else gq.qmv_q6_k
+    return {Q4K: gq.qmv_q4_k, Q5K: gq.qmv_q5_k, Q6K: gq.qmv_q6_k}[qtype]
 
 
-@pytest.mark.parametrize("qtype,n,k", [(Q4K, 7, 256), (Q4K, 33, 2048), (Q6K, 7, 256), (Q6K, 33, 4352)])
+@pytest.mark.parametrize("qtype,n,k", [(Q4K, 7, 256), (Q4K, 33, 2048), (Q5K, 7, 256), (Q5K, 33, 2304),
+                                       (Q6K, 7, 256), (Q6K, 33, 4352)])
 def test_kq_pack_lays_out_every_byte(qtype, n, k):
     # the packed sections are the layout's lossless rearrangement of the GGUF
     # bits (modelled on the host; the model is pinned by test_kq_layout.py)
@@ -36,12 +38,17 @@ def test_kq_pack_lays_out_every_byte(qtype, n, k):
     assert p.size >= gq.kq_packed_bytes(qtype, n, k)
     nsb = k // 256
     r256 = lambda b: (b + 255) // 256 * 256  # noqa: E731
-    if qtype == Q4K:
+    if qtype in (Q4K, Q5K):
         qs = p[: n * k // 2].reshape(n, nsb, 128)
         o1 = r256(n * k // 2)
         hdr = p[o1: o1 + n * nsb * 16].reshape(n, nsb, 16)
         assert np.array_equal(qs, w["qs"])
         assert np.array_equal(hdr, kq_model.q4_k_header(w))
+        if qtype == Q5K:
+            o2 = o1 + r256(n * nsb * 16)
+            assert p.size == o2 + n * k // 8
+            assert np.array_equal(p[o2: o2 + n * k // 8].copy().view("<u4").reshape(n, nsb, 8),
+                                  kq_model.q5_k_fifth_words(w))
     else:
         o1 = r256(n * k // 2)
         o2 = o1 + r256(n * k // 4)
@@ -61,7 +68,7 @@ SHAPES = [(2048, 2048), (8192, 2048), (1, 256), (3, 768), (1001, 1536), (515, 23
           (77, 8192), (45, 11776), (64, 16384), (17, 32768), (4096, 2048), (4099, 1792)]
 
 
-@pytest.mark.parametrize("qtype", [Q4K, Q6K])
+@pytest.mark.parametrize("qtype", KQ)
 @pytest.mark.parametrize("n,k", SHAPES)
 def test_qmv_kq(qtype, n, k):
     rng = np.random.default_rng(3 * n + k + qtype)
@@ -73,7 +80,7 @@ def test_qmv_kq(qtype, n, k):
     check_within(y, yr, oracle.fp32_path_bound(ar), "type %d %dx%d" % (qtype, n, k))
 
 
-@pytest.mark.parametrize("qtype", [Q4K, Q6K])
+@pytest.mark.parametrize("qtype", KQ)
 def test_qmv_kq_one_hot_layout(qtype):
     """x = e_c selects column c: y[r] must be the dequantised weight w[r][c]
     rounded once to fp32, for every c of a two-super-block row."""
@@ -88,7 +95,7 @@ def test_qmv_kq_one_hot_layout(qtype):
         assert np.array_equal(y, W[:, c].astype(np.float32)), c
 
 
-@pytest.mark.parametrize("qtype", [Q4K, Q6K])
+@pytest.mark.parametrize("qtype", KQ)
 def test_qmv_kq_exact_power_of_two_case(qtype):
     """Power-of-two super-block scales and small integer activations keep
     every partial sum exact in fp32: the GPU must equal the oracle bitwise."""
@@ -97,7 +104,7 @@ def test_qmv_kq_exact_power_of_two_case(qtype):
     w = synth.weights(rng, qtype, n, k)
     pw = lambda shape: (2.0 ** rng.integers(-10, -6, size=shape)).astype(np.float16).view(np.uint16)  # noqa: E731
     w["d"] = pw(w["d"].shape)
-    if qtype == Q4K:
+    if qtype in (Q4K, Q5K):
         w["dmin"] = pw(w["dmin"].shape)
     x = rng.integers(-2, 3, size=k).astype(np.float32)
     p = packed_kq(gq, qtype, w, n, k)
@@ -106,12 +113,12 @@ def test_qmv_kq_exact_power_of_two_case(qtype):
     assert np.array_equal(y.astype(np.float64), yr)
 
 
-@pytest.mark.parametrize("qtype", [Q4K, Q6K])
+@pytest.mark.parametrize("qtype", KQ)
 @pytest.mark.parametrize("n,k", [(2048, 2048), (77, 8192), (17, 32768)])
 def test_qmv_kq_special_scales(qtype, n, k):
     rng = np.random.default_rng(60 + n + qtype)
     w = synth.weights(rng, qtype, n, k)
-    fields = ["d", "dmin"] if qtype == Q4K else ["d"]
+    fields = ["d", "dmin"] if qtype in (Q4K, Q5K) else ["d"]
     finite = np.array([0x0000, 0x8000, 0x0001, 0x03FF, 0x8200, 0x7BFF, 0xFBFF], np.uint16)
     for f in fields:
         mask = rng.random(w[f].shape) < 0.1
@@ -127,7 +134,7 @@ def test_qmv_kq_special_scales(qtype, n, k):
     check_special(y, yr, ar, "type %d %dx%d special" % (qtype, n, k))
 
 
-@pytest.mark.parametrize("qtype", [Q4K, Q6K])
+@pytest.mark.parametrize("qtype", KQ)
 def test_qmv_kq_deterministic_and_large_x(qtype):
     rng = np.random.default_rng(70 + qtype)
     n, k = 4096, 4096
@@ -141,7 +148,7 @@ def test_qmv_kq_deterministic_and_large_x(qtype):
     check_within(y1, yr, oracle.fp32_path_bound(ar), "large x")
 
 
-@pytest.mark.parametrize("qtype", [Q4K, Q6K])
+@pytest.mark.parametrize("qtype", KQ)
 @pytest.mark.parametrize("scale", [1e-30, 1e-36])
 def test_qmv_kq_tiny_x(qtype, scale):
     """Activations near the bottom of the fp32 range (products below 2^-126

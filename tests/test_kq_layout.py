@@ -6,7 +6,7 @@ values, in every unit and chunk position."""
 import numpy as np
 
 import kq_layout_model as model
-from test_oracle_kquant_pins import blocks_from, enc_q4_k, enc_q6_k, f16
+from test_oracle_kquant_pins import blocks_from, enc_q4_k, enc_q5_k, enc_q6_k, f16
 
 import synth
 
@@ -82,3 +82,43 @@ def test_q6_k_single_high_bit_lands_once():
             got[128 * h + 16 * j: 128 * h + 16 * j + 16] = lo
             got[128 * h + 16 * j + 64: 128 * h + 16 * j + 80] = hi
         assert np.array_equal(got, q), e
+
+
+def _q5_k_unit_values(w, r, s_, q_words_of, fifth):
+    got = np.zeros(256, np.int64)
+    for u in range(8):
+        g, t = divmod(u, 2)
+        lo, hi = model.q5_k_read_back(q_words_of(u), fifth[r, s_, u])
+        got[64 * g + 16 * t: 64 * g + 16 * t + 16] = lo
+        got[64 * g + 32 + 16 * t: 64 * g + 32 + 16 * t + 16] = hi
+    return got
+
+
+def test_q5_k_fifth_bits_read_back_exactly():
+    rng = np.random.default_rng(13)
+    raw, truth = [], []
+    for _ in range(12):
+        q = rng.integers(0, 32, 256)
+        raw.append(enc_q5_k(f16(0.5), f16(0.25), rng.integers(0, 64, 8), rng.integers(0, 64, 8), q))
+        truth.append(q)
+    w = blocks_from(raw).view(synth.Q5_K_BLOCK).reshape(3, 4)
+    fifth = model.q5_k_fifth_words(w)
+    for i, q in enumerate(truth):
+        r, s_ = divmod(i, 4)
+        words = lambda u: w["qs"][r, s_, 16 * u: 16 * u + 16].copy().view("<u4")   # noqa: E731
+        assert np.array_equal(_q5_k_unit_values(w, r, s_, words, fifth), q), i
+    # the header is the Q4_K one: same packing, same read-back
+    hdr = model.q4_k_header(w)
+    assert np.array_equal(hdr[..., 0:2].copy().view(np.uint16)[..., 0], w["d"])
+
+
+def test_q5_k_single_fifth_bit_lands_once():
+    # one element at 16 (fifth bit only), the rest 0: exactly that element reads back nonzero
+    for e in range(256):
+        q = np.zeros(256, np.int64)
+        q[e] = 16
+        w = blocks_from([enc_q5_k(f16(1.0), f16(1.0), np.ones(8, np.int64), np.zeros(8, np.int64), q)])
+        w = w.view(synth.Q5_K_BLOCK).reshape(1, 1)
+        fifth = model.q5_k_fifth_words(w)
+        words = lambda u: w["qs"][0, 0, 16 * u: 16 * u + 16].copy().view("<u4")   # noqa: E731
+        assert np.array_equal(_q5_k_unit_values(w, 0, 0, words, fifth), q), e
