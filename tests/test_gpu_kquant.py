@@ -164,6 +164,25 @@ def test_qmv_kq_tiny_x(qtype, scale):
     check_within(y, yr, oracle.fp32_path_bound(ar), "tiny x %g" % scale)
 
 
+@pytest.mark.parametrize("qtype", KQ)
+def test_qmv_kq_full_size_sampled_rows(qtype):
+    """The tall launch shape the benchmark times (262144 x 2048, each wave
+    walking many row groups), plus a ragged 3-row tail: sampled rows -- the
+    first and last groups, both sides of every 4-row group boundary in a
+    stretch, and random rows -- against the oracle row by row."""
+    rng = np.random.default_rng(90 + qtype)
+    n, k = 262147, 2048
+    w = synth.weights(rng, qtype, n, k)
+    x = synth.activations(rng, k)
+    p = packed_kq(gq, qtype, w, n, k)
+    y = down(_fn(qtype)(p, n, k, up(x)))
+    rows = np.unique(np.concatenate([np.arange(0, 16), np.arange(n - 16, n), np.arange(131064, 131080),
+                                     rng.integers(0, n, 200)]))
+    yr, ar = oracle.matvec_rows(qtype, w, n, k, rows, x)
+    check_within(y[rows], yr, oracle.fp32_path_bound(ar), "type %d full size" % qtype)
+    assert np.isfinite(y).all()
+
+
 def test_kq_binding_errors():
     x = torch.zeros(256, dtype=torch.float32, device="cuda")
     p = torch.zeros(gq.kq_packed_bytes(Q4K, 4, 256), dtype=torch.uint8, device="cuda")
