@@ -131,7 +131,6 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
     return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
-// Largest of v over the 64 lanes, in every lane (max is exact in any order).
 // The largest of v over the 64 lanes, in every lane (64-bit keys, moved as
 // two 32-bit halves per step).
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
@@ -145,6 +144,7 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
     return v;
 }
 
+// Largest of v over the 64 lanes, in every lane (max is exact in any order).
 __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, dpp_f32<kDppQuadSwap1>(v));
     v = fmaxf(v, dpp_f32<kDppQuadSwap2>(v));
