@@ -105,10 +105,7 @@ __device__ __forceinline__ float wave_sum_swapped(float a) {
     return row_sum(fold_rows(h, h));
 }
 
-// Sum of a double over the 64 lanes of the wave, in every lane: the same
-// pairing and order as wave_sum (each DPP step moves the two 32-bit halves),
-// so the result is reproducible and identical in every lane -- and the same
-// bits as a xor butterfly over the lanes (fp64 addition is commutative).
+// One DPP move of a double: its two 32-bit halves with the same control.
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
     const uint64_t b = __builtin_bit_cast(uint64_t, v);
@@ -117,18 +114,32 @@ __device__ __forceinline__ double dpp_f64(double v) {
         static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), CTRL, 0xF, 0xF, false));
     return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
 }
-__device__ __forceinline__ double readlane_f64(double v, int l) {
-    const uint64_t b = __builtin_bit_cast(uint64_t, v);
-    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b), l));
-    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b >> 32), l));
+// The sum of v over the 64 lanes, in every lane, with no lane reads: a
+// lane-half swap and a row swap (each moving the two 32-bit halves of the
+// value) add the four rows' lanes pairwise, then four DPP steps add the 16
+// lanes of a row. Every lane holds the same bits.
+__device__ __forceinline__ double join_f64(uint32_t lo, uint32_t hi) {
     return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
 }
-__device__ __forceinline__ double wave_sum_f64(double v) {
+__device__ __forceinline__ double wave_sum_f64_all(double v) {
+    typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+    uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const u32x2_t l32 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane32_swap(
+        static_cast<uint32_t>(b), static_cast<uint32_t>(b), false, false));
+    const u32x2_t h32 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane32_swap(
+        static_cast<uint32_t>(b >> 32), static_cast<uint32_t>(b >> 32), false, false));
+    v = join_f64(l32.x, h32.x) + join_f64(l32.y, h32.y);
+    b = __builtin_bit_cast(uint64_t, v);
+    const u32x2_t l16 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane16_swap(
+        static_cast<uint32_t>(b), static_cast<uint32_t>(b), false, false));
+    const u32x2_t h16 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane16_swap(
+        static_cast<uint32_t>(b >> 32), static_cast<uint32_t>(b >> 32), false, false));
+    v = join_f64(l16.x, h16.x) + join_f64(l16.y, h16.y);
     v += dpp_f64<kDppQuadSwap1>(v);
     v += dpp_f64<kDppQuadSwap2>(v);
     v += dpp_f64<kDppRowHalfMirror>(v);
     v += dpp_f64<kDppRowMirror>(v);
-    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+    return v;
 }
 
 // The largest of v over the 64 lanes, in every lane (64-bit keys, moved as
@@ -144,17 +155,19 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
     return v;
 }
 
-// Largest of v over the 64 lanes, in every lane (max is exact in any order).
-__device__ __forceinline__ float wave_max(float v) {
+// The largest of v over the 64 lanes, in every lane: a lane-half swap, a
+// row swap and four DPP steps, as wave_sum_f64_all (max is exact in any
+// order).
+__device__ __forceinline__ float wave_max_all(float v) {
+    f32x2_t t = swap_halves(v, v);
+    v = fmaxf(t.x, t.y);
+    t = swap_rows(v, v);
+    v = fmaxf(t.x, t.y);
     v = fmaxf(v, dpp_f32<kDppQuadSwap1>(v));
     v = fmaxf(v, dpp_f32<kDppQuadSwap2>(v));
     v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v));
     v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
-    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
-    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
-    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+    return v;
 }
 
 // Exact int8x4 dot product with int32 accumulate (v_dot4_i32_i8).

@@ -551,8 +551,8 @@ void qmv_kernel(const QmvParams p) {
         }
         if constexpr (FOLD) {
             if (norm) {
-                ss = wave_sum_f64(ss);
-                mxl = wave_max(mxl);
+                ss = wave_sum_f64_all(ss);
+                mxl = wave_max_all(mxl);
                 if (lane == 0) {
                     nss[wave] = ss;
                     nmx[wave] = mxl;
@@ -680,8 +680,8 @@ void qmv_kernel(const QmvParams p) {
                         for (int c = 0; c < 4; ++c) mxl = fmaxf(mxl, fabsf(xr[i][4 * v + c]));   // zero past k
                     }
                 }
-                ss = wave_sum_f64(ss);
-                mxl = wave_max(mxl);
+                ss = wave_sum_f64_all(ss);
+                mxl = wave_max_all(mxl);
                 if (lane == 0) {
                     nss[wave] = ss;
                     nmx[wave] = mxl;
