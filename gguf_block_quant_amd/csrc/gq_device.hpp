@@ -155,19 +155,14 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
     return v;
 }
 
-// The largest of v over the 64 lanes, in every lane: a lane-half swap, a
-// row swap and four DPP steps, as wave_sum_f64_all (max is exact in any
-// order).
-__device__ __forceinline__ float wave_max_all(float v) {
-    f32x2_t t = swap_halves(v, v);
-    v = fmaxf(t.x, t.y);
-    t = swap_rows(v, v);
-    v = fmaxf(t.x, t.y);
-    v = fmaxf(v, dpp_f32<kDppQuadSwap1>(v));
-    v = fmaxf(v, dpp_f32<kDppQuadSwap2>(v));
-    v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v));
-    v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
-    return v;
+// Where the largest of v over the 64 lanes falls against [lo, hi], without
+// finding it: bit 0 set if some lane's v is above hi, bit 1 if some lane's v
+// is at or above lo (two ballots). The largest lies within [lo, hi] exactly
+// when the result is 2. (v is a lane's own maximum, NaN-free as fmaxf makes it.)
+__device__ __forceinline__ int range_flags(float v, float lo, float hi) {
+    const unsigned long long above = __ballot(v > hi);
+    const unsigned long long reach = __ballot(v >= lo);
+    return (above != 0ull ? 1 : 0) | (reach != 0ull ? 2 : 0);
 }
 
 // Exact int8x4 dot product with int32 accumulate (v_dot4_i32_i8).

@@ -274,7 +274,7 @@ void qmv_kernel(const QmvParams p) {
     __shared__ uint32_t qx_s[kQxWords];
     __shared__ uint16_t qd_s[kQuantX ? kQxWords / 8 : 1];
     __shared__ double nss[WAVES];
-    __shared__ float nmx[WAVES];
+    __shared__ int nfl[WAVES];      // per wave: 1 = some |x w| above 2^40, 2 = some at or above 2^-40
 
     // ---- this lane's units ------------------------------------------------
     int unit[NI];
@@ -552,10 +552,10 @@ void qmv_kernel(const QmvParams p) {
         if constexpr (FOLD) {
             if (norm) {
                 ss = wave_sum_f64_all(ss);
-                mxl = wave_max_all(mxl);
+                const int fl = range_flags(mxl, kPostLo, kPostHi);
                 if (lane == 0) {
                     nss[wave] = ss;
-                    nmx[wave] = mxl;
+                    nfl[wave] = fl;
                 }
             }
         }
@@ -564,14 +564,14 @@ void qmv_kernel(const QmvParams p) {
         if constexpr (FOLD) {
             if (norm) {
                 double t = nss[0];
-                float mx = nmx[0];
+                int fl = nfl[0];
 #pragma unroll
                 for (int w = 1; w < WAVES; ++w) {
                     t += nss[w];
-                    mx = fmaxf(mx, nmx[w]);
+                    fl |= nfl[w];
                 }
                 inv = norm_scale(t);
-                post = mx >= kPostLo && mx <= kPostHi;
+                post = fl == 2;             // the largest |x w| within [2^-40, 2^40]
                 if (post) {
                     post_inv = inv;
                     inv = 1.0;
@@ -681,21 +681,21 @@ void qmv_kernel(const QmvParams p) {
                     }
                 }
                 ss = wave_sum_f64_all(ss);
-                mxl = wave_max_all(mxl);
+                const int fl0 = range_flags(mxl, kPostLo, kPostHi);
                 if (lane == 0) {
                     nss[wave] = ss;
-                    nmx[wave] = mxl;
+                    nfl[wave] = fl0;
                 }
                 __syncthreads();
                 double t = nss[sub * WS];
-                float mx = nmx[sub * WS];
+                int fl = nfl[sub * WS];
 #pragma unroll
                 for (int sl = 1; sl < WS; ++sl) {
                     t += nss[sub * WS + sl];
-                    mx = fmaxf(mx, nmx[sub * WS + sl]);
+                    fl |= nfl[sub * WS + sl];
                 }
                 const double inv = norm_scale(t);
-                post = mx >= kPostLo && mx <= kPostHi;
+                post = fl == 2;             // the largest |x w| within [2^-40, 2^40]
                 if (post) {
                     post_inv = inv;
                 } else {
