@@ -491,14 +491,13 @@ void qmv_kernel(const QmvParams p) {
         return (a > 0.0 && a < __builtin_inf()) ? y1 : y0;
     };
     auto scaled = [](float v, double s) { return static_cast<float>(static_cast<double>(v) * s); };
-    // RMSNorm: when every |x_i w_i| lies in [2^-40, 2^40] (the usual case;
-    // uniform over the launch), the dots run on x w as staged and each
-    // finished row is multiplied by inv in fp64 (rounded once) -- no dot can
-    // overflow or lose precision to underflow there (|y| <= k 65504 127 2^40),
-    // and the prologue's fp64 work no longer delays the first dot. Outside
-    // that range the activations are scaled by inv before the dots, as an
-    // fp64 product rounded once, which keeps every dot in range for any
-    // finite x.
+    // RMSNorm: when the largest |x_i w_i| lies in [2^-40, 2^40] (the usual
+    // case; uniform over the launch, decided from two wave ballots), the dots
+    // run on x w as staged and each finished row is multiplied by inv in fp64
+    // (rounded once) -- no dot can overflow there (|y| <= k 65504 127 2^40)
+    // and the largest products stay far above fp32's underflow. Outside that
+    // range the activations are scaled by inv before the dots, as an fp64
+    // product rounded once, which keeps every dot in range for any finite x.
     float mxl = 0.f;                 // this thread's max |x w|
     bool post = false;               // scale the finished rows by post_inv
     double post_inv = 1.0;

@@ -180,8 +180,9 @@ int gq_qmv_q4_0(const uint8_t *qs, const uint16_t *d, int64_t n, int64_t k,
  *    norm_eps >= 0 and finite, else GQ_ERR_VALUE. The sum of squares is
  *    taken in fp64, and the scale (mean + norm_eps)^(-1/2) in fp64 to
  *    within about 1e-14 relative; the scale is applied to each finished row (an fp64
- *    product) when every |x[c] * norm_weight[c]| lies in [2^-40, 2^40],
- *    and otherwise to the activations before the products, so any finite
+ *    product) when the largest |x[c] * norm_weight[c]| lies in
+ *    [2^-40, 2^40], and otherwise to the activations before the products,
+ *    so any finite
  *    x is supported as long as every product x[c] * norm_weight[c] is
  *    finite in fp32 (|x w| <= 3.4e38);
  *  - if residual is not NULL, y[r] = residual[r] + (W x)[r]; residual fp32
