@@ -52,8 +52,8 @@
 // Measured on MI355X (fp32 x, k = 2048; 262144 / 8192 rows, and 2048 x 8192):
 // 4 rows per step with up to 2048 workgroups: Q4_K 52.2 / 4.5 / 4.7 us with
 // the nibbles read as binary16 subnormals (59.0 / 4.7 / 4.8 with the
-// normal-range form and its packed add), Q6_K 73.6-75.4 / 5.3-5.6 /
-// 5.4-5.8 us, with the four rows summed over the lanes together (one row
+// normal-range form and its packed add), Q6_K 73.5-73.8 / 5.1 / 5.3 us
+// (five waves per SIMD), with the four rows summed over the lanes together (one row
 // at a time was 2-3 % slower; with the packed fields read directly; the
 // byte-copy layout, unpacking the GGUF fields in the loop, gave 60-62 /
 // 5.3 / 5.6 and 82-84 / 6.0-6.2 / 5.5-5.8 us); 2 rows at 1024 workgroups
